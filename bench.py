@@ -1,0 +1,200 @@
+"""Benchmark one context-parallel rank's share of causal ring attention on one
+MI355X and print one JSON line.
+
+A step is one ra_forward call: state set-up, the n_cp ring steps (each block
+after the first staged on a side stream while the previous one computes) and
+normalisation, over inputs already resident in HBM.  The metric is visible
+causal attention TFLOP/s (4 * d_k * h_q FLOPs per visible query/key pair)
+and its fraction of the bf16 MFMA peak.
+
+The default workload is the Llama-3-405B long-context stage share: T=131072,
+n_cp=16 zigzag, 16 query heads and 1 key/value head of width 128, bf16, rank 0
+(8192 queries against 16 blocks of 8192 keys).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import ring_attention_rank_amd as ra  # noqa: E402
+import synth  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_F32_TFLOPS = 157.3
+HBM_GBPS = 8000.0
+METRIC = "causal attention TFLOP/s per rank-share and % of bf16 MFMA peak (1 GPU)"
+
+
+def visible_pairs(q_pos, k_pos):
+    ks = np.sort(np.asarray(k_pos, dtype=np.int64))
+    return int(np.searchsorted(ks, np.asarray(q_pos, dtype=np.int64), side="right").sum())
+
+
+def build_share(case, rank, device):
+    L = ra.layouts
+    q_pos = L.rank_positions(case.T, case.n_cp, rank, case.layout)
+    srcs = [L.ring_block_owner(case.n_cp, rank, b) for b in range(case.n_cp)]
+    k_pos = [L.rank_positions(case.T, case.n_cp, s, case.layout) for s in srcs]
+    q, kb, vb = synth.case_inputs(case, q_pos, k_pos)
+    dt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    gq = torch.from_numpy(q).to(dt).to(device)
+    n_cp = case.n_cp
+    h_kv, n_k, d = kb[0].shape
+    kk = torch.empty((n_cp, h_kv, n_k, d), dtype=dt, device=device)
+    vv = torch.empty((n_cp, h_kv, n_k, d), dtype=dt, device=device)
+    for b in range(n_cp):
+        kk[b].copy_(torch.from_numpy(kb[b]).to(dt))
+        vv[b].copy_(torch.from_numpy(vb[b]).to(dt))
+    share = dict(q=q, k=kb, v=vb, q_pos=q_pos, k_pos=k_pos, gq=gq,
+                 gq_pos=torch.from_numpy(q_pos).to(device),
+                 gk=[kk[b] for b in range(n_cp)], gv=[vv[b] for b in range(n_cp)],
+                 gk_pos=[torch.from_numpy(p).to(device) for p in k_pos])
+    share["pairs_per_step"] = [visible_pairs(q_pos, p) for p in k_pos]
+    return share
+
+
+def cpu_baseline(case, share, out, lse, budget_rows):
+    """The float64 oracle on a bounded sample of the same share's query rows
+    (every block, same ring order), timed on the host's cores."""
+    import oracle  # the CPU baseline is the oracle itself, untuned
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity count
+        blas = len(os.sched_getaffinity(0))
+    n_q = len(share["q_pos"])
+    rows = np.unique(np.linspace(0, n_q - 1, budget_rows).astype(np.int64))
+    q = share["q"][:, rows]
+    qp = share["q_pos"][rows]
+    t0 = time.perf_counter()
+    ro, rl = oracle.ring_forward_ref(q, qp, share["k"], share["v"], share["k_pos"])
+    dt = time.perf_counter() - t0
+    pairs = sum(visible_pairs(qp, p) for p in share["k_pos"])
+    flops = 4 * case.d_k * case.h_q * pairs
+    idx = torch.from_numpy(rows).to(out.device)
+    go = out[:, idx].cpu().numpy().astype(np.float64)
+    gl = lse[:, idx].cpu().numpy().astype(np.float64)
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas), "kind": "oracle",
+        "sample": f"{len(rows)} of {n_q} query rows (evenly spaced) x {case.h_q} heads against "
+                  f"all {case.n_cp} blocks, float64 numpy; {pairs} visible pairs in {dt:.2f} s",
+        "seconds": dt,
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "sample_max_abs_err_out": float(np.abs(go - ro).max()),
+        "sample_max_abs_err_lse": float(np.abs(gl - rl).max()),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="llama405b_stage_share",
+                    choices=[c.name for c in synth.CASES])
+    ap.add_argument("--rank", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--no-side-stream", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's rank share only; multi-GPU runs are not part of "
+              "this build (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    case = synth.case_by_name(args.config)
+    ranks = case.ranks if args.rank is None else (args.rank,)
+    dev = torch.device("cuda", 0)
+    props = torch.cuda.get_device_properties(dev)
+
+    total_flops = 0
+    total_time = 0.0
+    step_ms = []
+    per_rank = []
+    last = None
+    for r in ranks:
+        share = build_share(case, r, dev)
+        fwd = ra.Forward(share["gq"], share["gq_pos"], share["gk"], share["gv"], share["gk_pos"],
+                         side=not args.no_side_stream)
+        flops = 4 * case.d_k * case.h_q * sum(share["pairs_per_step"])
+        for _ in range(args.warmup):
+            fwd()
+        torch.cuda.synchronize()
+        main_stream = torch.cuda.current_stream()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e0, e1 in evs:
+            e0.record(main_stream)
+            fwd()
+            e1.record(main_stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+        step_ms += ms
+        total_flops += flops * args.steps
+        total_time += wall
+        per_rank.append({"rank": r, "median_ms": float(np.median(ms)),
+                         "tflops_median": flops / (np.median(ms) * 1e-3) / 1e12,
+                         "visible_flops": flops, "staged_bytes": fwd.staged.value,
+                         "work": fwd.work.tolist()})
+        last = (share, fwd, flops)
+
+    ms_per_step = total_time / (args.steps * len(ranks)) * 1e3
+    value = total_flops / total_time / 1e12
+    peak = PEAK_BF16_TFLOPS if case.dtype == "bf16" else PEAK_F32_TFLOPS
+    share, fwd, flops = last
+    n_launch = case.n_cp
+    avg_launch_ms = float(np.mean(step_ms)) / n_launch
+    achieved = flops / n_launch / (avg_launch_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": case.name, "T": case.T, "n_cp": case.n_cp, "layout": case.layout,
+            "ranks": list(ranks), "h_q": case.h_q, "h_kv": case.h_kv, "d_k": case.d_k,
+            "n_q": len(share["q_pos"]), "n_k_per_block": len(share["k_pos"][0]),
+            "visible_flops_per_step": flops, "side_stream_staging": not args.no_side_stream,
+        },
+        "per_rank": per_rank,
+        "roofline": {
+            "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak, "traffic": None,
+            "kernel": "step_kernel (bf16 MFMA 32x32x16)",
+            "avg_launch_ms": avg_launch_ms, "launches_per_step": n_launch,
+            "event_median_ms_per_step": float(np.median(step_ms)),
+        },
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    if not args.no_cpu_baseline and len(ranks) >= 1:
+        out, lse = fwd.out, fwd.lse
+        result["cpu_baseline"] = cpu_baseline(case, share, out, lse, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,140 @@
+/*
+ * ra.h -- C ABI of the MI355X (gfx950) ring-attention rank-share library.
+ *
+ * One context-parallel rank holds n_q queries at explicit global token
+ * positions and meets every key/value block of the sequence once, one block
+ * per ring step (Zero to Frontier, "distributed/context-expert", section
+ * "Splitting the sequence, and the one layer that objects": each step the
+ * GPU attends its queries to the block it holds while passing that block to
+ * its right neighbour and receiving the next from its left).  For every query
+ * it keeps the online-softmax state -- running maximum m of the scores,
+ * running sum l of their exponentials, unnormalised weighted value sum O --
+ * and rescales the old totals whenever a block brings a larger score (same
+ * section; also the "Context Parallelism (CP)" concept page, "Key math / How
+ * it works").  After the last block, out = O / l and lse = m + ln l.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named q, k, v, *_pos, m, l, o, out, lse, work and workspace are
+ *    DEVICE pointers, allocated and owned by the caller; the library keeps
+ *    none of them past the call.  Arrays of block pointers passed to
+ *    ra_forward are HOST arrays of device pointers.  staged_bytes is a host
+ *    pointer.
+ *  - Layouts are row-major with d_k fastest:  q[h_q][n_q][d_k],
+ *    k, v[h_kv][n_k][d_k], m, l[h_q][n_q], o, out[h_q][n_q][d_k], lse[h_q][n_q].
+ *    Element type of q, k, v: bfloat16 (RA_BF16) or float (RA_F32).  State,
+ *    out and lse are float.  q, k, v, o, out and workspace must be 16-byte
+ *    aligned; positions, m, l and lse 4-byte; work 8-byte.
+ *  - q_pos[n_q] and k_pos[n_k] are int32 global positions in [0, 2^31-2],
+ *    strictly increasing within each array (true of the contiguous, zigzag
+ *    and striped layouts).  Key j is visible to query i iff
+ *    k_pos[j] <= q_pos[i] when causal, always otherwise.  Positions that do
+ *    not increase give unspecified values but never an out-of-bounds access.
+ *  - Query head h reads key/value head h / (h_q / h_kv).
+ *  - m is kept in natural-log units of the scaled score (scale * q.k).  A row
+ *    that has seen no visible key has m = -inf, l = 0, O = 0.
+ *  - Calls are asynchronous on the given HIP stream (passed as void*, a
+ *    hipStream_t; NULL is the default stream).  Arguments are checked on the
+ *    host first: on an error nothing is enqueued and no output is touched.
+ *    RA_ERR_HIP reports a failed launch or enqueue; a fault inside a kernel
+ *    surfaces at the caller's next synchronisation.
+ *  - The library holds no mutable global state: concurrent calls on
+ *    different streams are safe when their output buffers do not overlap.
+ */
+#ifndef RA_H
+#define RA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ra_status;
+enum {
+  RA_OK = 0,
+  RA_ERR_NULL = -1,      /* a required pointer is NULL */
+  RA_ERR_SHAPE = -2,     /* sizes out of range, h_q % h_kv != 0, d_k not 64/128, n_cp < 1 */
+  RA_ERR_DTYPE = -3,     /* dtype not RA_BF16 / RA_F32 */
+  RA_ERR_ALIGN = -4,     /* a pointer breaks the alignment rules above */
+  RA_ERR_WORKSPACE = -5, /* workspace smaller than ra_forward_workspace_bytes() */
+  RA_ERR_HIP = -6,       /* a HIP runtime call or launch failed */
+  RA_ERR_ARG = -7        /* scale not finite and > 0 (or 0 for the default) */
+};
+
+enum { RA_BF16 = 0, RA_F32 = 1 };
+
+typedef struct ra_problem {
+  int32_t n_q;    /* queries on this rank, >= 0 */
+  int32_t n_k;    /* keys per key/value block, >= 0 (all blocks equal) */
+  int32_t h_q;    /* query heads, 1..256 */
+  int32_t h_kv;   /* key/value heads, h_q % h_kv == 0 */
+  int32_t d_k;    /* head width: 64 or 128 */
+  int32_t dtype;  /* RA_BF16 or RA_F32: element type of q, k, v */
+  int32_t causal; /* 1: key j visible to query i iff k_pos[j] <= q_pos[i]; 0: all */
+  float scale;    /* softmax scale; 0 selects 1/sqrt(d_k) */
+} ra_problem;
+
+/* Fill the state with the empty row: m = -inf, l = 0, o = 0. */
+ra_status ra_state_init(const ra_problem* p, float* m, float* l, float* o, void* stream);
+
+/*
+ * One ring step: fold the attention of q against one key/value block into the
+ * state (m, l, o) in place.  Exactly the online-softmax rescale of the pages
+ * (new max, old totals times exp(old max - new max), plus this block's terms).
+ * Rows that see no key of the block are left untouched.
+ * work: optional device int64[3] that gets += {full, masked, skipped} tile
+ * counts of this block (query tiles x key tiles of ra_tile_shape(), counted
+ * for head 0 only since the classes do not depend on the head); NULL skips it.
+ */
+ra_status ra_step(const ra_problem* p, const void* q, const int32_t* q_pos,
+                  const void* k, const void* v, const int32_t* k_pos,
+                  float* m, float* l, float* o, int64_t* work, void* stream);
+
+/* Normalise: out = o / l, lse = m + ln l; a row with l == 0 gives out = 0,
+ * lse = -inf. */
+ra_status ra_finalize(const ra_problem* p, const float* m, const float* l, const float* o,
+                      float* out, float* lse, void* stream);
+
+/* Bytes of device workspace ra_forward needs: the running state and two
+ * staging slots for incoming key/value blocks (the ring's "one block being
+ * computed plus the one arriving"). */
+size_t ra_forward_workspace_bytes(const ra_problem* p);
+
+/*
+ * The whole rank share: n_cp ring steps then normalisation.
+ * k_blocks, v_blocks, k_pos_blocks: HOST arrays of n_cp device pointers, in
+ * ring order; entry 0 is the rank's own block (used in place), and block b
+ * is the one received at step b.  Each block b >= 1 is copied into a staging
+ * slot of the workspace on side_stream while step b-1 computes on
+ * main_stream -- a one-GPU stand-in for the ring receive -- with events so a
+ * slot is never overwritten before its step has read it.  If side_stream is
+ * NULL or equal to main_stream the copies run on main_stream.
+ * out, lse: results.  work: optional device int64[3], zeroed and then filled
+ * with the tile counts summed over all steps.  staged_bytes: optional host
+ * pointer, receives the key/value bytes copied into staging slots
+ * ((n_cp - 1) blocks of 2 * h_kv * n_k * d_k elements).
+ * The workspace contents after the call are unspecified.  Work on
+ * main_stream after the call sees the results; nothing is left pending on
+ * side_stream that touches caller memory.
+ */
+ra_status ra_forward(const ra_problem* p, int32_t n_cp, const void* q, const int32_t* q_pos,
+                     const void* const* k_blocks, const void* const* v_blocks,
+                     const int32_t* const* k_pos_blocks, void* workspace, size_t ws_bytes,
+                     float* out, float* lse, int64_t* work, int64_t* staged_bytes,
+                     void* main_stream, void* side_stream);
+
+/* Query-tile rows (bm) and key-tile columns (bn) the tile counters use. */
+ra_status ra_tile_shape(const ra_problem* p, int32_t* bm, int32_t* bn);
+
+/* Static description of a status code. */
+const char* ra_status_string(ra_status s);
+
+/* ABI version of this header (bumped on any incompatible change). */
+int32_t ra_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_H */

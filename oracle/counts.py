@@ -84,25 +84,34 @@ def tile_work(q_pos, k_pos, BM, BN, causal=True):
     each may be short).  A tile pair is *full* if every (query, key) pair in it
     is visible, *skipped* if none is, and *masked* otherwise.  Returns
     (full, masked, skipped).  The classes do not depend on the head.
+
+    Computed by counting the visible pairs of every tile (query rows in
+    slices so the visibility matrix stays small) and comparing the count with
+    the tile's size.
     """
     q_pos = np.asarray(q_pos, dtype=np.int64)
     k_pos = np.asarray(k_pos, dtype=np.int64)
     n_q, n_k = q_pos.size, k_pos.size
+    if n_q == 0 or n_k == 0:
+        return 0, 0, 0
+    n_qt, n_kt = -(-n_q // BM), -(-n_k // BN)
+    if not causal:
+        return n_qt * n_kt, 0, 0
+    col_starts = np.arange(0, n_k, BN)
+    col_sizes = np.minimum(col_starts + BN, n_k) - col_starts
     full = masked = skipped = 0
-    for i0 in range(0, n_q, BM):
-        qp = q_pos[i0:i0 + BM]
-        for j0 in range(0, n_k, BN):
-            kp = k_pos[j0:j0 + BN]
-            if not causal:
-                full += 1
-                continue
-            vis = kp[None, :] <= qp[:, None]
-            if vis.all():
-                full += 1
-            elif vis.any():
-                masked += 1
-            else:
-                skipped += 1
+    rows_per_slice = max(BM, (1 << 22) // max(1, n_k) // BM * BM)
+    for r0 in range(0, n_q, rows_per_slice):
+        qp = q_pos[r0:r0 + rows_per_slice]
+        vis = (k_pos[None, :] <= qp[:, None]).astype(np.int32)
+        per_col_tile = np.add.reduceat(vis, col_starts, axis=1)  # [rows][n_kt]
+        row_starts = np.arange(0, qp.size, BM)
+        counts = np.add.reduceat(per_col_tile, row_starts, axis=0)  # [tiles][n_kt]
+        row_sizes = np.minimum(row_starts + BM, qp.size) - row_starts
+        sizes = row_sizes[:, None] * col_sizes[None, :]
+        full += int((counts == sizes).sum())
+        skipped += int((counts == 0).sum())
+        masked += int(((counts > 0) & (counts < sizes)).sum())
     return full, masked, skipped
 
 

@@ -1,0 +1,221 @@
+"""Python binding of the ring-attention rank-share library (libra.so).
+
+This layer only marshals arguments: torch tensors become device pointers and
+torch streams become hipStream_t handles; every step of the computation runs
+in the library's HIP kernels.  There is no CPU fallback: when libra.so is
+missing or the device is not a GPU, calls raise.
+
+Entry points mirror include/ra.h: ``state_init``, ``step``, ``finalize``,
+``forward``, ``tile_shape``, ``workspace_bytes``.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+from . import layouts  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libra.so")
+
+RA_BF16, RA_F32 = 0, 1
+
+SYMBOLS = (
+    "ra_state_init", "ra_step", "ra_finalize", "ra_forward_workspace_bytes", "ra_forward",
+    "ra_tile_shape", "ra_status_string", "ra_abi_version",
+)
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("n_q", ctypes.c_int32), ("n_k", ctypes.c_int32), ("h_q", ctypes.c_int32),
+        ("h_kv", ctypes.c_int32), ("d_k", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
+    ]
+
+
+class RAError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib():
+    """Load libra.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m ring_attention_rank_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p
+    P = ctypes.POINTER(Problem)
+    L.ra_state_init.argtypes = [P, vp, vp, vp, vp]
+    L.ra_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, i64p, vp]
+    L.ra_finalize.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    L.ra_forward_workspace_bytes.argtypes = [P]
+    L.ra_forward_workspace_bytes.restype = ctypes.c_size_t
+    L.ra_forward.argtypes = [P, i32, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                             ctypes.POINTER(vp), vp, ctypes.c_size_t, vp, vp, vp,
+                             ctypes.POINTER(ctypes.c_int64), vp, vp]
+    L.ra_tile_shape.argtypes = [P, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.ra_status_string.argtypes = [i32]
+    L.ra_status_string.restype = ctypes.c_char_p
+    L.ra_abi_version.argtypes = []
+    for name in ("ra_state_init", "ra_step", "ra_finalize", "ra_forward", "ra_tile_shape",
+                 "ra_abi_version"):
+        getattr(L, name).restype = i32
+    _lib = L
+    return L
+
+
+def status_string(status):
+    return lib().ra_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != 0:
+        raise RAError(status, where)
+
+
+def problem(n_q, n_k, h_q, h_kv, d_k, dtype, causal=True, scale=None):
+    """Build the ra_problem struct.  ``dtype`` is a torch dtype or RA_* code."""
+    if isinstance(dtype, torch.dtype):
+        dtype = {torch.bfloat16: RA_BF16, torch.float32: RA_F32}.get(dtype, -1)
+    return Problem(int(n_q), int(n_k), int(h_q), int(h_kv), int(d_k), int(dtype),
+                   1 if causal else 0, 0.0 if scale is None else float(scale))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _stream(s=None):
+    if s is None:
+        s = torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need_gpu(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def _problem_from(q, k, causal, scale):
+    h_q, n_q, d_k = q.shape
+    h_kv, n_k, _ = k.shape
+    return problem(n_q, n_k, h_q, h_kv, d_k, q.dtype, causal, scale)
+
+
+def tile_shape(p):
+    bm, bn = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().ra_tile_shape(ctypes.byref(p), ctypes.byref(bm), ctypes.byref(bn)), "ra_tile_shape")
+    return bm.value, bn.value
+
+
+def workspace_bytes(p):
+    return int(lib().ra_forward_workspace_bytes(ctypes.byref(p)))
+
+
+def new_state(h_q, n_q, d_k, device):
+    m = torch.empty((h_q, n_q), dtype=torch.float32, device=device)
+    l = torch.empty((h_q, n_q), dtype=torch.float32, device=device)
+    o = torch.empty((h_q, n_q, d_k), dtype=torch.float32, device=device)
+    return m, l, o
+
+
+def state_init(p, m, l, o, stream=None):
+    _need_gpu(m, l, o)
+    _check(lib().ra_state_init(ctypes.byref(p), _ptr(m), _ptr(l), _ptr(o), _stream(stream)),
+           "ra_state_init")
+
+
+def step(q, q_pos, k, v, k_pos, m, l, o, work=None, causal=True, scale=None, stream=None):
+    """Fold one key/value block into the state (m, l, o) in place."""
+    _need_gpu(q, q_pos, k, v, k_pos, m, l, o, work)
+    p = _problem_from(q, k, causal, scale)
+    _check(lib().ra_step(ctypes.byref(p), _ptr(q), _ptr(q_pos), _ptr(k), _ptr(v), _ptr(k_pos),
+                         _ptr(m), _ptr(l), _ptr(o), _ptr(work), _stream(stream)), "ra_step")
+
+
+def finalize(p, m, l, o, out=None, lse=None, stream=None):
+    _need_gpu(m, l, o)
+    if out is None:
+        out = torch.empty_like(o)
+    if lse is None:
+        lse = torch.empty_like(m)
+    _need_gpu(out, lse)
+    _check(lib().ra_finalize(ctypes.byref(p), _ptr(m), _ptr(l), _ptr(o), _ptr(out), _ptr(lse),
+                             _stream(stream)), "ra_finalize")
+    return out, lse
+
+
+_side_streams = {}
+
+
+def side_stream(device=None):
+    """A per-device side stream (default priority) for ring staging copies."""
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None else device) \
+        if not isinstance(device, torch.device) else device
+    s = _side_streams.get(dev.index)
+    if s is None:
+        s = torch.cuda.Stream(device=dev)
+        _side_streams[dev.index] = s
+    return s
+
+
+class Forward:
+    """A prepared ra_forward call: the pointer arrays, workspace and outputs
+    are built once, so repeated calls only cross the C ABI."""
+
+    def __init__(self, q, q_pos, k_blocks, v_blocks, k_pos_blocks, causal=True, scale=None,
+                 side=True, count_work=True, workspace=None):
+        _need_gpu(q, q_pos, *k_blocks, *v_blocks, *k_pos_blocks)
+        n_cp = len(k_blocks)
+        if not (n_cp == len(v_blocks) == len(k_pos_blocks)) or n_cp < 1:
+            raise ValueError("need n_cp >= 1 blocks of k, v and k_pos")
+        self.p = _problem_from(q, k_blocks[0], causal, scale)
+        self.n_cp = n_cp
+        dev = q.device
+        self.keep = (q, q_pos, list(k_blocks), list(v_blocks), list(k_pos_blocks))
+        arr = ctypes.c_void_p * n_cp
+        self.kp = arr(*[t.data_ptr() for t in k_blocks])
+        self.vp = arr(*[t.data_ptr() for t in v_blocks])
+        self.pp = arr(*[t.data_ptr() for t in k_pos_blocks])
+        nbytes = workspace_bytes(self.p)
+        if workspace is None:
+            workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        self.ws = workspace
+        self.out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        self.work = torch.zeros(3, dtype=torch.int64, device=dev) if count_work else None
+        self.side = side_stream(dev) if side else None
+        self.staged = ctypes.c_int64(0)
+
+    def __call__(self, stream=None):
+        main = torch.cuda.current_stream() if stream is None else stream
+        side = self.side if self.side is not None else None
+        q, q_pos = self.keep[0], self.keep[1]
+        _check(lib().ra_forward(
+            ctypes.byref(self.p), self.n_cp, _ptr(q), _ptr(q_pos), self.kp, self.vp, self.pp,
+            _ptr(self.ws), ctypes.c_size_t(self.ws.numel()), _ptr(self.out), _ptr(self.lse),
+            _ptr(self.work), ctypes.byref(self.staged), _stream(main),
+            ctypes.c_void_p(side.cuda_stream) if side is not None else ctypes.c_void_p(0)),
+            "ra_forward")
+        return self.out, self.lse
+
+
+def forward(q, q_pos, k_blocks, v_blocks, k_pos_blocks, causal=True, scale=None, side=True):
+    """One rank's share: returns (out, lse, work[3] tensor, staged_bytes)."""
+    f = Forward(q, q_pos, k_blocks, v_blocks, k_pos_blocks, causal, scale, side)
+    out, lse = f()
+    return out, lse, f.work, f.staged.value

@@ -1,0 +1,347 @@
+// Host side of the C ABI declared in include/ra.h: argument checks, launch
+// configuration and the ring loop of ra_forward.
+//
+// ra_forward follows the ring of Zero to Frontier, "distributed/context-expert",
+// section "Splitting the sequence, and the one layer that objects": each step
+// attends the local queries to the block held while the next block arrives,
+// and no more than two blocks are held at once.  On one GPU the arrival is a
+// device-to-device copy into one of two staging slots on a side stream,
+// overlapped with the step running on the main stream; events keep a slot
+// from being overwritten before its step has read it.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/ra.h"
+#include "ra_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+
+size_t elem_bytes(int32_t dtype) { return dtype == RA_BF16 ? 2 : 4; }
+
+ra_status check_problem(const ra_problem* p) {
+  if (!p) return RA_ERR_NULL;
+  if (p->dtype != RA_BF16 && p->dtype != RA_F32) return RA_ERR_DTYPE;
+  if (p->n_q < 0 || p->n_k < 0 || p->h_q < 1 || p->h_kv < 1 || p->h_q > ra::kMaxHeads)
+    return RA_ERR_SHAPE;
+  if (p->h_q % p->h_kv != 0) return RA_ERR_SHAPE;
+  if (p->d_k != 64 && p->d_k != 128) return RA_ERR_SHAPE;
+  if (p->causal != 0 && p->causal != 1) return RA_ERR_ARG;
+  if (!(p->scale == 0.f || (std::isfinite(p->scale) && p->scale > 0.f))) return RA_ERR_ARG;
+  // keep every element index of the largest tensor within int64 and every
+  // row index within int32
+  if ((int64_t)p->h_q * p->n_q > INT32_MAX || (int64_t)p->h_kv * p->n_k > INT32_MAX)
+    return RA_ERR_SHAPE;
+  return RA_OK;
+}
+
+float softmax_scale(const ra_problem* p) {
+  return p->scale == 0.f ? 1.0f / std::sqrt((float)p->d_k) : p->scale;
+}
+
+// Launch order of query heads.  Consecutive workgroups go to different XCDs
+// (8 on MI355X, each with its own L2), so slot j of every round of h_q
+// workgroups lands on XCD j % 8.  Heads that share a key/value head are
+// placed on the same XCD where the counts allow, so that XCD's L2 serves the
+// shared block.
+void head_order(const ra_problem* p, uint8_t* head_of) {
+  const int hq = p->h_q, hkv = p->h_kv, g = hq / hkv;
+  const int X = 8;
+  bool done = false;
+  if (hq % X == 0) {
+    const int per = hq / X;  // query heads per XCD
+    if (hkv % X == 0 || (X % hkv == 0)) {
+      for (int j = 0; j < hq; ++j) {
+        int x = j % X, i = j / X;  // XCD, index within the XCD
+        int head;
+        if (hkv % X == 0) {
+          // XCD x takes KV heads x, x+X, ...; per/g of them
+          int kv = x + X * (i / g);
+          head = kv * g + i % g;
+        } else {
+          // X/hkv XCDs share each KV head
+          int kv = x % hkv;
+          int sub = x / hkv;  // which of the sharing XCDs
+          head = kv * g + sub * per + i;
+        }
+        head_of[j] = (uint8_t)head;
+      }
+      done = true;
+    }
+  }
+  if (!done)
+    for (int j = 0; j < hq; ++j) head_of[j] = (uint8_t)j;
+}
+
+ra_status fill_args(const ra_problem* p, ra::StepArgs* a) {
+  std::memset(a, 0, sizeof(*a));
+  a->n_q = p->n_q;
+  a->n_k = p->n_k;
+  a->h_q = p->h_q;
+  a->h_kv = p->h_kv;
+  a->causal = p->causal;
+  a->n_qt = (p->n_q + ra::kRowsPerGroup - 1) / ra::kRowsPerGroup;
+  a->c2 = softmax_scale(p) * 1.4426950408889634f;
+  head_order(p, a->head_of);
+  return RA_OK;
+}
+
+ra_status launch(const ra_problem* p, const ra::StepArgs& a, bool read, bool final_,
+                 hipStream_t s) {
+  if (a.n_qt == 0) return RA_OK;
+  hipError_t e = ra::launch_step(a, p->dtype, p->d_k, read, final_, s);
+  return e == hipSuccess ? RA_OK : RA_ERR_HIP;
+}
+
+struct WsLayout {
+  size_t m, l, o, slot[2], kbytes, pbytes, total;
+};
+
+WsLayout ws_layout(const ra_problem* p) {
+  WsLayout w;
+  const size_t rows = (size_t)p->h_q * p->n_q;
+  w.kbytes = (size_t)p->h_kv * p->n_k * p->d_k * elem_bytes(p->dtype);
+  w.pbytes = (size_t)p->n_k * sizeof(int32_t);
+  size_t off = 0;
+  w.m = off;
+  off = align_up(off + rows * 4);
+  w.l = off;
+  off = align_up(off + rows * 4);
+  w.o = off;
+  off = align_up(off + rows * p->d_k * 4);
+  for (int s = 0; s < 2; ++s) {
+    w.slot[s] = off;  // K, then V, then positions
+    off = align_up(off + w.kbytes);
+    off = align_up(off + w.kbytes);
+    off = align_up(off + w.pbytes);
+  }
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ra_abi_version(void) { return 1; }
+
+const char* ra_status_string(ra_status s) {
+  switch (s) {
+    case RA_OK: return "ok";
+    case RA_ERR_NULL: return "a required pointer is NULL";
+    case RA_ERR_SHAPE: return "sizes out of range (h_q % h_kv, d_k in {64,128}, counts)";
+    case RA_ERR_DTYPE: return "unsupported dtype (RA_BF16 or RA_F32)";
+    case RA_ERR_ALIGN: return "misaligned pointer (16 B for q,k,v,o,out,workspace; 4 B positions,m,l,lse; 8 B work)";
+    case RA_ERR_WORKSPACE: return "workspace too small";
+    case RA_ERR_HIP: return "HIP runtime call or kernel launch failed";
+    case RA_ERR_ARG: return "invalid argument (scale must be finite and > 0, causal 0 or 1)";
+    default: return "unknown status";
+  }
+}
+
+ra_status ra_tile_shape(const ra_problem* p, int32_t* bm, int32_t* bn) {
+  ra_status st = check_problem(p);
+  if (st != RA_OK) return st;
+  if (!bm || !bn) return RA_ERR_NULL;
+  *bm = ra::kRowsPerWave;
+  *bn = ra::kKeysPerTile;
+  return RA_OK;
+}
+
+ra_status ra_state_init(const ra_problem* p, float* m, float* l, float* o, void* stream) {
+  ra_status st = check_problem(p);
+  if (st != RA_OK) return st;
+  const int64_t rows = (int64_t)p->h_q * p->n_q;
+  if (rows == 0) return RA_OK;
+  if (!m || !l || !o) return RA_ERR_NULL;
+  if (!aligned4(m) || !aligned4(l) || !aligned16(o)) return RA_ERR_ALIGN;
+  hipError_t e = ra::launch_state_init(m, l, o, rows, p->d_k, (hipStream_t)stream);
+  return e == hipSuccess ? RA_OK : RA_ERR_HIP;
+}
+
+ra_status ra_step(const ra_problem* p, const void* q, const int32_t* q_pos, const void* k,
+                  const void* v, const int32_t* k_pos, float* m, float* l, float* o,
+                  int64_t* work, void* stream) {
+  ra_status st = check_problem(p);
+  if (st != RA_OK) return st;
+  if (p->n_q == 0) return RA_OK;
+  if (!q || !q_pos || !m || !l || !o) return RA_ERR_NULL;
+  if (p->n_k > 0 && (!k || !v || !k_pos)) return RA_ERR_NULL;
+  if (!aligned16(q) || !aligned4(q_pos) || !aligned4(m) || !aligned4(l) || !aligned16(o) ||
+      (work && !aligned8(work)))
+    return RA_ERR_ALIGN;
+  if (p->n_k > 0 && (!aligned16(k) || !aligned16(v) || !aligned4(k_pos))) return RA_ERR_ALIGN;
+  ra::StepArgs a;
+  fill_args(p, &a);
+  a.q = q;
+  a.q_pos = q_pos;
+  a.k = k;
+  a.v = v;
+  a.k_pos = k_pos;
+  a.m_in = m;
+  a.l_in = l;
+  a.o_in = o;
+  a.m_out = m;
+  a.l_out = l;
+  a.o_out = o;
+  a.work = reinterpret_cast<unsigned long long*>(work);
+  return launch(p, a, true, false, (hipStream_t)stream);
+}
+
+ra_status ra_finalize(const ra_problem* p, const float* m, const float* l, const float* o,
+                      float* out, float* lse, void* stream) {
+  ra_status st = check_problem(p);
+  if (st != RA_OK) return st;
+  const int64_t rows = (int64_t)p->h_q * p->n_q;
+  if (rows == 0) return RA_OK;
+  if (!m || !l || !o || !out || !lse) return RA_ERR_NULL;
+  if (!aligned4(m) || !aligned4(l) || !aligned16(o) || !aligned16(out) || !aligned4(lse))
+    return RA_ERR_ALIGN;
+  hipError_t e = ra::launch_finalize(m, l, o, out, lse, rows, p->d_k, (hipStream_t)stream);
+  return e == hipSuccess ? RA_OK : RA_ERR_HIP;
+}
+
+size_t ra_forward_workspace_bytes(const ra_problem* p) {
+  if (check_problem(p) != RA_OK) return 0;
+  return ws_layout(p).total;
+}
+
+ra_status ra_forward(const ra_problem* p, int32_t n_cp, const void* q, const int32_t* q_pos,
+                     const void* const* k_blocks, const void* const* v_blocks,
+                     const int32_t* const* k_pos_blocks, void* workspace, size_t ws_bytes,
+                     float* out, float* lse, int64_t* work, int64_t* staged_bytes,
+                     void* main_stream, void* side_stream) {
+  ra_status st = check_problem(p);
+  if (st != RA_OK) return st;
+  if (n_cp < 1) return RA_ERR_SHAPE;
+  if (!k_blocks || !v_blocks || !k_pos_blocks) return RA_ERR_NULL;
+  const WsLayout w = ws_layout(p);
+  if (p->n_q > 0) {
+    if (!q || !q_pos || !out || !lse) return RA_ERR_NULL;
+    if (!aligned16(q) || !aligned4(q_pos) || !aligned16(out) || !aligned4(lse))
+      return RA_ERR_ALIGN;
+  }
+  if (work && !aligned8(work)) return RA_ERR_ALIGN;
+  if (p->n_k > 0) {
+    for (int b = 0; b < n_cp; ++b) {
+      if (!k_blocks[b] || !v_blocks[b] || !k_pos_blocks[b]) return RA_ERR_NULL;
+      if (!aligned16(k_blocks[b]) || !aligned16(v_blocks[b]) || !aligned4(k_pos_blocks[b]))
+        return RA_ERR_ALIGN;
+    }
+  }
+  if (!workspace) return RA_ERR_NULL;
+  if (!aligned16(workspace)) return RA_ERR_ALIGN;
+  if (ws_bytes < w.total) return RA_ERR_WORKSPACE;
+
+  hipStream_t ms = (hipStream_t)main_stream;
+  hipStream_t ss = (hipStream_t)side_stream;
+  const bool use_side = ss != nullptr && ss != ms;
+  char* ws = (char*)workspace;
+  float* m = (float*)(ws + w.m);
+  float* l = (float*)(ws + w.l);
+  float* o = (float*)(ws + w.o);
+
+  if (staged_bytes) *staged_bytes = 0;
+  if (work) {
+    if (ra::launch_zero_i64(work, 3, ms) != hipSuccess) return RA_ERR_HIP;
+  }
+  if (p->n_q == 0) return RA_OK;
+
+  ra::StepArgs a;
+  fill_args(p, &a);
+  a.q = q;
+  a.q_pos = q_pos;
+  a.m_in = m;
+  a.l_in = l;
+  a.o_in = o;
+  a.m_out = m;
+  a.l_out = l;
+  a.o_out = o;
+  a.out = out;
+  a.lse = lse;
+  a.work = reinterpret_cast<unsigned long long*>(work);
+
+  // Events: slot s staged (side -> main), slot s consumed (main -> side), and
+  // the caller's prior work on main (main -> side) before the first copy.
+  hipEvent_t ev_staged[2] = {nullptr, nullptr}, ev_used[2] = {nullptr, nullptr},
+             ev_start = nullptr;
+  ra_status result = RA_OK;
+  int64_t staged = 0;
+  auto mk = [](hipEvent_t* e) {
+    return hipEventCreateWithFlags(e, hipEventDisableTiming) == hipSuccess;
+  };
+  if (use_side && n_cp > 1) {
+    if (!mk(&ev_start) || !mk(&ev_staged[0]) || !mk(&ev_staged[1]) || !mk(&ev_used[0]) ||
+        !mk(&ev_used[1])) {
+      result = RA_ERR_HIP;
+      goto cleanup;
+    }
+    if (hipEventRecord(ev_start, ms) != hipSuccess ||
+        hipStreamWaitEvent(ss, ev_start, 0) != hipSuccess) {
+      result = RA_ERR_HIP;
+      goto cleanup;
+    }
+  }
+
+  for (int b = 0; b < n_cp; ++b) {
+    const bool first = b == 0, last = b == n_cp - 1;
+    if (first) {
+      a.k = k_blocks[0];
+      a.v = v_blocks[0];
+      a.k_pos = k_pos_blocks[0];
+    } else {
+      const int s = b & 1;
+      char* slot = ws + w.slot[s];
+      void* dk = slot;
+      void* dv = slot + align_up(w.kbytes);
+      void* dp = slot + 2 * align_up(w.kbytes);
+      hipStream_t cs = use_side ? ss : ms;
+      if (use_side && b >= 3) {
+        // slot s was last read by step b-2
+        if (hipStreamWaitEvent(ss, ev_used[s], 0) != hipSuccess) { result = RA_ERR_HIP; goto cleanup; }
+      }
+      if (w.kbytes) {
+        if (hipMemcpyAsync(dk, k_blocks[b], w.kbytes, hipMemcpyDeviceToDevice, cs) != hipSuccess ||
+            hipMemcpyAsync(dv, v_blocks[b], w.kbytes, hipMemcpyDeviceToDevice, cs) != hipSuccess ||
+            hipMemcpyAsync(dp, k_pos_blocks[b], w.pbytes, hipMemcpyDeviceToDevice, cs) != hipSuccess) {
+          result = RA_ERR_HIP;
+          goto cleanup;
+        }
+      }
+      staged += 2 * (int64_t)w.kbytes;
+      if (use_side) {
+        if (hipEventRecord(ev_staged[s], ss) != hipSuccess ||
+            hipStreamWaitEvent(ms, ev_staged[s], 0) != hipSuccess) {
+          result = RA_ERR_HIP;
+          goto cleanup;
+        }
+      }
+      a.k = dk;
+      a.v = dv;
+      a.k_pos = (const int32_t*)dp;
+    }
+    result = launch(p, a, /*read=*/!first, /*final=*/last, ms);
+    if (result != RA_OK) goto cleanup;
+    if (use_side && !first && b + 2 < n_cp) {
+      if (hipEventRecord(ev_used[b & 1], ms) != hipSuccess) { result = RA_ERR_HIP; goto cleanup; }
+    }
+  }
+  if (staged_bytes) *staged_bytes = staged;
+
+cleanup:
+  for (hipEvent_t e : {ev_start, ev_staged[0], ev_staged[1], ev_used[0], ev_used[1]})
+    if (e) hipEventDestroy(e);
+  return result;
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Internal interface between the C-ABI host code and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kWavesPerGroup = 4;  // one wave per SIMD of a CU
+constexpr int kRowsPerWave = 64;   // query rows a wave owns (two 32-row MFMA blocks)
+constexpr int kRowsPerGroup = kWavesPerGroup * kRowsPerWave;  // 256
+constexpr int kKeysPerTile = 64;   // keys per LDS tile
+constexpr int kMaxHeads = 256;
+
+// Arguments of one ring-step launch (one key/value block against all local
+// queries of all heads).  READ selects whether the state is read (else it
+// starts empty); FINAL whether the result is normalised into out/lse (else
+// the state is written back).
+struct StepArgs {
+  const void* q;
+  const int32_t* q_pos;
+  const void* k;
+  const void* v;
+  const int32_t* k_pos;
+  const float* m_in;
+  const float* l_in;
+  const float* o_in;
+  float* m_out;
+  float* l_out;
+  float* o_out;
+  float* out;
+  float* lse;
+  unsigned long long* work;  // int64[3] {full, masked, skipped} or null
+  int32_t n_q, n_k, h_q, h_kv, causal;
+  int32_t n_qt;              // query tiles of kRowsPerGroup rows
+  float c2;                  // scale * log2(e): scores go to base-2 units
+  uint8_t head_of[kMaxHeads];  // launch-order slot -> query head (L2 locality)
+};
+
+hipError_t launch_step(const StepArgs& a, int dtype, int d_k, bool read, bool final_,
+                       hipStream_t stream);
+hipError_t launch_state_init(float* m, float* l, float* o, int64_t rows, int d_k,
+                             hipStream_t stream);
+hipError_t launch_finalize(const float* m, const float* l, const float* o, float* out,
+                           float* lse, int64_t rows, int d_k, hipStream_t stream);
+hipError_t launch_zero_i64(int64_t* p, int n, hipStream_t stream);
+
+}  // namespace ra

@@ -1,0 +1,112 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol that
+include/ra.h declares, and rejects bad arguments on the host before any
+device work (these calls never reach the HIP runtime)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import ring_attention_rank_amd as ra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ra.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ra.LIB_PATH), reason="libra.so not built")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, HIP, ARG = 0, -1, -2, -3, -4, -5, -6, -7
+FAKE = 1 << 40  # an aligned address that is never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(ra_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(ra.SYMBOLS)
+    L = ra.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.ra_abi_version() == 1
+
+
+def test_status_strings():
+    for s in (OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, HIP, ARG):
+        assert ra.status_string(s)
+    assert ra.status_string(12345) == "unknown status"
+
+
+def good(**kw):
+    d = dict(n_q=256, n_k=256, h_q=4, h_kv=2, d_k=128, dtype=ra.RA_BF16, causal=True, scale=None)
+    d.update(kw)
+    return ra.problem(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h_q=3, h_kv=2), SHAPE),
+    (dict(d_k=96), SHAPE),
+    (dict(n_q=-1), SHAPE),
+    (dict(h_q=0), SHAPE),
+    (dict(h_q=512, h_kv=1), SHAPE),
+    (dict(dtype=7), DTYPE),
+    (dict(scale=-1.0), ARG),
+    (dict(scale=float("inf")), ARG),
+])
+def test_bad_problem(kw, status):
+    p = good(**kw)
+    bm, bn = ctypes.c_int32(), ctypes.c_int32()
+    assert ra.lib().ra_tile_shape(ctypes.byref(p), ctypes.byref(bm), ctypes.byref(bn)) == status
+    assert ra.lib().ra_forward_workspace_bytes(ctypes.byref(p)) == 0
+    v = ctypes.c_void_p(FAKE)
+    assert ra.lib().ra_step(ctypes.byref(p), v, v, v, v, v, v, v, v, None, None) == status
+
+
+def test_null_problem():
+    v = ctypes.c_void_p(FAKE)
+    assert ra.lib().ra_step(None, v, v, v, v, v, v, v, v, None, None) == NULL
+    assert ra.lib().ra_state_init(None, v, v, v, None) == NULL
+
+
+def test_tile_shape_and_workspace():
+    p = good()
+    assert ra.tile_shape(p) == (64, 64)
+    n = ra.workspace_bytes(p)
+    # state (m, l, o in fp32) + 2 slots of K, V (bf16) and positions
+    state = 4 * 256 * 4 * 2 + 4 * 256 * 128 * 4
+    slots = 2 * (2 * 2 * 256 * 128 * 2 + 256 * 4)
+    assert state + slots <= n <= state + slots + 16 * 256
+
+
+def test_step_pointer_checks():
+    p = good()
+    v = ctypes.c_void_p(FAKE)
+    z = ctypes.c_void_p(0)
+    L = ra.lib()
+    assert L.ra_step(ctypes.byref(p), z, v, v, v, v, v, v, v, None, None) == NULL
+    assert L.ra_step(ctypes.byref(p), v, v, v, z, v, v, v, v, None, None) == NULL
+    odd = ctypes.c_void_p(FAKE + 8)
+    assert L.ra_step(ctypes.byref(p), odd, v, v, v, v, v, v, v, None, None) == ALIGN
+    assert L.ra_step(ctypes.byref(p), v, v, odd, v, v, v, v, v, None, None) == ALIGN
+    assert L.ra_step(ctypes.byref(p), v, v, v, v, v, v, v, odd, None, None) == ALIGN
+    assert L.ra_step(ctypes.byref(p), v, ctypes.c_void_p(FAKE + 2), v, v, v, v, v, v, None, None) == ALIGN
+
+
+def test_forward_checks():
+    p = good()
+    L = ra.lib()
+    v = ctypes.c_void_p(FAKE)
+    arr = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    staged = ctypes.c_int64(0)
+    need = ra.workspace_bytes(p)
+    args = lambda ncp, ws, wsb: (ctypes.byref(p), ncp, v, v, arr, arr, arr, ws, wsb, v, v,
+                                 None, ctypes.byref(staged), None, None)
+    assert L.ra_forward(*args(0, v, need)) == SHAPE
+    assert L.ra_forward(*args(2, v, need - 1)) == WORKSPACE
+    assert L.ra_forward(*args(2, ctypes.c_void_p(0), need)) == NULL
+    assert L.ra_forward(*args(2, ctypes.c_void_p(FAKE + 4), need)) == ALIGN
+    bad = (ctypes.c_void_p * 2)(FAKE, 0)
+    assert L.ra_forward(ctypes.byref(p), 2, v, v, bad, arr, arr, v, need, v, v, None,
+                        ctypes.byref(staged), None, None) == NULL

@@ -1,0 +1,231 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle, at
+sizes the oracle finishes in seconds: element by element, tile counters bit
+exact, staged bytes exact.  Edge cases: ragged tiles, empty blocks, rows that
+see nothing, non-causal, explicit scale, both dtypes and head widths."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ring_attention_rank_amd as ra
+import synth
+from gpu_util import TOL, Share, max_err
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def run_forward(sh, side=True):
+    out, lse, work, staged = ra.forward(sh.gq, sh.gq_pos, sh.gk, sh.gv, sh.gk_pos,
+                                        causal=sh.case.causal, side=side)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy(), work.cpu().numpy(), staged
+
+
+def check_share(sh, label):
+    print(f"[parity] {label}: T={sh.case.T} n_cp={sh.case.n_cp} rank={sh.rank} "
+          f"h={sh.case.h_q}/{sh.case.h_kv} d={sh.case.d_k} {sh.case.dtype}", flush=True)
+    out, lse, work, staged = run_forward(sh)
+    ro, rl = sh.oracle()
+    tol = TOL[sh.case.dtype]
+    eo, el = max_err(out, ro), max_err(lse, rl)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    assert eo <= tol["out"], f"{label}: out max-abs {eo}"
+    assert el <= tol["lse"], f"{label}: lse max-abs {el}"
+    bm, bn = ra.tile_shape(ra.problem(1, 1, sh.case.h_q, sh.case.h_kv, sh.case.d_k,
+                                      torch.float32 if sh.case.dtype == "f32" else torch.bfloat16))
+    assert list(work) == list(sh.tile_work(bm, bn)), label
+    assert staged == sh.staged_bytes()
+    return eo, el
+
+
+def test_tiny_f32_contiguous_full_size():
+    case = synth.case_by_name("tiny_f32_contiguous")
+    sh = Share(case, 2).to_gpu()
+    check_share(sh, case.name)
+
+
+@pytest.mark.parametrize("name,T,n_cp,ranks", [
+    ("llama8b_gqa_zigzag", 4096, 4, (0, 1, 2, 3)),
+    ("llama70b_stage_share", 8192, 16, (0, 15)),
+    ("llama405b_stage_share", 8192, 16, (0, 7)),
+    ("million_striped_mha", 8192, 16, (0, 15)),
+    ("million_striped_mha", 16384, 64, (3,)),
+])
+def test_reduced_configs(name, T, n_cp, ranks):
+    case = synth.case_by_name(name)
+    for r in ranks:
+        sh = Share(case, r, T=T, n_cp=n_cp).to_gpu()
+        check_share(sh, f"{name}@T{T}/r{r}")
+
+
+def _custom_share(rng, dtype, d_k, h_q, h_kv, n_q, n_k, n_cp, causal=True):
+    """Random strictly increasing positions, ragged sizes, blocks in order."""
+    case = synth.Case("custom", T=0, n_cp=n_cp, layout="custom", ranks=(0,), h_q=h_q,
+                      h_kv=h_kv, d_k=d_k, dtype=dtype, seed=77, causal=causal)
+    sh = Share.__new__(Share)
+    sh.case, sh.rank = case, 0
+    span = 4 * (n_q + n_k * n_cp) + 10
+    sh.q_pos = np.sort(rng.choice(span, n_q, replace=False)).astype(np.int64)
+    sh.k_pos = [np.sort(rng.choice(span, n_k, replace=False)).astype(np.int64) for _ in range(n_cp)]
+    sh.sources = list(range(n_cp))
+    bf = dtype == "bf16"
+    q = rng.standard_normal((h_q, n_q, d_k)).astype(np.float32)
+    sh.q = synth.round_to_bf16(q) if bf else q
+    sh.k, sh.v = [], []
+    for _ in range(n_cp):
+        k = rng.standard_normal((h_kv, n_k, d_k)).astype(np.float32)
+        v = rng.standard_normal((h_kv, n_k, d_k)).astype(np.float32)
+        sh.k.append(synth.round_to_bf16(k) if bf else k)
+        sh.v.append(synth.round_to_bf16(v) if bf else v)
+    return sh.to_gpu()
+
+
+@pytest.mark.parametrize("dtype,d_k", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
+@pytest.mark.parametrize("n_q,n_k,h_q,h_kv", [(300, 200, 4, 2), (64, 64, 2, 1), (1, 70, 3, 3),
+                                              (517, 129, 2, 2)])
+def test_ragged_and_small(dtype, d_k, n_q, n_k, h_q, h_kv):
+    rng = np.random.default_rng(n_q * 7 + n_k)
+    sh = _custom_share(rng, dtype, d_k, h_q, h_kv, n_q, n_k, 3)
+    check_share(sh, f"ragged {dtype} d{d_k} nq{n_q} nk{n_k}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_noncausal(dtype):
+    rng = np.random.default_rng(11)
+    sh = _custom_share(rng, dtype, 128, 4, 1, 200, 100, 3, causal=False)
+    check_share(sh, f"noncausal {dtype}")
+
+
+def test_explicit_scale():
+    rng = np.random.default_rng(12)
+    sh = _custom_share(rng, "bf16", 128, 2, 1, 128, 128, 2)
+    out, lse, _, _ = ra.forward(sh.gq, sh.gq_pos, sh.gk, sh.gv, sh.gk_pos, scale=0.05)
+    ro, rl = oracle.ring_forward_ref(sh.q, sh.q_pos, sh.k, sh.v, sh.k_pos, scale=0.05)
+    assert max_err(out.cpu(), ro) <= 1e-2 and max_err(lse.cpu(), rl) <= 1e-3
+
+
+def test_step_by_step_matches_oracle_and_forward():
+    """state_init + ra_step per block + ra_finalize: after every step the
+    state finalises to the oracle's, and the end result equals ra_forward
+    bit for bit."""
+    case = synth.case_by_name("llama405b_stage_share")
+    sh = Share(case, 3, T=8192, n_cp=8).to_gpu()
+    h_q, n_q, d = sh.gq.shape
+    p = ra.problem(n_q, sh.gk[0].shape[1], h_q, sh.gk[0].shape[0], d, torch.bfloat16)
+    m, l, o = ra.new_state(h_q, n_q, d, "cuda")
+    ra.state_init(p, m, l, o)
+    work = torch.zeros(3, dtype=torch.int64, device="cuda")
+    st = oracle.init_state(h_q, n_q, d)
+    for b in range(len(sh.gk)):
+        ra.step(sh.gq, sh.gq_pos, sh.gk[b], sh.gv[b], sh.gk_pos[b], m, l, o, work)
+        st = oracle.ring_step_ref(sh.q, sh.q_pos, sh.k[b], sh.v[b], sh.k_pos[b], st)
+        out, lse = ra.finalize(p, m, l, o)
+        ro, rl = oracle.finalize(*st)
+        assert max_err(out.cpu(), ro) <= 1e-2, b
+        assert max_err(lse.cpu(), rl) <= 1e-3, b
+        # the state itself: m is the running maximum, l and o relative to it
+        mc = m.cpu().numpy()
+        fin = np.isfinite(st[0])
+        assert np.array_equal(np.isfinite(mc), fin)
+        assert max_err(mc[fin], st[0][fin]) <= 1e-3
+    fo, fl, fw, _ = run_forward(sh)
+    assert np.array_equal(out.cpu().numpy(), fo) and np.array_equal(lse.cpu().numpy(), fl)
+    assert np.array_equal(work.cpu().numpy(), fw)
+
+
+def test_checkpoint_resume_bitwise():
+    """The state after k steps, saved to the host and restored, resumes to the
+    uninterrupted result bit for bit."""
+    case = synth.case_by_name("million_striped_mha")
+    sh = Share(case, 1, T=8192, n_cp=8).to_gpu()
+    h_q, n_q, d = sh.gq.shape
+    p = ra.problem(n_q, sh.gk[0].shape[1], h_q, sh.gk[0].shape[0], d, torch.bfloat16)
+
+    def run(cut):
+        m, l, o = ra.new_state(h_q, n_q, d, "cuda")
+        ra.state_init(p, m, l, o)
+        for b in range(len(sh.gk)):
+            if b == cut:
+                saved = [x.cpu() for x in (m, l, o)]
+                m, l, o = [x.cuda() for x in saved]
+            ra.step(sh.gq, sh.gq_pos, sh.gk[b], sh.gv[b], sh.gk_pos[b], m, l, o)
+        return [x.cpu().numpy() for x in ra.finalize(p, m, l, o)]
+
+    ref = run(-1)
+    for cut in (1, 4, 7):
+        got = run(cut)
+        assert all(np.array_equal(a, b) for a, b in zip(ref, got))
+
+
+def test_untouched_rows_and_empty_blocks():
+    """A block wholly after every query leaves the state bit-identical; an
+    empty block (n_k = 0) too; a share with no keys finalises to 0 / -inf."""
+    rng = np.random.default_rng(13)
+    sh = _custom_share(rng, "bf16", 128, 2, 1, 256, 128, 1)
+    h_q, n_q, d = sh.gq.shape
+    p = ra.problem(n_q, 128, h_q, 1, d, torch.bfloat16)
+    m, l, o = ra.new_state(h_q, n_q, d, "cuda")
+    ra.state_init(p, m, l, o)
+    ra.step(sh.gq, sh.gq_pos, sh.gk[0], sh.gv[0], sh.gk_pos[0], m, l, o)
+    before = [x.clone() for x in (m, l, o)]
+    future = sh.gk_pos[0] + int(sh.q_pos.max()) + 1
+    work = torch.zeros(3, dtype=torch.int64, device="cuda")
+    ra.step(sh.gq, sh.gq_pos, sh.gk[0], sh.gv[0], future, m, l, o, work)
+    for a, b in zip(before, (m, l, o)):
+        assert torch.equal(a, b)
+    assert work.tolist() == [0, 0, 4 * 2]  # 4 query tiles x 2 key tiles, all skipped
+    ek = torch.empty((1, 0, d), dtype=torch.bfloat16, device="cuda")
+    ep = torch.empty((0,), dtype=torch.int32, device="cuda")
+    ra.step(sh.gq, sh.gq_pos, ek, ek, ep, m, l, o)
+    for a, b in zip(before, (m, l, o)):
+        assert torch.equal(a, b)
+    out, lse, work, staged = ra.forward(sh.gq, sh.gq_pos, [ek, ek], [ek, ek], [ep, ep])
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    assert work.tolist() == [0, 0, 0] and staged == 0
+
+
+def test_empty_queries():
+    d = 128
+    q = torch.empty((2, 0, d), dtype=torch.bfloat16, device="cuda")
+    qp = torch.empty((0,), dtype=torch.int32, device="cuda")
+    k = torch.randn((1, 64, d), device="cuda").to(torch.bfloat16)
+    kp = torch.arange(64, dtype=torch.int32, device="cuda")
+    out, lse, work, staged = ra.forward(q, qp, [k], [k], [kp])
+    assert out.shape == (2, 0, d) and work.tolist() == [0, 0, 0]
+
+
+def test_deterministic_and_staging_order_independent():
+    """Repeat runs, runs without the side stream and runs whose side stream is
+    held back by a spin kernel all give the same bits."""
+    case = synth.case_by_name("llama70b_stage_share")
+    sh = Share(case, 0, T=16384, n_cp=16).to_gpu()
+    a = run_forward(sh)
+    b = run_forward(sh)
+    c = run_forward(sh, side=False)
+    side = ra.side_stream()
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)  # ~10 ms: staging starts late
+    d = run_forward(sh)
+    for x in (b, c, d):
+        assert np.array_equal(a[0], x[0]) and np.array_equal(a[1], x[1])
+        assert np.array_equal(a[2], x[2]) and a[3] == x[3]
+
+
+def test_work_counts_give_pages_half_blocks():
+    """Tile counters reproduce the pages' causal work: contiguous rank i does
+    2i+1 half-blocks, zigzag ranks all do 4*n_cp."""
+    n_cp = 4
+    for layout, chunk in (("contiguous", 1024), ("zigzag", 512)):
+        case = synth.Case("w", T=4096, n_cp=n_cp, layout=layout, ranks=(0,), h_q=2, h_kv=1,
+                          d_k=128, dtype="bf16", seed=5)
+        got = []
+        for r in range(n_cp):
+            sh = Share(case, r).to_gpu()
+            _, _, work, _ = run_forward(sh)
+            got.append(oracle.half_blocks_from_tiles(int(work[0]), int(work[1]), chunk, 64, 64))
+        if layout == "contiguous":
+            assert got == [2 * i + 1 for i in range(n_cp)]
+        else:
+            assert got == [4 * n_cp] * n_cp
