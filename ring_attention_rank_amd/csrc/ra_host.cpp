@@ -91,6 +91,7 @@ ra_status fill_args(const ra_problem* p, ra::StepArgs* a) {
   a->h_kv = p->h_kv;
   a->causal = p->causal;
   a->n_qt = (p->n_q + ra::kRowsPerGroup - 1) / ra::kRowsPerGroup;
+  a->n_pairs = (a->n_qt + 1) / 2;
   a->c2 = softmax_scale(p) * 1.4426950408889634f;
   head_order(p, a->head_of);
   return RA_OK;

@@ -8,8 +8,8 @@ namespace ra {
 
 constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kWavesPerGroup = 4;  // one wave per SIMD of a CU
-constexpr int kRowsPerWave = 64;   // query rows a wave owns (two 32-row MFMA blocks)
-constexpr int kRowsPerGroup = kWavesPerGroup * kRowsPerWave;  // 256
+constexpr int kRowsPerWave = 32;   // query rows a wave owns (one 32-row MFMA block)
+constexpr int kRowsPerGroup = kWavesPerGroup * kRowsPerWave;  // 128
 constexpr int kKeysPerTile = 64;   // keys per LDS tile
 constexpr int kMaxHeads = 256;
 
@@ -34,6 +34,7 @@ struct StepArgs {
   unsigned long long* work;  // int64[3] {full, masked, skipped} or null
   int32_t n_q, n_k, h_q, h_kv, causal;
   int32_t n_qt;              // query tiles of kRowsPerGroup rows
+  int32_t n_pairs;           // workgroups per head: tile t is paired with tile n_qt-1-t
   float c2;                  // scale * log2(e): scores go to base-2 units
   uint8_t head_of[kMaxHeads];  // launch-order slot -> query head (L2 locality)
 };

@@ -3,34 +3,39 @@
 // What a step computes (Zero to Frontier, "distributed/context-expert",
 // section "Splitting the sequence, and the one layer that objects"): every
 // local query meets one key/value block; its running maximum, running sum of
-// exponentials and running weighted sum of values are rescaled whenever the
-// block brings a larger score, then the block's terms are added.  Done one
-// 64-key tile at a time inside the block, this is the blockwise online
-// softmax the "Context Parallelism (CP)" concept page names in "Key math /
-// How it works".
+// exponentials and running weighted sum of values are rescaled when the block
+// brings a larger score, then the block's terms are added.  Done one 64-key
+// tile at a time inside the block, this is the blockwise online softmax the
+// "Context Parallelism (CP)" concept page names in "Key math / How it works".
 //
 // Mapping onto CDNA4:
-//  * A workgroup is 4 waves (one per SIMD) and owns 256 consecutive query
-//    rows of one head; each wave owns 64 rows as two 32-row MFMA blocks.
+//  * A workgroup is 4 waves and owns a pair of 128-row query tiles of one
+//    head (tile t and its mirror n_qt-1-t, processed in turn, so causal
+//    triangles and zigzag steps give every workgroup the same work).  Each
+//    wave owns 32 query rows.  A wave needs at most 256 registers, so two
+//    workgroups can share a CU (two waves per SIMD).
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
 //    (fp32 inputs: v_mfma_f32_32x32x2_f32).  K is the A operand, read from
-//    LDS; Q is the B operand and stays in registers for the whole block.  In
-//    the S^T accumulator every lane holds one query column and 16 keys, so
-//    row max and row sum are in-lane, plus one v_permlane32_swap between the
-//    two half-waves.
-//  * The accumulator rows are mapped to keys through sigma (swap of index
-//    bits 2 and 3), which makes each half-wave's 8 P values of a 16-key step
-//    8 consecutive keys.  P^T then feeds the PV MFMA (O^T = V^T P^T) as the B
-//    operand straight from the accumulators, and V^T is staged in LDS so the
-//    A operand is one 16-byte read.
-//  * K and V^T tiles are double-buffered in LDS (rows padded by 16 bytes
-//    against bank conflicts), loaded from HBM with 16-byte loads one tile
-//    ahead.
+//    LDS; Q is the B operand and stays in registers.  In the S^T accumulator
+//    every lane holds one query column and 16 keys, so row max and row sum are
+//    in-lane, plus one v_permlane32_swap between the two half-waves.
+//  * Accumulator rows map to keys through sigma (swap of index bits 2 and 3),
+//    which makes a half-wave's 8 P values of a 16-key step 8 consecutive keys:
+//    P^T then feeds the PV MFMA (O^T = V^T P^T) as the B operand straight from
+//    the accumulators, and V^T staged in LDS gives the A operand in one
+//    16-byte read.
+//  * Software pipeline: while tile j's softmax runs on the VALU, the QK MFMAs
+//    of tile j+1 are issued, and the PV MFMAs of tile j's first 32 keys run
+//    while the exponentials of its last 32 keys are computed.  K tiles are
+//    staged two tiles ahead and V tiles one ahead (register-staged 16-byte
+//    loads, padded LDS rows), so one barrier per tile suffices.
+//  * Lazy rescale: O and l are rescaled only when a tile's maximum exceeds the
+//    running reference by more than 8 (base-2 units).  O, l and m always
+//    share that reference, so the result is the same softmax; P stays below
+//    2^8.  Row sums come from v_dot2_f32_bf16 over the bf16 P pairs.
 //  * Tiles are classified from the explicit positions: skipped (no visible
-//    pair), full (every pair visible) or masked (diagonal or ragged).  Only
-//    masked tiles compare positions.
-//  * Units (query tile, head) are launched heaviest first: positions increase
-//    within a rank, so later query tiles see at least as many keys.
+//    pair), full, or masked (diagonal or ragged).  Only masked tiles compare
+//    positions.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,6 +44,7 @@
 namespace ra {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -47,6 +53,7 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.0f;         // lazy-rescale margin, base-2 units
 constexpr int kPosHidden = 0x7fffffff;        // key slot past the block's end
 constexpr int kPosAlways = (int)0x80000000;   // key visible to every row (non-causal)
 constexpr int kPosRowNone = (int)0x80000000;  // query row past the end: sees no causal key
@@ -75,17 +82,19 @@ __device__ __forceinline__ int wave_sum_i(int x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
-// Element-type traits.  Each provides: the Q registers, staging a K/V tile
-// from HBM into registers and then into LDS, S^T = K Q^T for one tile and
-// O^T += V^T P^T for one tile.
+// Element-type traits.  Each provides the Q registers, staging of K / V tiles
+// from HBM through registers into LDS, S^T = K Q^T for one 32-key half of a
+// tile, the exponentials of one half (returning the PV operand and adding to
+// the row sum), and O^T += V^T P^T for one half.
 // ---------------------------------------------------------------------------
 
 // bfloat16 inputs, v_mfma_f32_32x32x16_bf16.
 template <int D>
 struct TraitsBf16 {
-  typedef uint16_t Elem;  // bfloat16 bits in HBM
-  typedef uint16_t LA;    // LDS element of the K stage
-  typedef uint16_t LB;    // LDS element of the V^T stage
+  typedef uint16_t Elem;   // bfloat16 bits in HBM
+  typedef uint16_t LK;     // LDS element of the K stage
+  typedef uint16_t LV;     // LDS element of the V^T stage
+  static constexpr int WAVES_PER_EU = 2;
   static constexpr int CPR = D / 8;                      // 16-byte chunks per row
   static constexpr int KCH = kKeysPerTile * CPR / 256;   // K chunks per thread per tile
   static constexpr int NV = KCH;                         // V keys per thread per tile
@@ -93,71 +102,56 @@ struct TraitsBf16 {
   static constexpr int DB = D / 32;                      // 32-wide d blocks of O^T
   static constexpr int KSTR = D + 8;                     // padded K row (elements)
   static constexpr int VSTR = kKeysPerTile + 8;          // padded V^T row (elements)
-  static constexpr int A_ELEMS = kKeysPerTile * KSTR;    // K stage
-  static constexpr int B_ELEMS = D * VSTR;               // V^T stage
+  static constexpr int K_ELEMS = kKeysPerTile * KSTR;
+  static constexpr int V_ELEMS = D * VSTR;
 
-  struct Regs {
-    u32x4 k[KCH];
-    u32x4 v[NV];
-  };
-  struct Q {
-    bf16x8 r[2][KS];
-  };
+  struct KRegs { u32x4 c[KCH]; };
+  struct VRegs { u32x4 c[NV]; };
+  struct Q { bf16x8 r[KS]; };
+  struct P { bf16x8 t[2]; };
 
   // Rows are padded by 16 bytes: 16 consecutive rows read at the same column
-  // then fall on 16 distinct groups of 4 banks, and every offset used inside
-  // the tile loops is a compile-time immediate.
+  // fall on 16 distinct groups of 4 banks, and every offset inside the tile
+  // loops is a compile-time immediate.
   static __device__ __forceinline__ int k_off(int key, int chunk) { return key * KSTR + chunk * 8; }
   static __device__ __forceinline__ int vt_off(int d, int key) { return d * VSTR + key; }
 
-  static __device__ __forceinline__ void load_q(Q& q, const void* qbase, int row0, int n_q,
-                                                int col, int h) {
-    const uint16_t* Qp = (const uint16_t*)qbase;
+  static __device__ __forceinline__ void load_q(Q& q, const Elem* qbase, int row, int n_q, int h) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      int r = row0 + qb * 32 + col;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (r < n_q) {
-          q.r[qb][ks] = *(const bf16x8*)(Qp + (size_t)r * D + ks * 16 + h * 8);
-        } else {
-          q.r[qb][ks] = bf16x8{};
-        }
-      }
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      q.r[ks] = row < n_q ? *(const bf16x8*)(qbase + (size_t)row * D + ks * 16 + h * 8) : bf16x8{};
   }
 
-  static __device__ __forceinline__ void load_tile(Regs& g, const void* kbase, const void* vbase,
-                                                   int j0, int n_k, int tid) {
-    const uint16_t* Kp = (const uint16_t*)kbase;
-    const uint16_t* Vp = (const uint16_t*)vbase;
+  static __device__ __forceinline__ void load_k(KRegs& g, const Elem* kb, int j0, int n_k, int tid) {
 #pragma unroll
     for (int p = 0; p < KCH; ++p) {
       int c = tid + 256 * p;
       int key = c / CPR, dc = c % CPR;
       int gk = j0 + key;
-      g.k[p] = gk < n_k ? *(const u32x4*)(Kp + (size_t)gk * D + dc * 8) : u32x4{0, 0, 0, 0};
-    }
-    constexpr int KG = kKeysPerTile / NV;  // key groups per tile
-    int kg = tid % KG, dc = tid / KG;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      int gk = j0 + kg * NV + i;
-      g.v[i] = gk < n_k ? *(const u32x4*)(Vp + (size_t)gk * D + dc * 8) : u32x4{0, 0, 0, 0};
+      g.c[p] = gk < n_k ? *(const u32x4*)(kb + (size_t)gk * D + dc * 8) : u32x4{0, 0, 0, 0};
     }
   }
-
-  static __device__ __forceinline__ void store_tile(const Regs& g, uint16_t* sk, uint16_t* svt,
-                                                    int tid) {
+  static __device__ __forceinline__ void store_k(const KRegs& g, LK* sk, int tid) {
 #pragma unroll
     for (int p = 0; p < KCH; ++p) {
       int c = tid + 256 * p;
       int key = c / CPR, dc = c % CPR;
-      *(u32x4*)(sk + k_off(key, dc)) = g.k[p];
+      *(u32x4*)(sk + k_off(key, dc)) = g.c[p];
     }
-    // Transpose the thread's NV keys x 8 d block into V^T rows d = 8*dc + e.
-    // Lanes of one store cover consecutive keys of one row (and the next 32
-    // lanes the row 8 further, 32 banks away), so the stores do not conflict.
+  }
+  // Each thread loads NV consecutive keys x 8 d values and writes them
+  // transposed into V^T rows 8*dc .. 8*dc+7.  Lanes of one store cover
+  // consecutive keys of one row, so the stores do not conflict.
+  static __device__ __forceinline__ void load_v(VRegs& g, const Elem* vb, int j0, int n_k, int tid) {
+    constexpr int KG = kKeysPerTile / NV;
+    int kg = tid % KG, dc = tid / KG;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      int gk = j0 + kg * NV + i;
+      g.c[i] = gk < n_k ? *(const u32x4*)(vb + (size_t)gk * D + dc * 8) : u32x4{0, 0, 0, 0};
+    }
+  }
+  static __device__ __forceinline__ void store_v(const VRegs& g, LV* svt, int tid) {
     constexpr int KG = kKeysPerTile / NV;
     int kg = tid % KG, dc = tid / KG;
     int key0 = kg * NV;
@@ -166,11 +160,11 @@ struct TraitsBf16 {
       int w = e >> 1;
       bool hi = e & 1;
       int d = dc * 8 + e;
-      uint32_t a0 = g.v[0][w], a1 = g.v[1][w];
+      uint32_t a0 = g.c[0][w], a1 = g.c[1][w];
       uint32_t lo = hi ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
-      uint16_t* dst = svt + vt_off(d, key0);
+      LV* dst = svt + vt_off(d, key0);
       if constexpr (NV == 4) {
-        uint32_t a2 = g.v[2][w], a3 = g.v[3][w];
+        uint32_t a2 = g.c[2][w], a3 = g.c[3][w];
         uint32_t up = hi ? ((a2 >> 16) | (a3 & 0xffff0000u)) : ((a2 & 0xffffu) | (a3 << 16));
         *(u32x2*)dst = u32x2{lo, up};
       } else {
@@ -179,46 +173,45 @@ struct TraitsBf16 {
     }
   }
 
-  // S^T[kb][qb] = K[32kb + sigma(.)] . Q[qb]^T for the 64-key tile in LDS.
-  static __device__ __forceinline__ void qk(f32x16 (&s)[2][2], const Q& q, const uint16_t* sk,
-                                            int col, int h) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = f32x16{};
+  // S^T rows 32kb..32kb+31 (keys 32kb + sigma(.)) against this wave's Q.
+  static __device__ __forceinline__ f32x16 qk(const Q& q, const LK* sk, int kb, int col, int h) {
+    f32x16 s = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        bf16x8 a = *(const bf16x8*)(sk + k_off(32 * kb + sigma(col), 2 * ks + h));
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q.r[qb][ks], s[kb][qb], 0, 0, 0);
-      }
+      bf16x8 a = *(const bf16x8*)(sk + k_off(32 * kb + sigma(col), 2 * ks + h));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q.r[ks], s, 0, 0, 0);
     }
+    return s;
   }
 
-  // O^T[db][qb] += V^T[db] P^T[qb]; P is the softmax numerator held in s.
-  static __device__ __forceinline__ void pv(f32x16 (&o)[DB][2], const f32x16 (&s)[2][2],
-                                            const uint16_t* svt, int col, int h) {
+  // P = 2^(s*c2 - m) as bf16 pairs; the row sum adds the same bf16 values.
+  static __device__ __forceinline__ P exp_pack(const f32x16& s, float c2, float m, float& lsum) {
+    P p;
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        bf16x8 pb[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pb[qb][e] = (__bf16)s[kb][qb][8 * t + e];
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          bf16x8 a = *(const bf16x8*)(svt + vt_off(db * 32 + col, 32 * kb + 16 * t + 8 * h));
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb], o[db][qb], 0, 0, 0);
-        }
+      for (int e = 0; e < 8; e += 2) {
+        float x0 = fast_exp2(__builtin_fmaf(s[8 * t + e], c2, -m));
+        float x1 = fast_exp2(__builtin_fmaf(s[8 * t + e + 1], c2, -m));
+        bf16x2 pr = {(__bf16)x0, (__bf16)x1};
+        p.t[t][e] = pr[0];
+        p.t[t][e + 1] = pr[1];
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, lsum, false);
       }
-    }
+    return p;
+  }
+
+  // O^T[db] += V^T[db rows, keys 32kb + ...] P^T.
+  static __device__ __forceinline__ void pv(f32x16 (&o)[DB], const P& p, const LV* svt, int kb,
+                                            int col, int h) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        bf16x8 a = *(const bf16x8*)(svt + vt_off(db * 32 + col, 32 * kb + 16 * t + 8 * h));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p.t[t], o[db], 0, 0, 0);
+      }
   }
 };
 
@@ -226,309 +219,277 @@ struct TraitsBf16 {
 template <int D>
 struct TraitsF32 {
   typedef float Elem;
-  typedef float LA;
-  typedef float LB;
+  typedef float LK;
+  typedef float LV;
+  static constexpr int WAVES_PER_EU = 1;
   static constexpr int CPR = D / 4;                     // 16-byte chunks per row
-  static constexpr int KCH = kKeysPerTile * CPR / 256;  // chunks per thread per tile (K and V)
+  static constexpr int KCH = kKeysPerTile * CPR / 256;  // chunks per thread per tile
   static constexpr int KS = D / 2;                      // QK k-steps
   static constexpr int DB = D / 32;
-  static constexpr int STRIDE = D + 1;                  // padded LDS row (floats)
-  static constexpr int A_ELEMS = kKeysPerTile * STRIDE;  // K stage
-  static constexpr int B_ELEMS = kKeysPerTile * STRIDE;  // V stage
+  static constexpr int STR = D + 1;                     // padded LDS row (floats)
+  static constexpr int K_ELEMS = kKeysPerTile * STR;
+  static constexpr int V_ELEMS = kKeysPerTile * STR;
 
-  struct Regs {
-    f32x4 k[KCH];
-    f32x4 v[KCH];
-  };
-  struct Q {
-    float r[2][KS];
-  };
+  struct KRegs { f32x4 c[KCH]; };
+  struct VRegs { f32x4 c[KCH]; };
+  struct Q { float r[KS]; };
+  struct P { f32x16 v; };
 
-  static __device__ __forceinline__ void load_q(Q& q, const void* qbase, int row0, int n_q,
-                                                int col, int h) {
-    const float* Qp = (const float*)qbase;
+  static __device__ __forceinline__ void load_q(Q& q, const Elem* qbase, int row, int n_q, int h) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      int r = row0 + qb * 32 + col;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) q.r[qb][ks] = r < n_q ? Qp[(size_t)r * D + 2 * ks + h] : 0.f;
-    }
+    for (int ks = 0; ks < KS; ++ks) q.r[ks] = row < n_q ? qbase[(size_t)row * D + 2 * ks + h] : 0.f;
   }
-
-  static __device__ __forceinline__ void load_tile(Regs& g, const void* kbase, const void* vbase,
-                                                   int j0, int n_k, int tid) {
-    const float* Kp = (const float*)kbase;
-    const float* Vp = (const float*)vbase;
+  static __device__ __forceinline__ void load_rows(f32x4 (&c)[KCH], const Elem* base, int j0,
+                                                   int n_k, int tid) {
 #pragma unroll
     for (int p = 0; p < KCH; ++p) {
-      int c = tid + 256 * p;
-      int key = c / CPR, dc = c % CPR;
+      int ci = tid + 256 * p;
+      int key = ci / CPR, dc = ci % CPR;
       int gk = j0 + key;
-      g.k[p] = gk < n_k ? *(const f32x4*)(Kp + (size_t)gk * D + dc * 4) : f32x4{0, 0, 0, 0};
-      g.v[p] = gk < n_k ? *(const f32x4*)(Vp + (size_t)gk * D + dc * 4) : f32x4{0, 0, 0, 0};
+      c[p] = gk < n_k ? *(const f32x4*)(base + (size_t)gk * D + dc * 4) : f32x4{0, 0, 0, 0};
     }
   }
-
-  static __device__ __forceinline__ void store_tile(const Regs& g, float* sk, float* sv, int tid) {
+  static __device__ __forceinline__ void store_rows(const f32x4 (&c)[KCH], float* sm, int tid) {
 #pragma unroll
     for (int p = 0; p < KCH; ++p) {
-      int c = tid + 256 * p;
-      int key = c / CPR, dc = c % CPR;
+      int ci = tid + 256 * p;
+      int key = ci / CPR, dc = ci % CPR;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sk[key * STRIDE + dc * 4 + e] = g.k[p][e];
-        sv[key * STRIDE + dc * 4 + e] = g.v[p][e];
-      }
+      for (int e = 0; e < 4; ++e) sm[key * STR + dc * 4 + e] = c[p][e];
     }
   }
+  static __device__ __forceinline__ void load_k(KRegs& g, const Elem* kb, int j0, int n_k, int tid) {
+    load_rows(g.c, kb, j0, n_k, tid);
+  }
+  static __device__ __forceinline__ void store_k(const KRegs& g, LK* sk, int tid) {
+    store_rows(g.c, sk, tid);
+  }
+  static __device__ __forceinline__ void load_v(VRegs& g, const Elem* vb, int j0, int n_k, int tid) {
+    load_rows(g.c, vb, j0, n_k, tid);
+  }
+  static __device__ __forceinline__ void store_v(const VRegs& g, LV* sv, int tid) {
+    store_rows(g.c, sv, tid);
+  }
 
-  static __device__ __forceinline__ void qk(f32x16 (&s)[2][2], const Q& q, const float* sk,
-                                            int col, int h) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = f32x16{};
+  static __device__ __forceinline__ f32x16 qk(const Q& q, const LK* sk, int kb, int col, int h) {
+    f32x16 s = {};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float a = sk[(32 * kb + sigma(col)) * STRIDE + 2 * ks + h];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, q.r[qb][ks], s[kb][qb], 0, 0, 0);
-      }
+      float a = sk[(32 * kb + sigma(col)) * STR + 2 * ks + h];
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(a, q.r[ks], s, 0, 0, 0);
     }
+    return s;
   }
 
-  // Accumulator register u of block kb holds key 32kb + 16(u/8) + 8h + u%8.
-  static __device__ __forceinline__ void pv(f32x16 (&o)[DB][2], const f32x16 (&s)[2][2],
-                                            const float* sv, int col, int h) {
+  static __device__ __forceinline__ P exp_pack(const f32x16& s, float c2, float m, float& lsum) {
+    P p;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int r = 0; r < 16; ++r) {
+      p.v[r] = fast_exp2(__builtin_fmaf(s[r], c2, -m));
+      lsum += p.v[r];
+    }
+    return p;
+  }
+
+  // Accumulator register u holds key 32kb + 16(u/8) + 8h + u%8.
+  static __device__ __forceinline__ void pv(f32x16 (&o)[DB], const P& p, const LV* sv, int kb,
+                                            int col, int h) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        int key = 32 * kb + 16 * (u >> 3) + 8 * h + (u & 7);
+    for (int u = 0; u < 16; ++u) {
+      int key = 32 * kb + 16 * (u >> 3) + 8 * h + (u & 7);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          float a = sv[key * STRIDE + db * 32 + col];
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[kb][qb][u], o[db][qb], 0, 0, 0);
-        }
+      for (int db = 0; db < DB; ++db) {
+        float a = sv[key * STR + db * 32 + col];
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, p.v[u], o[db], 0, 0, 0);
       }
     }
   }
 };
 
-// ---------------------------------------------------------------------------
-// The step kernel.
-// ---------------------------------------------------------------------------
-template <typename Tr, int D, bool READ, bool FINAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void step_kernel(const StepArgs a) {
-  typedef typename Tr::Elem E;
-  typedef typename Tr::LA LA;
-  typedef typename Tr::LB LB;
-  constexpr int AE = Tr::A_ELEMS;
-  constexpr int BE = Tr::B_ELEMS;
-  constexpr int DB = D / 32;
-  __shared__ __attribute__((aligned(16))) LA s_a[2][AE];
-  __shared__ __attribute__((aligned(16))) LB s_b[2][BE];
-  __shared__ __attribute__((aligned(16))) int32_t s_pos[2][kKeysPerTile];
+template <typename Tr>
+struct Smem {
+  typename Tr::LK k[2][Tr::K_ELEMS];
+  typename Tr::LV v[2][Tr::V_ELEMS];
+  int32_t pos[3][kKeysPerTile];
+};
 
-  const int tid = threadIdx.x;
+// Masks hidden keys of one 32-key half to -inf.  Accumulator register r of
+// half kb holds tile key 32kb + 8h + 16(r/8) + r%8.
+__device__ __forceinline__ void apply_mask(f32x16& s, const int32_t* pos, int kb, int h, int qp) {
+  i32x4 kp4[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+    kp4[x] = *(const i32x4*)&pos[32 * kb + 8 * h + 16 * (x >> 1) + 4 * (x & 1)];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = (kp4[r >> 2][r & 3] <= qp) ? s[r] : -INFINITY;
+}
+
+__device__ __forceinline__ int key_pos(const StepArgs& a, int gk, bool causal) {
+  return gk < a.n_k ? (causal ? a.k_pos[gk] : kPosAlways) : kPosHidden;
+}
+
+// One 128-row query tile of one head against the whole key/value block.
+template <typename Tr, int D, bool READ, bool FINAL>
+__device__ __forceinline__ void run_qtile(const StepArgs& a, Smem<Tr>& sm, int qt, int head,
+                                          int tid) {
+  typedef typename Tr::Elem E;
+  constexpr int DB = D / 32;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int h = lane >> 5;
   const int col = lane & 31;
-
-  const int u = blockIdx.x;
-  const int head = a.head_of[u % a.h_q];
-  const int qt = a.n_qt - 1 - u / a.h_q;
+  const int n_q = a.n_q, n_k = a.n_k;
+  const bool causal = a.causal != 0;
   const int kvh = head / (a.h_q / a.h_kv);
   const int row0_wg = qt * kRowsPerGroup;
   const int row0 = row0_wg + wave * kRowsPerWave;
-  const int n_q = a.n_q, n_k = a.n_k;
-  const bool causal = a.causal != 0;
 
-  // Key tiles this workgroup must visit: those whose first key is visible to
-  // the group's last row (a prefix, since positions increase).
+  // Key tiles this workgroup visits: those whose first key is visible to the
+  // group's last row (a prefix, since positions increase).
   const int n_kt = (n_k + kKeysPerTile - 1) / kKeysPerTile;
-  const int wg_last = min(row0_wg + kRowsPerGroup, n_q) - 1;
   int n_iter = n_kt;
   if (causal) {
-    const int qmax_wg = a.q_pos[wg_last];
+    const int qmax_wg = a.q_pos[min(row0_wg + kRowsPerGroup, n_q) - 1];
     int cnt = 0;
     for (int j = lane; j < n_kt; j += 64) cnt += (a.k_pos[j * kKeysPerTile] <= qmax_wg) ? 1 : 0;
     n_iter = wave_sum_i(cnt);
   }
-
   const bool wave_valid = row0 < n_q;
   const bool count = a.work != nullptr && head == 0 && wave_valid;
   if (READ && !FINAL && n_iter == 0) {
-    // No row of this group sees the block: the state stays as it is.
+    // No row of this tile sees the block: its state stays as it is.
     if (count && lane == 0) atomicAdd(a.work + 2, (unsigned long long)n_kt);
     return;
   }
 
-  // This wave's rows: extreme positions for tile classification and each
-  // lane's own query position per 32-row block.
-  const int wlast = min(row0 + kRowsPerWave, n_q) - 1;
+  // This wave's rows and this lane's query position.
   int qmin_w, qmax_w;
   if (!wave_valid) {
-    qmin_w = kPosRowNone;
-    qmax_w = kPosRowNone;
+    qmin_w = qmax_w = kPosRowNone;
   } else if (causal) {
     qmin_w = a.q_pos[row0];
-    qmax_w = a.q_pos[wlast];
+    qmax_w = a.q_pos[min(row0 + kRowsPerWave, n_q) - 1];
   } else {
-    qmin_w = kPosRowAll;
-    qmax_w = kPosRowAll;
+    qmin_w = qmax_w = kPosRowAll;
   }
-  int qp[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    int r = row0 + qb * 32 + col;
-    qp[qb] = r < n_q ? (causal ? a.q_pos[r] : kPosRowAll) : kPosRowNone;
-  }
+  const int row = row0 + col;
+  const int qp = row < n_q ? (causal ? a.q_pos[row] : kPosRowAll) : kPosRowNone;
 
-  const size_t qoff = ((size_t)head * n_q) * D;
-  const size_t kvoff = ((size_t)kvh * n_k) * D;
+  const E* kbase = (const E*)a.k + ((size_t)kvh * n_k) * D;
+  const E* vbase = (const E*)a.v + ((size_t)kvh * n_k) * D;
   typename Tr::Q q;
-  Tr::load_q(q, (const E*)a.q + qoff, row0, n_q, col, h);
-  const E* kbase = (const E*)a.k + kvoff;
-  const E* vbase = (const E*)a.v + kvoff;
+  Tr::load_q(q, (const E*)a.q + ((size_t)head * n_q) * D, row, n_q, h);
 
-  // Running state in base-2 units: m2 = max(scale*log2e * s); lsum = this
-  // half-wave's share of the exp-sum; o = O^T accumulators.
-  // m_nat0 / m2_0 remember the state's max as read, so a row whose max does
-  // not move writes back the identical bits (no ln2 round trip).
-  f32x16 o[DB][2];
-  float m2[2], lsum[2], m_nat0[2], m2_0[2];
+  // Running state in base-2 units: m2 is the reference the sums are taken
+  // against (within kRescaleSlack of the running maximum), lsum this
+  // half-wave's share of the exp-sum, o the O^T accumulators.
+  f32x16 o[DB];
+  float m2 = -INFINITY, lsum = 0.f, m_nat0 = -INFINITY;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    m2[qb] = -INFINITY;
-    m_nat0[qb] = -INFINITY;
-    lsum[qb] = 0.f;
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  const size_t srow = (size_t)head * n_q + row;
+  if (READ && row < n_q) {
+    m_nat0 = a.m_in[srow];
+    m2 = m_nat0 * kLog2e;  // -inf stays -inf
+    lsum = h == 0 ? a.l_in[srow] : 0.f;
+    const float* orow = a.o_in + srow * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) o[db][qb] = f32x16{};
-  }
-  if (READ) {
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      int r = row0 + qb * 32 + col;
-      if (r < n_q) {
-        size_t sr = (size_t)head * n_q + r;
-        float mn = a.m_in[sr];
-        m_nat0[qb] = mn;
-        m2[qb] = mn * kLog2e;  // -inf stays -inf
-        lsum[qb] = h == 0 ? a.l_in[sr] : 0.f;
-        const float* orow = a.o_in + sr * D;
+      for (int g = 0; g < 4; ++g) {
+        f32x4 x = *(const f32x4*)(orow + db * 32 + 8 * g + 4 * h);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f32x4 x = *(const f32x4*)(orow + db * 32 + 8 * g + 4 * h);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[db][qb][4 * g + e] = x[e];
-          }
+        for (int e = 0; e < 4; ++e) o[db][4 * g + e] = x[e];
       }
-    }
   }
-
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) m2_0[qb] = m2[qb];
-
-  int cnt_full = 0, cnt_masked = 0;
+  const float m2_0 = m2;
   const float c2 = a.c2;
+  int cnt_full = 0, cnt_masked = 0;
 
-  typename Tr::Regs g;
+  typename Tr::KRegs gk;
+  typename Tr::VRegs gv;
+  f32x16 s_cur[2];
   if (n_iter > 0) {
-    Tr::load_tile(g, kbase, vbase, 0, n_k, tid);
-    if (tid < kKeysPerTile) {
-      int gk = tid;
-      s_pos[0][tid] = gk < n_k ? (causal ? a.k_pos[gk] : kPosAlways) : kPosHidden;
+    // Prologue: K0, K1, V0 and positions 0, 1 into LDS, then S^T of tile 0.
+    Tr::load_k(gk, kbase, 0, n_k, tid);
+    Tr::load_v(gv, vbase, 0, n_k, tid);
+    if (tid < kKeysPerTile) sm.pos[0][tid] = key_pos(a, tid, causal);
+    Tr::store_k(gk, sm.k[0], tid);
+    Tr::store_v(gv, sm.v[0], tid);
+    if (n_iter > 1) {
+      Tr::load_k(gk, kbase, kKeysPerTile, n_k, tid);
+      if (tid < kKeysPerTile) sm.pos[1][tid] = key_pos(a, kKeysPerTile + tid, causal);
+      Tr::store_k(gk, sm.k[1], tid);
     }
-    Tr::store_tile(g, s_a[0], s_b[0], tid);
+    __syncthreads();
+    s_cur[0] = Tr::qk(q, sm.k[0], 0, col, h);
+    s_cur[1] = Tr::qk(q, sm.k[0], 1, col, h);
+    // K stage 0 is refilled during the first iteration: every wave must be
+    // done reading it.
+    if (n_iter > 2) __syncthreads();
   }
-  __syncthreads();
 
   for (int j = 0; j < n_iter; ++j) {
-    const int st = j & 1;
-    const bool more = j + 1 < n_iter;
+    const bool has1 = j + 1 < n_iter, has2 = j + 2 < n_iter;
+    const int sk_next = (j + 1) & 1, sv_cur = j & 1;
     int next_pos = kPosHidden;
-    if (more) {
-      const int j1 = (j + 1) * kKeysPerTile;
-      Tr::load_tile(g, kbase, vbase, j1, n_k, tid);
-      if (tid < kKeysPerTile) {
-        int gk = j1 + tid;
-        next_pos = gk < n_k ? (causal ? a.k_pos[gk] : kPosAlways) : kPosHidden;
-      }
+    if (has2) {
+      Tr::load_k(gk, kbase, (j + 2) * kKeysPerTile, n_k, tid);
+      if (tid < kKeysPerTile) next_pos = key_pos(a, (j + 2) * kKeysPerTile + tid, causal);
     }
+    if (has1) Tr::load_v(gv, vbase, (j + 1) * kKeysPerTile, n_k, tid);
 
-    // Classify this tile for this wave's rows (valid keys only).
+    // Classify tile j for this wave's rows (valid keys only).
+    const int32_t* pos = sm.pos[j % 3];
     const int j0 = j * kKeysPerTile;
     const int last_valid = min(j0 + kKeysPerTile, n_k) - 1 - j0;
-    const int kmin = s_pos[st][0];
-    const int kmax = s_pos[st][last_valid];
+    const int kmin = pos[0], kmax = pos[last_valid];
     const bool ragged = j0 + kKeysPerTile > n_k;
     const bool skip = !wave_valid || kmin > qmax_w;
     const bool full = kmax <= qmin_w;
 
+    f32x16 s_next[2];
     if (!skip) {
       if (full) ++cnt_full; else ++cnt_masked;
-      f32x16 s[2][2];
-      Tr::qk(s, q, s_a[st], col, h);
       if (!full || ragged) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          i32x4 kp4[4];
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            kp4[x] = *(const i32x4*)&s_pos[st][32 * kb + 8 * h + 16 * (x >> 1) + 4 * (x & 1)];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            int kp = kp4[r >> 2][r & 3];
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-              s[kb][qb][r] = (kp <= qp[qb]) ? s[kb][qb][r] : -INFINITY;
-          }
-        }
+        apply_mask(s_cur[0], pos, 0, h, qp);
+        apply_mask(s_cur[1], pos, 1, h, qp);
       }
-      // Online softmax: new max, rescale old totals, exponentiate.
+      if (has1) s_next[0] = Tr::qk(q, sm.k[sk_next], 0, col, h);
+      float mx = -INFINITY;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float mx = -INFINITY;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s_cur[0][r], s_cur[1][r]));
+      const float mloc = half_swap_max(mx) * c2;
+      if (__ballot(mloc > m2 + kRescaleSlack) != 0) {
+        const float mnew = fmaxf(m2, mloc);
+        const float alpha = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mnew);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-        mx = half_swap_max(mx);
-        const float mnew = fmaxf(m2[qb], mx * c2);
-        const float alpha = (m2[qb] == -INFINITY) ? 0.f : fast_exp2(m2[qb] - mnew);
-        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-        float ps = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float p = fast_exp2(__builtin_fmaf(s[kb][qb][r], c2, -muse));
-            s[kb][qb][r] = p;
-            ps += p;
-          }
-        lsum[qb] = lsum[qb] * alpha + ps;
-        m2[qb] = mnew;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[db][qb] *= alpha;
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        lsum *= alpha;
+        m2 = mnew;
       }
-      Tr::pv(o, s, s_b[st], col, h);
+      // A row with nothing visible yet keeps m2 = -inf and gets P = 0.
+      const float muse = (m2 == -INFINITY) ? 0.f : m2;
+      if (has1) s_next[1] = Tr::qk(q, sm.k[sk_next], 1, col, h);
+      typename Tr::P p0 = Tr::exp_pack(s_cur[0], c2, muse, lsum);
+      Tr::pv(o, p0, sm.v[sv_cur], 0, col, h);
+      typename Tr::P p1 = Tr::exp_pack(s_cur[1], c2, muse, lsum);
+      Tr::pv(o, p1, sm.v[sv_cur], 1, col, h);
+    } else if (has1) {
+      s_next[0] = Tr::qk(q, sm.k[sk_next], 0, col, h);
+      s_next[1] = Tr::qk(q, sm.k[sk_next], 1, col, h);
     }
 
-    if (more) {
-      Tr::store_tile(g, s_a[st ^ 1], s_b[st ^ 1], tid);
-      if (tid < kKeysPerTile) s_pos[st ^ 1][tid] = next_pos;
+    if (has2) {
+      Tr::store_k(gk, sm.k[j & 1], tid);
+      if (tid < kKeysPerTile) sm.pos[(j + 2) % 3][tid] = next_pos;
     }
+    if (has1) Tr::store_v(gv, sm.v[(j + 1) & 1], tid);
     __syncthreads();
+    if (has1) {
+      s_cur[0] = s_next[0];
+      s_cur[1] = s_next[1];
+    }
   }
 
   if (count && lane == 0) {
@@ -538,43 +499,57 @@ void step_kernel(const StepArgs a) {
   }
 
   // Epilogue: combine the half-wave sums and write the state or the result.
+  const float ltot = half_swap_sum(lsum);
+  if (row >= n_q) return;
+  // A row whose reference did not move writes back its exact bits.
+  const float m_nat = (m2 == m2_0) ? m_nat0 : m2 * kLn2;
+  if (FINAL) {
+    const bool ok = ltot > 0.f;
+    const float inv = ok ? 1.f / ltot : 0.f;
+    float* orow = a.out + srow * D;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float ltot = half_swap_sum(lsum[qb]);
-    const float m_nat = (m2[qb] == m2_0[qb]) ? m_nat0[qb] : m2[qb] * kLn2;
-    const int r = row0 + qb * 32 + col;
-    if (r >= n_q) continue;
-    const size_t sr = (size_t)head * n_q + r;
-    if (FINAL) {
-      const bool ok = ltot > 0.f;
-      const float inv = ok ? 1.f / ltot : 0.f;
-      float* orow = a.out + sr * D;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int g = 0; g < 4; ++g) {
+        f32x4 x;
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          f32x4 x;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = o[db][qb][4 * gq + e] * inv;
-          *(f32x4*)(orow + db * 32 + 8 * gq + 4 * h) = x;
-        }
-      if (h == 0) a.lse[sr] = ok ? m_nat + logf(ltot) : -INFINITY;
-    } else {
-      float* orow = a.o_out + sr * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          f32x4 x;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = o[db][qb][4 * gq + e];
-          *(f32x4*)(orow + db * 32 + 8 * gq + 4 * h) = x;
-        }
-      if (h == 0) {
-        a.m_out[sr] = m_nat;
-        a.l_out[sr] = ltot;
+        for (int e = 0; e < 4; ++e) x[e] = o[db][4 * g + e] * inv;
+        *(f32x4*)(orow + db * 32 + 8 * g + 4 * h) = x;
       }
+    if (h == 0) a.lse[srow] = ok ? m_nat + logf(ltot) : -INFINITY;
+  } else {
+    float* orow = a.o_out + srow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = o[db][4 * g + e];
+        *(f32x4*)(orow + db * 32 + 8 * g + 4 * h) = x;
+      }
+    if (h == 0) {
+      a.m_out[srow] = m_nat;
+      a.l_out[srow] = ltot;
     }
+  }
+}
+
+// One workgroup: a query head and a pair of query tiles (heavier one first).
+template <typename Tr, int D, bool READ, bool FINAL>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(Tr::WAVES_PER_EU, Tr::WAVES_PER_EU)))
+void step_kernel(const StepArgs a) {
+  __shared__ __attribute__((aligned(16))) Smem<Tr> sm;
+  const int tid = threadIdx.x;
+  const int u = blockIdx.x;
+  const int head = a.head_of[u % a.h_q];
+  const int p = u / a.h_q;
+  const int t_hi = a.n_qt - 1 - p, t_lo = p;
+  run_qtile<Tr, D, READ, FINAL>(a, sm, t_hi, head, tid);
+  if (t_lo < t_hi) {
+    __syncthreads();  // LDS of the first tile is fully consumed
+    run_qtile<Tr, D, READ, FINAL>(a, sm, t_lo, head, tid);
   }
 }
 
@@ -613,7 +588,7 @@ __global__ void zero_i64_kernel(int64_t* p, int n) {
 
 template <typename Tr, int D>
 static hipError_t launch_typed(const StepArgs& a, bool read, bool final_, hipStream_t stream) {
-  dim3 grid((unsigned)(a.n_qt * a.h_q)), block(256);
+  dim3 grid((unsigned)(a.n_pairs * a.h_q)), block(256);
   if (read && final_)
     hipLaunchKernelGGL((step_kernel<Tr, D, true, true>), grid, block, 0, stream, a);
   else if (read)

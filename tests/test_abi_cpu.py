@@ -72,7 +72,7 @@ def test_null_problem():
 
 def test_tile_shape_and_workspace():
     p = good()
-    assert ra.tile_shape(p) == (64, 64)
+    assert ra.tile_shape(p) == (32, 64)
     n = ra.workspace_bytes(p)
     # state (m, l, o in fp32) + 2 slots of K, V (bf16) and positions
     state = 4 * 256 * 4 * 2 + 4 * 256 * 128 * 4
