@@ -30,13 +30,10 @@
  *    k_pos[j] <= q_pos[i] when causal, always otherwise.  Positions that do
  *    not increase give unspecified values but never an out-of-bounds access.
  *  - Query head h reads key/value head h / (h_q / h_kv).
- *  - State (m, l, O): l = sum exp(s - m) and O = sum exp(s - m) v over the
- *    visible keys seen so far, with s = scale * q.k, in natural-log units.  m
- *    is the reference both sums are taken against: the running maximum, or
- *    up to 8 ln 2 below it (the kernels move the reference only when a
- *    larger score would push exp(s - m) past 2^8, which saves rescaling O on
- *    most tiles; any reference gives the same softmax).  A row that has seen
- *    no visible key has m = -inf, l = 0, O = 0.
+ *  - State (m, l, O): m is the running maximum of the scores s = scale * q.k
+ *    (natural-log units) over the visible keys seen so far, l = sum exp(s - m)
+ *    and O = sum exp(s - m) v over the same keys.  A row that has seen no
+ *    visible key has m = -inf, l = 0, O = 0.
  *  - Calls are asynchronous on the given HIP stream (passed as void*, a
  *    hipStream_t; NULL is the default stream).  Arguments are checked on the
  *    host first: on an error nothing is enqueued and no output is touched.

@@ -29,10 +29,12 @@
 //    while the exponentials of its last 32 keys are computed.  K tiles are
 //    staged two tiles ahead and V tiles one ahead (register-staged 16-byte
 //    loads, padded LDS rows), so one barrier per tile suffices.
-//  * Lazy rescale: O and l are rescaled only when a tile's maximum exceeds the
-//    running reference by more than 8 (base-2 units).  O, l and m always
-//    share that reference, so the result is the same softmax; P stays below
-//    2^8.  Row sums come from v_dot2_f32_bf16 over the bf16 P pairs.
+//  * Rescale on demand: O and l are multiplied by exp(m_old - m_new) only on
+//    tiles where some row of the wave raised its maximum (a wave-wide ballot);
+//    once a row has seen a few hundred keys that is rare.  m stays the exact
+//    running maximum, so the largest P of a row is exactly 1 and its bf16
+//    rounding costs nothing (a slack that let P exceed 1 cost ~3x in output
+//    error on peaky rows).
 //  * Tiles are classified from the explicit positions: skipped (no visible
 //    pair), full, or masked (diagonal or ragged).  Only masked tiles compare
 //    positions.
@@ -44,7 +46,6 @@
 namespace ra {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -53,7 +54,6 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleSlack = 8.0f;         // lazy-rescale margin, base-2 units
 constexpr int kPosHidden = 0x7fffffff;        // key slot past the block's end
 constexpr int kPosAlways = (int)0x80000000;   // key visible to every row (non-causal)
 constexpr int kPosRowNone = (int)0x80000000;  // query row past the end: sees no causal key
@@ -184,21 +184,24 @@ struct TraitsBf16 {
     return s;
   }
 
-  // P = 2^(s*c2 - m) as bf16 pairs; the row sum adds the same bf16 values.
+  // P = 2^(s*c2 - m) rounded to bf16 for the PV product; the row sum adds
+  // the fp32 values (summing the rounded values costs ~1e-3 in lse when one
+  // key dominates a row).
   static __device__ __forceinline__ P exp_pack(const f32x16& s, float c2, float m, float& lsum) {
     P p;
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         float x0 = fast_exp2(__builtin_fmaf(s[8 * t + e], c2, -m));
         float x1 = fast_exp2(__builtin_fmaf(s[8 * t + e + 1], c2, -m));
-        bf16x2 pr = {(__bf16)x0, (__bf16)x1};
-        p.t[t][e] = pr[0];
-        p.t[t][e + 1] = pr[1];
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, lsum, false);
+        p.t[t][e] = (__bf16)x0;
+        p.t[t][e + 1] = (__bf16)x1;
+        acc0 += x0;
+        acc1 += x1;
       }
+    lsum += acc0 + acc1;
     return p;
   }
 
@@ -380,9 +383,9 @@ __device__ __forceinline__ void run_qtile(const StepArgs& a, Smem<Tr>& sm, int q
   typename Tr::Q q;
   Tr::load_q(q, (const E*)a.q + ((size_t)head * n_q) * D, row, n_q, h);
 
-  // Running state in base-2 units: m2 is the reference the sums are taken
-  // against (within kRescaleSlack of the running maximum), lsum this
-  // half-wave's share of the exp-sum, o the O^T accumulators.
+  // Running state in base-2 units: m2 is the running maximum the sums are
+  // taken against, lsum this half-wave's share of the exp-sum, o the O^T
+  // accumulators.
   f32x16 o[DB];
   float m2 = -INFINITY, lsum = 0.f, m_nat0 = -INFINITY;
 #pragma unroll
@@ -460,7 +463,7 @@ __device__ __forceinline__ void run_qtile(const StepArgs& a, Smem<Tr>& sm, int q
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s_cur[0][r], s_cur[1][r]));
       const float mloc = half_swap_max(mx) * c2;
-      if (__ballot(mloc > m2 + kRescaleSlack) != 0) {
+      if (__ballot(mloc > m2) != 0) {
         const float mnew = fmaxf(m2, mloc);
         const float alpha = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mnew);
 #pragma unroll

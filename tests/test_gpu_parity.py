@@ -134,15 +134,12 @@ def test_step_by_step_matches_oracle_and_forward():
         out, lse = ra.finalize(p, m, l, o)
         ro, rl = oracle.finalize(*st)
         compare(out.cpu(), lse.cpu(), ro, rl, TOL["bf16"], f"step {b}")
-        # the state itself: m is a reference at most 8 ln 2 below the running
-        # maximum, and l, o are taken against it
+        # the state itself: m is the running maximum, l the exp-sum against it
         mc, lc = m.cpu().numpy(), l.cpu().numpy()
         fin = np.isfinite(st[0])
         assert np.array_equal(np.isfinite(mc), fin)
-        assert np.all(mc[fin] <= st[0][fin] + 1e-3)
-        assert np.all(mc[fin] >= st[0][fin] - 8 * np.log(2) - 1e-3)
-        l_rescaled = lc[fin] * np.exp(mc[fin] - st[0][fin])
-        assert np.abs(l_rescaled / st[1][fin] - 1).max() <= 1e-2
+        assert max_err(mc[fin], st[0][fin]) <= 1e-3
+        assert np.abs(lc[fin] / st[1][fin] - 1).max() <= 1e-3
     fo, fl, fw, _ = run_forward(sh)
     assert np.array_equal(out.cpu().numpy(), fo) and np.array_equal(lse.cpu().numpy(), fl)
     assert np.array_equal(work.cpu().numpy(), fw)
