@@ -12,7 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libra.so")
-SOURCES = [os.path.join(CSRC, "ra_kernels.hip"), os.path.join(CSRC, "ra_host.cpp")]
+SOURCES = [os.path.join(CSRC, "ra_kernels.hip"), os.path.join(CSRC, "ra_fast.hip"),
+           os.path.join(CSRC, "ra_host.cpp")]
 ARCH = "gfx950"
 
 
@@ -28,6 +29,9 @@ def command(out=LIB):
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed fp32 VALU forms are kept out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # the kernels never create NaN (empty rows are guarded), so max needs
+        # no quieting; infinities stay honoured (masked scores are -inf)
+        "-fno-honor-nans",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
         *SOURCES, "-o", out,
     ]

@@ -1,0 +1,522 @@
+// Fast ring-step kernel for bfloat16 inputs with d_k = 128 on gfx950.
+//
+// Computes exactly what the generic step kernel computes (one key/value block
+// folded into the online-softmax state, Zero to Frontier
+// "distributed/context-expert", section "Splitting the sequence, and the one
+// layer that objects"), organised for CDNA4 throughput:
+//
+//  * Two waves per SIMD.  A single wave issues VALU work at about half rate
+//    on gfx950, so the softmax only keeps up with the MFMA pipe when two
+//    waves share each SIMD.  A workgroup is 8 waves: two groups of 4 waves
+//    on the same 128 query rows (32 per wave).  Group g takes the key tiles
+//    j = g, g+2, g+4, ... of the block; the two partial states are folded
+//    together through LDS at the end (the same online-softmax fold).
+//  * No staging registers.  K and V tiles go from HBM straight into LDS with
+//    global_load_lds_dwordx4, in row-major 256-byte rows whose 16-byte chunks
+//    are XOR-swizzled by row, so both read patterns below are free of bank
+//    conflicts.  That leaves each wave under 256 registers.
+//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K rows are the A operand
+//    (one ds_read_b128 each), Q stays in registers as the B operand.  Every
+//    lane then holds one query column, so row max and row sum are in-lane
+//    plus one v_permlane32_swap.  Accumulator row i holds key sigma(i) (index
+//    bits 2 and 3 swapped), so P^T feeds O^T = V^T P^T straight from the
+//    accumulators, 8 consecutive keys per half-wave.
+//  * The V^T operand comes from row-major V with ds_read_b64_tr_b16: within
+//    each 16-lane group, lane j receives element j of the 4 rows the group
+//    addressed, i.e. 4 consecutive keys of one d column.
+//  * Pipeline per wave, on its own tile j: the MFMA pipe runs PV of its
+//    previous tile and QK of its next tile while the VALU does the softmax
+//    of tile j; O is rescaled (only when some row's max moved) at the top of
+//    the next iteration.  K tiles are fetched two own-tiles ahead, V tiles one
+//    ahead; one barrier per tile pair.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ra_internal.h"
+
+namespace ra {
+namespace fast {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int D = 128;
+constexpr int BN = 64;                      // keys per tile
+constexpr int ROWS = 128;                   // query rows per workgroup tile
+constexpr int WAVE_ROWS = 32;
+constexpr int THREADS = 512;                // 8 waves: 2 groups of 4
+constexpr int TILE_BYTES = BN * D * 2;      // 16 KiB
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kPosHidden = 0x7fffffff;
+constexpr int kPosAlways = (int)0x80000000;
+constexpr int kPosRowNone = (int)0x80000000;
+constexpr int kPosRowAll = 0x7ffffffe;
+
+static_assert(ROWS == 4 * WAVE_ROWS, "4 waves per group");
+static_assert(kRowsPerGroup == ROWS, "host launch geometry");
+
+struct __attribute__((aligned(1024))) Smem {
+  uint8_t k[2][2][TILE_BYTES];   // [group][stage]
+  uint8_t v[2][2][TILE_BYTES];
+  int32_t pos[2][3][BN];         // [group][stage]
+};
+// The merge of the two groups reuses the K/V area.
+static_assert(4 * 64 * 64 * 4 + 4 * 64 * 2 * 4 <= (int)sizeof(uint8_t[2][2][TILE_BYTES]) * 2,
+              "merge buffer fits");
+
+__device__ __forceinline__ int sigma(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+__device__ __forceinline__ float half_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Byte offset of 16-byte chunk c of row r inside a K tile / a V tile.
+__device__ __forceinline__ int k_chunk_off(int r, int c) { return r * 256 + 16 * (c ^ (r & 15)); }
+__device__ __forceinline__ int v_chunk_off(int r, int c) { return r * 256 + 16 * (c ^ (2 * (r & 3))); }
+
+template <bool READ, bool FINAL>
+struct Step {
+  const StepArgs& a;
+  Smem& sm;
+  const int tid, lane, gwave, grp, h, col;
+  const int n_q, n_k;
+  const bool causal;
+  const uint16_t* kbase;
+  const uint16_t* vbase;
+  int n_iter = 0, n_own = 0;
+  bool wave_valid = false;
+  int qmin_w = 0, qmax_w = 0, qp = 0;
+  float c2 = 0.f;
+
+  // per-lane LDS/global offsets (loop invariant)
+  int k_ld_off[4];   // byte offset inside a K tile for this lane's 4 load instructions
+  int v_ld_off;      // ditto for V (the 4 instructions differ by 1 KiB)
+  int k_rd;          // K read base, XOR'ed with 32*ks
+  int v_rd;          // V read base, XOR'ed with 64*db
+
+  bf16x8 q[8];
+  f32x16 o[4];
+  float m2 = -INFINITY, lsum = 0.f;
+  int cnt_full = 0, cnt_masked = 0;
+  f32x16 s_cur[2], s_next[2];
+  bf16x8 p_prev[2][2];
+  bool need_rescale = false;
+  float alpha_pending = 1.f;
+
+  __device__ Step(const StepArgs& a_, Smem& sm_, int tid_)
+      : a(a_), sm(sm_), tid(tid_), lane(tid_ & 63),
+        gwave(__builtin_amdgcn_readfirstlane((tid_ >> 6) & 3)),
+        grp(__builtin_amdgcn_readfirstlane(tid_ >> 8)), h((tid_ & 63) >> 5), col(tid_ & 31),
+        n_q(a_.n_q), n_k(a_.n_k), causal(a_.causal != 0), kbase(nullptr), vbase(nullptr) {
+    // K loads: instruction i of this wave fills rows 4b..4b+3, b = 4*gwave + i;
+    // lane L writes LDS chunk L%16 of row 4b + L/16, which holds logical chunk
+    // (L%16) ^ (row & 15).
+    const int L = lane;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * (4 * gwave + i) + L / 16;
+      const int c = (L % 16) ^ (r & 15);
+      k_ld_off[i] = r * 256 + c * 16;  // global byte offset of that chunk in the tile
+    }
+    {
+      const int r = 4 * (4 * gwave) + L / 16;
+      const int c = (L % 16) ^ (2 * (r & 3));
+      v_ld_off = r * 256 + c * 16;
+    }
+    // K reads: row sigma(col) (+32 kb), logical chunk 2ks + h.
+    {
+      const int r = sigma(col);
+      const int x = r & 15;
+      k_rd = r * 256 + 16 * (h ^ (x & 1)) + 32 * (x >> 1);  // ^ (32 ks) gives chunk 2ks+h
+    }
+    // V reads (transposing): 16-lane group g4, lane i in the group.
+    {
+      const int g4 = lane >> 4, i = lane & 15;
+      const int hh = g4 >> 1, dgrp = g4 & 1, rho = i >> 2, b = (i & 3) >> 1, half = i & 1;
+      const int T = (32 * dgrp + 16 * b) ^ (32 * rho);
+      v_rd = (8 * hh + rho) * 256 + 8 * half + T;  // ^ (64 db) selects the d block
+    }
+  }
+
+  // ---- tile staging (direct to LDS) --------------------------------------
+  __device__ __forceinline__ void load_k_tile(int j, int stage) {
+    const int j0 = j * BN;
+    const char* src = (const char*)kbase;
+    uint8_t* dst = sm.k[grp][stage];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * gwave + i;
+      // clamp rows past the block to its last row (masked off by position)
+      const int r = (k_ld_off[i] >> 8);
+      const int gr = min(j0 + r, n_k - 1);
+      const char* g = src + (size_t)gr * 256 + (k_ld_off[i] & 255);
+      __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(dst + b * 1024), 16, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void load_v_tile(int j, int stage) {
+    const int j0 = j * BN;
+    const char* src = (const char*)vbase;
+    uint8_t* dst = sm.v[grp][stage];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * gwave + i;
+      const int r = (v_ld_off >> 8) + 4 * i;
+      const int gr = min(j0 + r, n_k - 1);
+      const char* g = src + (size_t)gr * 256 + (v_ld_off & 255);
+      __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(dst + b * 1024), 16, 0, 0);
+    }
+  }
+  __device__ __forceinline__ int fetch_pos(int j) const {
+    const int gk = j * BN + (tid & 63);
+    const int p = a.k_pos[min(gk, n_k - 1)];
+    return gk < n_k ? (causal ? p : kPosAlways) : kPosHidden;
+  }
+
+  // ---- MFMA pieces --------------------------------------------------------
+  __device__ __forceinline__ f32x16 qk(int stage, int kb) const {
+    const uint8_t* base = sm.k[grp][stage] + kb * 32 * 256;
+    f32x16 s = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      bf16x8 av = *(const bf16x8*)(base + (k_rd ^ (32 * ks)));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, q[ks], s, 0, 0, 0);
+    }
+    return s;
+  }
+  __device__ __forceinline__ void pv(int stage, int kb, const bf16x8 (&p)[2]) {
+    const uint8_t* base = sm.v[grp][stage] + kb * 32 * 256;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int off = (v_rd ^ (64 * db)) + t * 16 * 256;
+        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
+        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off + 4 * 256));
+        // whole-vector assembly: element-wise __bf16 inserts were mis-lowered
+        const s16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, w);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, p[t], o[db], 0, 0, 0);
+      }
+  }
+
+  // Masks hidden keys of one 32-key half to -inf.  Accumulator register r of
+  // half kb holds tile key 32kb + 8h + 16(r/8) + r%8.
+  __device__ __forceinline__ void mask(f32x16& s, const int32_t* pos, int kb, int qpe) const {
+    i32x4 kp4[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      kp4[x] = *(const i32x4*)&pos[32 * kb + 8 * h + 16 * (x >> 1) + 4 * (x & 1)];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = (kp4[r >> 2][r & 3] <= qpe) ? s[r] : -INFINITY;
+  }
+
+  __device__ __forceinline__ void exp_pack(const f32x16& s, float muse, bf16x8 (&p)[2]) {
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float x0 = fast_exp2(__builtin_fmaf(s[8 * t + e], c2, -muse));
+        float x1 = fast_exp2(__builtin_fmaf(s[8 * t + e + 1], c2, -muse));
+        p[t][e] = (__bf16)x0;
+        p[t][e + 1] = (__bf16)x1;
+        acc0 += x0;
+        acc1 += x1;
+      }
+    lsum += acc0 + acc1;
+  }
+
+  __device__ __forceinline__ void apply_pending_rescale() {
+    if (need_rescale) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha_pending;
+    }
+  }
+
+  // One own tile i (global tile j = 2i + grp).  HAS_PREV: PV of own tile i-1
+  // is pending; HAS_NEXT: own tile i+1 exists.
+  template <bool HAS_PREV, bool HAS_NEXT>
+  __device__ __forceinline__ void iteration(int i) {
+    apply_pending_rescale();
+    const int j = 2 * i + grp;
+    // Stage K of own tile i+2 (clamped to the last own tile: a repeat lands
+    // in a stage nobody reads) and V of own tile i.
+    const int i2 = min(i + 2, n_own - 1);
+    load_k_tile(2 * i2 + grp, i & 1);
+    load_v_tile(j, i & 1);
+    const int next_pos = fetch_pos(2 * i2 + grp);
+
+    const int32_t* pos = sm.pos[grp][i % 3];
+    const int j0 = j * BN;
+    const int last_valid = min(j0 + BN, n_k) - 1 - j0;
+    const int kmin = pos[0], kmax = pos[last_valid];
+    const bool ragged = j0 + BN > n_k;
+    const bool skip = !wave_valid || kmin > qmax_w;
+    const bool full = kmax <= qmin_w;
+    if (!skip) {
+      if (full) ++cnt_full; else ++cnt_masked;
+    }
+    if (skip || !full || ragged) {
+      const int qpe = skip ? kPosRowNone : qp;
+      mask(s_cur[0], pos, 0, qpe);
+      mask(s_cur[1], pos, 1, qpe);
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s_cur[0][r], s_cur[1][r]));
+    const float mloc = half_swap_max(mx) * c2;
+    need_rescale = __ballot(mloc > m2) != 0;
+    const float mnew = fmaxf(m2, mloc);
+    alpha_pending = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mnew);
+    m2 = mnew;
+    const float muse = (m2 == -INFINITY) ? 0.f : m2;
+
+    if (HAS_PREV) {
+      pv((i - 1) & 1, 0, p_prev[0]);
+      pv((i - 1) & 1, 1, p_prev[1]);
+    }
+    if (HAS_NEXT) {
+      s_next[0] = qk((i + 1) & 1, 0);
+      s_next[1] = qk((i + 1) & 1, 1);
+    }
+    lsum *= alpha_pending;
+    exp_pack(s_cur[0], muse, p_prev[0]);
+    exp_pack(s_cur[1], muse, p_prev[1]);
+
+    sm.pos[grp][(i + 2) % 3][tid & 63] = next_pos;
+    // this wave's LDS loads must land before the barrier publishes them
+    __builtin_amdgcn_s_waitcnt(0x0f70 /* vmcnt(0) */ & 0xffff);
+    __syncthreads();
+    if (HAS_NEXT) {
+      s_cur[0] = s_next[0];
+      s_cur[1] = s_next[1];
+    }
+  }
+
+  __device__ void run(int qt, int head) {
+    const int kvh = head / (a.h_q / a.h_kv);
+    const int row0_wg = qt * ROWS;
+    const int row0 = row0_wg + gwave * WAVE_ROWS;
+    const int n_kt = (n_k + BN - 1) / BN;
+    n_iter = n_kt;
+    if (causal) {
+      const int qmax_wg = a.q_pos[min(row0_wg + ROWS, n_q) - 1];
+      int cnt = 0;
+      for (int j = lane; j < n_kt; j += 64) cnt += (a.k_pos[j * BN] <= qmax_wg) ? 1 : 0;
+      n_iter = wave_sum_i(cnt);
+    }
+    wave_valid = row0 < n_q;
+    const bool count = a.work != nullptr && head == 0 && wave_valid;
+    // tiles of this group among all key tiles, and among the visited ones
+    const int n_kt_g = (n_kt - grp + 1) / 2;
+    n_own = (n_iter - grp + 1) / 2;
+    if (READ && !FINAL && n_iter == 0) {
+      if (count && lane == 0) atomicAdd(a.work + 2, (unsigned long long)n_kt_g);
+      return;
+    }
+
+    if (!wave_valid) {
+      qmin_w = qmax_w = kPosRowNone;
+    } else if (causal) {
+      qmin_w = a.q_pos[row0];
+      qmax_w = a.q_pos[min(row0 + WAVE_ROWS, n_q) - 1];
+    } else {
+      qmin_w = qmax_w = kPosRowAll;
+    }
+    const int row = row0 + col;
+    qp = row < n_q ? (causal ? a.q_pos[row] : kPosRowAll) : kPosRowNone;
+    kbase = (const uint16_t*)a.k + ((size_t)kvh * n_k) * D;
+    vbase = (const uint16_t*)a.v + ((size_t)kvh * n_k) * D;
+    {
+      const uint16_t* qb = (const uint16_t*)a.q + ((size_t)head * n_q) * D;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        q[ks] = row < n_q ? *(const bf16x8*)(qb + (size_t)row * D + ks * 16 + h * 8) : bf16x8{};
+    }
+
+    float m_nat0 = -INFINITY;
+    m2 = -INFINITY;
+    lsum = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+    const size_t srow = (size_t)head * n_q + row;
+    // Group 0 carries the incoming state; group 1 starts empty.
+    if (READ && grp == 0 && row < n_q) {
+      m_nat0 = a.m_in[srow];
+      m2 = m_nat0 * kLog2e;
+      lsum = h == 0 ? a.l_in[srow] : 0.f;
+      const float* orow = a.o_in + srow * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 x = *(const f32x4*)(orow + db * 32 + 8 * g + 4 * h);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[db][4 * g + e] = x[e];
+        }
+    }
+    const float m2_0 = m2;
+    c2 = a.c2;
+    cnt_full = cnt_masked = 0;
+    need_rescale = false;
+
+    const int n_super = (n_iter + 1) / 2;
+    if (n_super > 0) {
+      // Prologue: K of own tiles 0 and 1 and their positions, then S^T of
+      // own tile 0.  Both groups run every barrier.
+      if (n_own > 0) {
+        load_k_tile(grp, 0);
+        sm.pos[grp][0][tid & 63] = fetch_pos(grp);
+      }
+      if (n_own > 1) {
+        load_k_tile(2 + grp, 1);
+        sm.pos[grp][1][tid & 63] = fetch_pos(2 + grp);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0f70 & 0xffff);
+      __syncthreads();
+      if (n_own > 0) {
+        s_cur[0] = qk(0, 0);
+        s_cur[1] = qk(0, 1);
+      }
+      __syncthreads();  // K stage 0 is refilled in own iteration 0
+
+      for (int si = 0; si < n_super; ++si) {
+        if (si >= 1 && si + 1 < n_own) {
+          iteration<true, true>(si);
+        } else if (si < n_own) {
+          if (si == 0 && n_own > 1) iteration<false, true>(si);
+          else if (si == 0) iteration<false, false>(si);
+          else iteration<true, false>(si);
+        } else {
+          __syncthreads();  // this group has no tile in this round
+        }
+      }
+      if (n_own > 0) {
+        apply_pending_rescale();
+        pv((n_own - 1) & 1, 0, p_prev[0]);
+        pv((n_own - 1) & 1, 1, p_prev[1]);
+      }
+    }
+
+    if (count && lane == 0) {
+      atomicAdd(a.work + 0, (unsigned long long)cnt_full);
+      atomicAdd(a.work + 1, (unsigned long long)cnt_masked);
+      atomicAdd(a.work + 2, (unsigned long long)(n_kt_g - cnt_full - cnt_masked));
+    }
+
+    // Fold group 1's partial state into group 0's through LDS.
+    __syncthreads();  // every wave is done with the K/V stages
+    float* mo = (float*)&sm.k[0][0][0];            // [wave][reg][lane] O^T values
+    float* ml = mo + 4 * 64 * 64;                  // [wave][lane] m2, then lsum
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mo[(gwave * 64 + db * 16 + r) * 64 + lane] = o[db][r];
+      ml[gwave * 64 + lane] = m2;
+      ml[4 * 64 + gwave * 64 + lane] = lsum;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    {
+      const float m2b = ml[gwave * 64 + lane];
+      const float lb = ml[4 * 64 + gwave * 64 + lane];
+      const float mn = fmaxf(m2, m2b);
+      const float fa = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mn);
+      const float fb = (m2b == -INFINITY) ? 0.f : fast_exp2(m2b - mn);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          o[db][r] = o[db][r] * fa + mo[(gwave * 64 + db * 16 + r) * 64 + lane] * fb;
+      lsum = lsum * fa + lb * fb;
+      m2 = mn;
+    }
+
+    const float ltot = half_swap_sum(lsum);
+    if (row >= n_q) return;
+    const float m_nat = (m2 == m2_0) ? m_nat0 : m2 * kLn2;
+    if (FINAL) {
+      const bool ok = ltot > 0.f;
+      const float inv = ok ? 1.f / ltot : 0.f;
+      float* orow = a.out + srow * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = o[db][4 * g + e] * inv;
+          *(f32x4*)(orow + db * 32 + 8 * g + 4 * h) = x;
+        }
+      if (h == 0) a.lse[srow] = ok ? m_nat + logf(ltot) : -INFINITY;
+    } else {
+      float* orow = a.o_out + srow * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = o[db][4 * g + e];
+          *(f32x4*)(orow + db * 32 + 8 * g + 4 * h) = x;
+        }
+      if (h == 0) {
+        a.m_out[srow] = m_nat;
+        a.l_out[srow] = ltot;
+      }
+    }
+  }
+};
+
+template <bool READ, bool FINAL>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void step_kernel_fast(const StepArgs a) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x;
+  const int u = blockIdx.x;
+  const int head = a.head_of[u % a.h_q];
+  const int p = u / a.h_q;
+  const int t_hi = a.n_qt - 1 - p, t_lo = p;
+  Step<READ, FINAL> s(a, sm, tid);
+  s.run(t_hi, head);
+  if (t_lo < t_hi) {
+    __syncthreads();
+    s.run(t_lo, head);
+  }
+}
+
+}  // namespace fast
+
+hipError_t launch_step_fast(const StepArgs& a, bool read, bool final_, hipStream_t stream) {
+  dim3 grid((unsigned)(a.n_pairs * a.h_q)), block(fast::THREADS);
+  if (read && final_)
+    hipLaunchKernelGGL((fast::step_kernel_fast<true, true>), grid, block, 0, stream, a);
+  else if (read)
+    hipLaunchKernelGGL((fast::step_kernel_fast<true, false>), grid, block, 0, stream, a);
+  else if (final_)
+    hipLaunchKernelGGL((fast::step_kernel_fast<false, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((fast::step_kernel_fast<false, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace ra

@@ -41,6 +41,8 @@ struct StepArgs {
 
 hipError_t launch_step(const StepArgs& a, int dtype, int d_k, bool read, bool final_,
                        hipStream_t stream);
+// bfloat16, d_k = 128: the 8-wave kernel with direct-to-LDS staging.
+hipError_t launch_step_fast(const StepArgs& a, bool read, bool final_, hipStream_t stream);
 hipError_t launch_state_init(float* m, float* l, float* o, int64_t rows, int d_k,
                              hipStream_t stream);
 hipError_t launch_finalize(const float* m, const float* l, const float* o, float* out,

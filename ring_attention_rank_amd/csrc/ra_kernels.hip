@@ -9,11 +9,11 @@
 // "Context Parallelism (CP)" concept page names in "Key math / How it works".
 //
 // Mapping onto CDNA4:
-//  * A workgroup is 4 waves and owns a pair of 128-row query tiles of one
-//    head (tile t and its mirror n_qt-1-t, processed in turn, so causal
-//    triangles and zigzag steps give every workgroup the same work).  Each
-//    wave owns 32 query rows.  A wave needs at most 256 registers, so two
-//    workgroups can share a CU (two waves per SIMD).
+//  * A workgroup is 4 waves (one per SIMD) and owns a pair of 128-row query
+//    tiles of one head (tile t and its mirror n_qt-1-t, processed in turn, so
+//    causal triangles and zigzag steps give every workgroup the same work).
+//    Each wave owns 32 query rows and has the SIMD's whole register file, so
+//    operands can be fetched from LDS well ahead of their MFMAs.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
 //    (fp32 inputs: v_mfma_f32_32x32x2_f32).  K is the A operand, read from
 //    LDS; Q is the B operand and stays in registers.  In the S^T accumulator
@@ -24,11 +24,11 @@
 //    P^T then feeds the PV MFMA (O^T = V^T P^T) as the B operand straight from
 //    the accumulators, and V^T staged in LDS gives the A operand in one
 //    16-byte read.
-//  * Software pipeline: while tile j's softmax runs on the VALU, the QK MFMAs
-//    of tile j+1 are issued, and the PV MFMAs of tile j's first 32 keys run
-//    while the exponentials of its last 32 keys are computed.  K tiles are
-//    staged two tiles ahead and V tiles one ahead (register-staged 16-byte
-//    loads, padded LDS rows), so one barrier per tile suffices.
+//  * Software pipeline: while tile j's softmax runs on the VALU, the MFMA
+//    pipe runs the PV of tile j-1 and the QK of tile j+1, neither of which
+//    depends on it.  K tiles are staged two tiles ahead and V tiles one ahead
+//    (register-staged 16-byte loads, padded LDS rows), so one barrier per
+//    tile suffices.
 //  * Rescale on demand: O and l are multiplied by exp(m_old - m_new) only on
 //    tiles where some row of the wave raised its maximum (a wave-wide ballot);
 //    once a row has seen a few hundred keys that is rare.  m stays the exact
@@ -44,6 +44,16 @@
 #include "ra_internal.h"
 
 namespace ra {
+
+#ifndef RA_SCHED_PREFETCH
+#define RA_SCHED_PREFETCH 4
+#endif
+#ifndef RA_SCHED_VALU
+#define RA_SCHED_VALU 4
+#endif
+#ifndef RA_BF16_WAVES_PER_EU
+#define RA_BF16_WAVES_PER_EU 1
+#endif
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -94,7 +104,7 @@ struct TraitsBf16 {
   typedef uint16_t Elem;   // bfloat16 bits in HBM
   typedef uint16_t LK;     // LDS element of the K stage
   typedef uint16_t LV;     // LDS element of the V^T stage
-  static constexpr int WAVES_PER_EU = 2;
+  static constexpr int WAVES_PER_EU = RA_BF16_WAVES_PER_EU;
   static constexpr int CPR = D / 8;                      // 16-byte chunks per row
   static constexpr int KCH = kKeysPerTile * CPR / 256;   // K chunks per thread per tile
   static constexpr int NV = KCH;                         // V keys per thread per tile
@@ -128,7 +138,10 @@ struct TraitsBf16 {
       int c = tid + 256 * p;
       int key = c / CPR, dc = c % CPR;
       int gk = j0 + key;
-      g.c[p] = gk < n_k ? *(const u32x4*)(kb + (size_t)gk * D + dc * 8) : u32x4{0, 0, 0, 0};
+      // Rows past the block are read from its last row and zeroed, so the
+      // load needs no branch.
+      u32x4 x = *(const u32x4*)(kb + (size_t)min(gk, n_k - 1) * D + dc * 8);
+      g.c[p] = gk < n_k ? x : u32x4{0, 0, 0, 0};
     }
   }
   static __device__ __forceinline__ void store_k(const KRegs& g, LK* sk, int tid) {
@@ -148,7 +161,8 @@ struct TraitsBf16 {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       int gk = j0 + kg * NV + i;
-      g.c[i] = gk < n_k ? *(const u32x4*)(vb + (size_t)gk * D + dc * 8) : u32x4{0, 0, 0, 0};
+      u32x4 x = *(const u32x4*)(vb + (size_t)min(gk, n_k - 1) * D + dc * 8);
+      g.c[i] = gk < n_k ? x : u32x4{0, 0, 0, 0};
     }
   }
   static __device__ __forceinline__ void store_v(const VRegs& g, LV* svt, int tid) {
@@ -249,7 +263,8 @@ struct TraitsF32 {
       int ci = tid + 256 * p;
       int key = ci / CPR, dc = ci % CPR;
       int gk = j0 + key;
-      c[p] = gk < n_k ? *(const f32x4*)(base + (size_t)gk * D + dc * 4) : f32x4{0, 0, 0, 0};
+      f32x4 x = *(const f32x4*)(base + (size_t)min(gk, n_k - 1) * D + dc * 4);
+      c[p] = gk < n_k ? x : f32x4{0, 0, 0, 0};
     }
   }
   static __device__ __forceinline__ void store_rows(const f32x4 (&c)[KCH], float* sm, int tid) {
@@ -327,120 +342,97 @@ __device__ __forceinline__ void apply_mask(f32x16& s, const int32_t* pos, int kb
   for (int r = 0; r < 16; ++r) s[r] = (kp4[r >> 2][r & 3] <= qp) ? s[r] : -INFINITY;
 }
 
+// Position of key gk of the block as the tile masks see it (branch-free:
+// the load is clamped into the block).  Requires n_k >= 1.
 __device__ __forceinline__ int key_pos(const StepArgs& a, int gk, bool causal) {
-  return gk < a.n_k ? (causal ? a.k_pos[gk] : kPosAlways) : kPosHidden;
+  const int p = a.k_pos[min(gk, a.n_k - 1)];
+  return gk < a.n_k ? (causal ? p : kPosAlways) : kPosHidden;
 }
 
 // One 128-row query tile of one head against the whole key/value block.
+//
+// Pipeline, per wave, for key tile j (PV(j-1) and QK(j+1) are independent of
+// the softmax of tile j, so the MFMA and VALU streams of an iteration overlap):
+//   MFMA: O^T += V_{j-1}^T P_{j-1}^T        (previous tile's probabilities)
+//         S_{j+1}^T = K_{j+1} Q^T          (next tile's scores)
+//   VALU: mask S_j (diagonal/ragged tiles), row max, P_j = 2^(S_j c - m)
+//   O is rescaled, if the max moved, at the top of the next iteration (after
+//   PV(j-1), before PV(j)).
+// LDS: K_{j+1} and V_{j-1} are read while K_{j+2} and V_j are written to the
+// other stages, so one barrier per tile orders everything.
 template <typename Tr, int D, bool READ, bool FINAL>
-__device__ __forceinline__ void run_qtile(const StepArgs& a, Smem<Tr>& sm, int qt, int head,
-                                          int tid) {
+struct QTile {
   typedef typename Tr::Elem E;
-  constexpr int DB = D / 32;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int h = lane >> 5;
-  const int col = lane & 31;
-  const int n_q = a.n_q, n_k = a.n_k;
-  const bool causal = a.causal != 0;
-  const int kvh = head / (a.h_q / a.h_kv);
-  const int row0_wg = qt * kRowsPerGroup;
-  const int row0 = row0_wg + wave * kRowsPerWave;
+  static constexpr int DB = D / 32;
 
-  // Key tiles this workgroup visits: those whose first key is visible to the
-  // group's last row (a prefix, since positions increase).
-  const int n_kt = (n_k + kKeysPerTile - 1) / kKeysPerTile;
-  int n_iter = n_kt;
-  if (causal) {
-    const int qmax_wg = a.q_pos[min(row0_wg + kRowsPerGroup, n_q) - 1];
-    int cnt = 0;
-    for (int j = lane; j < n_kt; j += 64) cnt += (a.k_pos[j * kKeysPerTile] <= qmax_wg) ? 1 : 0;
-    n_iter = wave_sum_i(cnt);
-  }
-  const bool wave_valid = row0 < n_q;
-  const bool count = a.work != nullptr && head == 0 && wave_valid;
-  if (READ && !FINAL && n_iter == 0) {
-    // No row of this tile sees the block: its state stays as it is.
-    if (count && lane == 0) atomicAdd(a.work + 2, (unsigned long long)n_kt);
-    return;
-  }
+  const StepArgs& a;
+  Smem<Tr>& sm;
+  const int tid, lane, wave, h, col;
+  const int n_q, n_k;
+  const bool causal;
+  const E* kbase;
+  const E* vbase;
+  int n_iter = 0;
+  bool wave_valid = false;
+  int qmin_w = 0, qmax_w = 0, qp = 0;
+  float c2 = 0.f;
 
-  // This wave's rows and this lane's query position.
-  int qmin_w, qmax_w;
-  if (!wave_valid) {
-    qmin_w = qmax_w = kPosRowNone;
-  } else if (causal) {
-    qmin_w = a.q_pos[row0];
-    qmax_w = a.q_pos[min(row0 + kRowsPerWave, n_q) - 1];
-  } else {
-    qmin_w = qmax_w = kPosRowAll;
-  }
-  const int row = row0 + col;
-  const int qp = row < n_q ? (causal ? a.q_pos[row] : kPosRowAll) : kPosRowNone;
-
-  const E* kbase = (const E*)a.k + ((size_t)kvh * n_k) * D;
-  const E* vbase = (const E*)a.v + ((size_t)kvh * n_k) * D;
   typename Tr::Q q;
-  Tr::load_q(q, (const E*)a.q + ((size_t)head * n_q) * D, row, n_q, h);
-
-  // Running state in base-2 units: m2 is the running maximum the sums are
-  // taken against, lsum this half-wave's share of the exp-sum, o the O^T
-  // accumulators.
   f32x16 o[DB];
-  float m2 = -INFINITY, lsum = 0.f, m_nat0 = -INFINITY;
-#pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  const size_t srow = (size_t)head * n_q + row;
-  if (READ && row < n_q) {
-    m_nat0 = a.m_in[srow];
-    m2 = m_nat0 * kLog2e;  // -inf stays -inf
-    lsum = h == 0 ? a.l_in[srow] : 0.f;
-    const float* orow = a.o_in + srow * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 x = *(const f32x4*)(orow + db * 32 + 8 * g + 4 * h);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[db][4 * g + e] = x[e];
-      }
-  }
-  const float m2_0 = m2;
-  const float c2 = a.c2;
+  float m2 = -INFINITY, lsum = 0.f;
   int cnt_full = 0, cnt_masked = 0;
-
   typename Tr::KRegs gk;
   typename Tr::VRegs gv;
-  f32x16 s_cur[2];
-  if (n_iter > 0) {
-    // Prologue: K0, K1, V0 and positions 0, 1 into LDS, then S^T of tile 0.
-    Tr::load_k(gk, kbase, 0, n_k, tid);
-    Tr::load_v(gv, vbase, 0, n_k, tid);
-    if (tid < kKeysPerTile) sm.pos[0][tid] = key_pos(a, tid, causal);
-    Tr::store_k(gk, sm.k[0], tid);
-    Tr::store_v(gv, sm.v[0], tid);
-    if (n_iter > 1) {
-      Tr::load_k(gk, kbase, kKeysPerTile, n_k, tid);
-      if (tid < kKeysPerTile) sm.pos[1][tid] = key_pos(a, kKeysPerTile + tid, causal);
-      Tr::store_k(gk, sm.k[1], tid);
+  f32x16 s_cur[2], s_next[2];
+  typename Tr::P p_prev[2];
+  bool need_rescale = false;
+  float alpha_pending = 1.f;
+
+  __device__ QTile(const StepArgs& a_, Smem<Tr>& sm_, int tid_)
+      : a(a_), sm(sm_), tid(tid_), lane(tid_ & 63),
+        wave(__builtin_amdgcn_readfirstlane(tid_ >> 6)), h((tid_ & 63) >> 5),
+        col(tid_ & 31), n_q(a_.n_q), n_k(a_.n_k), causal(a_.causal != 0), kbase(nullptr),
+        vbase(nullptr) {}
+
+  // Scheduling hint for the iteration's main block: alternate one MFMA, one
+  // LDS read and a few VALU instructions, with a few LDS reads issued ahead,
+  // so the softmax fills the MFMA pipe's shadow and operand reads are in
+  // flight before their MFMAs.
+  template <int NM>
+  __device__ __forceinline__ static void interleave() {
+    if constexpr (NM > 0) {
+      __builtin_amdgcn_sched_group_barrier(0x100, RA_SCHED_PREFETCH, 0);  // DS read
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);               // DS read
+        __builtin_amdgcn_sched_group_barrier(0x402, RA_SCHED_VALU, 0);   // VALU incl. exp
+      }
     }
-    __syncthreads();
-    s_cur[0] = Tr::qk(q, sm.k[0], 0, col, h);
-    s_cur[1] = Tr::qk(q, sm.k[0], 1, col, h);
-    // K stage 0 is refilled during the first iteration: every wave must be
-    // done reading it.
-    if (n_iter > 2) __syncthreads();
   }
 
-  for (int j = 0; j < n_iter; ++j) {
-    const bool has1 = j + 1 < n_iter, has2 = j + 2 < n_iter;
-    const int sk_next = (j + 1) & 1, sv_cur = j & 1;
-    int next_pos = kPosHidden;
-    if (has2) {
-      Tr::load_k(gk, kbase, (j + 2) * kKeysPerTile, n_k, tid);
-      if (tid < kKeysPerTile) next_pos = key_pos(a, (j + 2) * kKeysPerTile + tid, causal);
+  // Rescale O when the previous iteration's softmax moved the max.  It runs
+  // at the top of an iteration: after PV(j-2) (issued last iteration) and
+  // before PV(j-1), and outside the block where MFMAs and exponentials
+  // interleave.
+  __device__ __forceinline__ void apply_pending_rescale() {
+    if (need_rescale) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha_pending;
     }
-    if (has1) Tr::load_v(gv, vbase, (j + 1) * kKeysPerTile, n_k, tid);
+  }
+
+  template <bool PV_PREV, bool QK_NEXT>
+  __device__ __forceinline__ void iteration(int j) {
+    apply_pending_rescale();
+    // Staging loads: K two tiles ahead (clamped; a repeated tile lands in a
+    // stage nobody reads), V of this tile for the next iteration's PV.
+    const int jk = min(j + 2, n_iter - 1);
+    Tr::load_k(gk, kbase, jk * kKeysPerTile, n_k, tid);
+    // Every thread fetches one position; the four waves write the same 64
+    // values, which keeps the block free of divergent branches.
+    const int next_pos = key_pos(a, jk * kKeysPerTile + (tid & (kKeysPerTile - 1)), causal);
+    Tr::load_v(gv, vbase, j * kKeysPerTile, n_k, tid);
 
     // Classify tile j for this wave's rows (valid keys only).
     const int32_t* pos = sm.pos[j % 3];
@@ -450,93 +442,189 @@ __device__ __forceinline__ void run_qtile(const StepArgs& a, Smem<Tr>& sm, int q
     const bool ragged = j0 + kKeysPerTile > n_k;
     const bool skip = !wave_valid || kmin > qmax_w;
     const bool full = kmax <= qmin_w;
-
-    f32x16 s_next[2];
     if (!skip) {
       if (full) ++cnt_full; else ++cnt_masked;
-      if (!full || ragged) {
-        apply_mask(s_cur[0], pos, 0, h, qp);
-        apply_mask(s_cur[1], pos, 1, h, qp);
-      }
-      if (has1) s_next[0] = Tr::qk(q, sm.k[sk_next], 0, col, h);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s_cur[0][r], s_cur[1][r]));
-      const float mloc = half_swap_max(mx) * c2;
-      if (__ballot(mloc > m2) != 0) {
-        const float mnew = fmaxf(m2, mloc);
-        const float alpha = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mnew);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= alpha;
-        lsum *= alpha;
-        m2 = mnew;
-      }
-      // A row with nothing visible yet keeps m2 = -inf and gets P = 0.
-      const float muse = (m2 == -INFINITY) ? 0.f : m2;
-      if (has1) s_next[1] = Tr::qk(q, sm.k[sk_next], 1, col, h);
-      typename Tr::P p0 = Tr::exp_pack(s_cur[0], c2, muse, lsum);
-      Tr::pv(o, p0, sm.v[sv_cur], 0, col, h);
-      typename Tr::P p1 = Tr::exp_pack(s_cur[1], c2, muse, lsum);
-      Tr::pv(o, p1, sm.v[sv_cur], 1, col, h);
-    } else if (has1) {
-      s_next[0] = Tr::qk(q, sm.k[sk_next], 0, col, h);
-      s_next[1] = Tr::qk(q, sm.k[sk_next], 1, col, h);
+    }
+    if (skip || !full || ragged) {
+      // A skipped tile is masked completely: P = 0, nothing changes.
+      const int qpe = skip ? kPosRowNone : qp;
+      apply_mask(s_cur[0], pos, 0, h, qpe);
+      apply_mask(s_cur[1], pos, 1, h, qpe);
     }
 
-    if (has2) {
-      Tr::store_k(gk, sm.k[j & 1], tid);
-      if (tid < kKeysPerTile) sm.pos[(j + 2) % 3][tid] = next_pos;
+    // ---- one branch-free block: MFMA stream and softmax interleave ----
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s_cur[0][r], s_cur[1][r]));
+    const float mloc = half_swap_max(mx) * c2;
+    need_rescale = __ballot(mloc > m2) != 0;
+    const float mnew = fmaxf(m2, mloc);
+    alpha_pending = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mnew);
+    m2 = mnew;
+    // A row with nothing visible yet keeps m2 = -inf and gets P = 0.
+    const float muse = (m2 == -INFINITY) ? 0.f : m2;
+
+    if (PV_PREV) {
+      Tr::pv(o, p_prev[0], sm.v[(j - 1) & 1], 0, col, h);
+      Tr::pv(o, p_prev[1], sm.v[(j - 1) & 1], 1, col, h);
     }
-    if (has1) Tr::store_v(gv, sm.v[(j + 1) & 1], tid);
+    if (QK_NEXT) {
+      s_next[0] = Tr::qk(q, sm.k[(j + 1) & 1], 0, col, h);
+      s_next[1] = Tr::qk(q, sm.k[(j + 1) & 1], 1, col, h);
+    }
+    lsum *= alpha_pending;
+    p_prev[0] = Tr::exp_pack(s_cur[0], c2, muse, lsum);
+    p_prev[1] = Tr::exp_pack(s_cur[1], c2, muse, lsum);
+
+    Tr::store_k(gk, sm.k[j & 1], tid);
+    sm.pos[(j + 2) % 3][tid & (kKeysPerTile - 1)] = next_pos;
+    Tr::store_v(gv, sm.v[j & 1], tid);
+    interleave<(PV_PREV ? 16 : 0) + (QK_NEXT ? 16 : 0)>();
     __syncthreads();
-    if (has1) {
+    if (QK_NEXT) {
       s_cur[0] = s_next[0];
       s_cur[1] = s_next[1];
     }
   }
 
-  if (count && lane == 0) {
-    atomicAdd(a.work + 0, (unsigned long long)cnt_full);
-    atomicAdd(a.work + 1, (unsigned long long)cnt_masked);
-    atomicAdd(a.work + 2, (unsigned long long)(n_kt - cnt_full - cnt_masked));
-  }
+  __device__ void run(int qt, int head) {
+    const int kvh = head / (a.h_q / a.h_kv);
+    const int row0_wg = qt * kRowsPerGroup;
+    const int row0 = row0_wg + wave * kRowsPerWave;
 
-  // Epilogue: combine the half-wave sums and write the state or the result.
-  const float ltot = half_swap_sum(lsum);
-  if (row >= n_q) return;
-  // A row whose reference did not move writes back its exact bits.
-  const float m_nat = (m2 == m2_0) ? m_nat0 : m2 * kLn2;
-  if (FINAL) {
-    const bool ok = ltot > 0.f;
-    const float inv = ok ? 1.f / ltot : 0.f;
-    float* orow = a.out + srow * D;
+    // Key tiles this workgroup visits: those whose first key is visible to
+    // the group's last row (a prefix, since positions increase).
+    const int n_kt = (n_k + kKeysPerTile - 1) / kKeysPerTile;
+    n_iter = n_kt;
+    if (causal) {
+      const int qmax_wg = a.q_pos[min(row0_wg + kRowsPerGroup, n_q) - 1];
+      int cnt = 0;
+      for (int j = lane; j < n_kt; j += 64) cnt += (a.k_pos[j * kKeysPerTile] <= qmax_wg) ? 1 : 0;
+      n_iter = wave_sum_i(cnt);
+    }
+    wave_valid = row0 < n_q;
+    const bool count = a.work != nullptr && head == 0 && wave_valid;
+    if (READ && !FINAL && n_iter == 0) {
+      // No row of this tile sees the block: its state stays as it is.
+      if (count && lane == 0) atomicAdd(a.work + 2, (unsigned long long)n_kt);
+      return;
+    }
+
+    // This wave's rows and this lane's query position.
+    if (!wave_valid) {
+      qmin_w = qmax_w = kPosRowNone;
+    } else if (causal) {
+      qmin_w = a.q_pos[row0];
+      qmax_w = a.q_pos[min(row0 + kRowsPerWave, n_q) - 1];
+    } else {
+      qmin_w = qmax_w = kPosRowAll;
+    }
+    const int row = row0 + col;
+    qp = row < n_q ? (causal ? a.q_pos[row] : kPosRowAll) : kPosRowNone;
+
+    kbase = (const E*)a.k + ((size_t)kvh * n_k) * D;
+    vbase = (const E*)a.v + ((size_t)kvh * n_k) * D;
+    Tr::load_q(q, (const E*)a.q + ((size_t)head * n_q) * D, row, n_q, h);
+
+    // Running state in base-2 units: m2 is the running maximum the sums are
+    // taken against, lsum this half-wave's share of the exp-sum, o the O^T
+    // accumulators.  m_nat0 / m2_0 keep the state's max as read, so a row
+    // whose max does not move writes back the identical bits.
+    float m_nat0 = -INFINITY;
+    m2 = -INFINITY;
+    lsum = 0.f;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+    const size_t srow = (size_t)head * n_q + row;
+    if (READ && row < n_q) {
+      m_nat0 = a.m_in[srow];
+      m2 = m_nat0 * kLog2e;  // -inf stays -inf
+      lsum = h == 0 ? a.l_in[srow] : 0.f;
+      const float* orow = a.o_in + srow * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 x;
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = o[db][4 * g + e] * inv;
-        *(f32x4*)(orow + db * 32 + 8 * g + 4 * h) = x;
+        for (int g = 0; g < 4; ++g) {
+          f32x4 x = *(const f32x4*)(orow + db * 32 + 8 * g + 4 * h);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[db][4 * g + e] = x[e];
+        }
+    }
+    const float m2_0 = m2;
+    c2 = a.c2;
+    cnt_full = cnt_masked = 0;
+    need_rescale = false;
+
+    if (n_iter > 0) {
+      // Prologue: K0, K1 and their positions into LDS, then S^T of tile 0.
+      Tr::load_k(gk, kbase, 0, n_k, tid);
+      if (tid < kKeysPerTile) sm.pos[0][tid] = key_pos(a, tid, causal);
+      Tr::store_k(gk, sm.k[0], tid);
+      if (n_iter > 1) {
+        Tr::load_k(gk, kbase, kKeysPerTile, n_k, tid);
+        if (tid < kKeysPerTile) sm.pos[1][tid] = key_pos(a, kKeysPerTile + tid, causal);
+        Tr::store_k(gk, sm.k[1], tid);
       }
-    if (h == 0) a.lse[srow] = ok ? m_nat + logf(ltot) : -INFINITY;
-  } else {
-    float* orow = a.o_out + srow * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = o[db][4 * g + e];
-        *(f32x4*)(orow + db * 32 + 8 * g + 4 * h) = x;
+      __syncthreads();
+      s_cur[0] = Tr::qk(q, sm.k[0], 0, col, h);
+      s_cur[1] = Tr::qk(q, sm.k[0], 1, col, h);
+      __syncthreads();  // K stage 0 is refilled during the first iteration
+
+      if (n_iter == 1) {
+        iteration<false, false>(0);
+      } else {
+        iteration<false, true>(0);
+        for (int j = 1; j < n_iter - 1; ++j) iteration<true, true>(j);
+        iteration<true, false>(n_iter - 1);
       }
-    if (h == 0) {
-      a.m_out[srow] = m_nat;
-      a.l_out[srow] = ltot;
+      // The last tile's PV.
+      apply_pending_rescale();
+      Tr::pv(o, p_prev[0], sm.v[(n_iter - 1) & 1], 0, col, h);
+      Tr::pv(o, p_prev[1], sm.v[(n_iter - 1) & 1], 1, col, h);
+    }
+
+    if (count && lane == 0) {
+      atomicAdd(a.work + 0, (unsigned long long)cnt_full);
+      atomicAdd(a.work + 1, (unsigned long long)cnt_masked);
+      atomicAdd(a.work + 2, (unsigned long long)(n_kt - cnt_full - cnt_masked));
+    }
+
+    // Epilogue: combine the half-wave sums and write the state or the result.
+    const float ltot = half_swap_sum(lsum);
+    if (row >= n_q) return;
+    const float m_nat = (m2 == m2_0) ? m_nat0 : m2 * kLn2;
+    if (FINAL) {
+      const bool ok = ltot > 0.f;
+      const float inv = ok ? 1.f / ltot : 0.f;
+      float* orow = a.out + srow * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = o[db][4 * g + e] * inv;
+          *(f32x4*)(orow + db * 32 + 8 * g + 4 * h) = x;
+        }
+      if (h == 0) a.lse[srow] = ok ? m_nat + logf(ltot) : -INFINITY;
+    } else {
+      float* orow = a.o_out + srow * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = o[db][4 * g + e];
+          *(f32x4*)(orow + db * 32 + 8 * g + 4 * h) = x;
+        }
+      if (h == 0) {
+        a.m_out[srow] = m_nat;
+        a.l_out[srow] = ltot;
+      }
     }
   }
-}
+};
 
 // One workgroup: a query head and a pair of query tiles (heavier one first).
 template <typename Tr, int D, bool READ, bool FINAL>
@@ -549,10 +637,11 @@ void step_kernel(const StepArgs a) {
   const int head = a.head_of[u % a.h_q];
   const int p = u / a.h_q;
   const int t_hi = a.n_qt - 1 - p, t_lo = p;
-  run_qtile<Tr, D, READ, FINAL>(a, sm, t_hi, head, tid);
+  QTile<Tr, D, READ, FINAL> t(a, sm, tid);
+  t.run(t_hi, head);
   if (t_lo < t_hi) {
     __syncthreads();  // LDS of the first tile is fully consumed
-    run_qtile<Tr, D, READ, FINAL>(a, sm, t_lo, head, tid);
+    t.run(t_lo, head);
   }
 }
 
@@ -606,7 +695,7 @@ static hipError_t launch_typed(const StepArgs& a, bool read, bool final_, hipStr
 hipError_t launch_step(const StepArgs& a, int dtype, int d_k, bool read, bool final_,
                        hipStream_t stream) {
   if (dtype == 0) {
-    if (d_k == 128) return launch_typed<TraitsBf16<128>, 128>(a, read, final_, stream);
+    if (d_k == 128) return launch_step_fast(a, read, final_, stream);
     return launch_typed<TraitsBf16<64>, 64>(a, read, final_, stream);
   }
   if (d_k == 128) return launch_typed<TraitsF32<128>, 128>(a, read, final_, stream);
