@@ -102,7 +102,7 @@ def main():
                     choices=[c.name for c in synth.CASES])
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-side-stream", action="store_true")
     args = ap.parse_args()
 
