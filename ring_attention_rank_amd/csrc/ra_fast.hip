@@ -26,9 +26,10 @@
 //    addressed, i.e. 4 consecutive keys of one d column.
 //  * Pipeline per wave, on its own tile j: the MFMA pipe runs PV of its
 //    previous tile and QK of its next tile while the VALU does the softmax
-//    of tile j; O is rescaled (only when some row's max moved) at the top of
-//    the next iteration.  K tiles are fetched two own-tiles ahead, V tiles one
-//    ahead; one barrier per tile pair.
+//    of tile j, in four phases that reuse the score and probability
+//    registers in place; O is rescaled (only when some row's max moved) at
+//    the top of the next iteration.  K tiles are fetched two own-tiles ahead,
+//    V tiles one ahead; one barrier per tile pair.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -58,6 +59,9 @@ constexpr int kPosHidden = 0x7fffffff;
 constexpr int kPosAlways = (int)0x80000000;
 constexpr int kPosRowNone = (int)0x80000000;
 constexpr int kPosRowAll = 0x7ffffffe;
+// Word 3 of a raw (untyped, stride-0) buffer resource on gfx9: 32-bit data
+// format; offsets at or past num_records read as zero.
+constexpr int kBufferFlags = 0x00020000;
 
 static_assert(ROWS == 4 * WAVE_ROWS, "4 waves per group");
 static_assert(kRowsPerGroup == ROWS, "host launch geometry");
@@ -105,9 +109,12 @@ struct Step {
   int qmin_w = 0, qmax_w = 0, qp = 0;
   float c2 = 0.f;
 
-  // per-lane LDS/global offsets (loop invariant)
-  int k_ld_off[4];   // byte offset inside a K tile for this lane's 4 load instructions
-  int v_ld_off;      // ditto for V (the 4 instructions differ by 1 KiB)
+  // Buffer resources of this head's K, V and key positions: loads past the
+  // block's end return zeros, so ragged tiles need no clamping.
+  __amdgpu_buffer_rsrc_t krs, vrs, prs;
+  // per-lane offsets (loop invariant)
+  int k_ld_off;      // byte offset in a K tile of this lane's first load (+4 KiB per instruction)
+  int v_ld_off;      // ditto for V
   int k_rd;          // K read base, XOR'ed with 32*ks
   int v_rd;          // V read base, XOR'ed with 64*db
 
@@ -115,8 +122,8 @@ struct Step {
   f32x16 o[4];
   float m2 = -INFINITY, lsum = 0.f;
   int cnt_full = 0, cnt_masked = 0;
-  f32x16 s_cur[2], s_next[2];
-  bf16x8 p_prev[2][2];
+  f32x16 sc[2];        // scores of the current own tile, overwritten by the next
+  bf16x8 pp[2][2];      // probabilities of the previous own tile, then the current
   bool need_rescale = false;
   float alpha_pending = 1.f;
 
@@ -125,20 +132,17 @@ struct Step {
         gwave(__builtin_amdgcn_readfirstlane((tid_ >> 6) & 3)),
         grp(__builtin_amdgcn_readfirstlane(tid_ >> 8)), h((tid_ & 63) >> 5), col(tid_ & 31),
         n_q(a_.n_q), n_k(a_.n_k), causal(a_.causal != 0), kbase(nullptr), vbase(nullptr) {
-    // K loads: instruction i of this wave fills rows 4b..4b+3, b = 4*gwave + i;
-    // lane L writes LDS chunk L%16 of row 4b + L/16, which holds logical chunk
-    // (L%16) ^ (row & 15).
-    const int L = lane;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * (4 * gwave + i) + L / 16;
-      const int c = (L % 16) ^ (r & 15);
-      k_ld_off[i] = r * 256 + c * 16;  // global byte offset of that chunk in the tile
-    }
+    // Tile loads: instruction i of this wave fills LDS rows 4b..4b+3 with
+    // b = gwave + 4i (rows 4*gwave + 16i + L/16 for lane L), so row & 15 and
+    // hence each lane's swizzle is the same for all four instructions, which
+    // then differ only by a scalar 4 KiB offset.  Lane L writes physical
+    // chunk L%16, holding logical chunk (L%16) ^ (row & 15) for K and
+    // (L%16) ^ 2(row & 3) for V.
     {
-      const int r = 4 * (4 * gwave) + L / 16;
-      const int c = (L % 16) ^ (2 * (r & 3));
-      v_ld_off = r * 256 + c * 16;
+      const int L = lane;
+      const int r = 4 * gwave + L / 16;
+      k_ld_off = r * 256 + 16 * ((L % 16) ^ (r & 15));
+      v_ld_off = r * 256 + 16 * ((L % 16) ^ (2 * (r & 3)));
     }
     // K reads: row sigma(col) (+32 kb), logical chunk 2ks + h.
     {
@@ -157,35 +161,22 @@ struct Step {
 
   // ---- tile staging (direct to LDS) --------------------------------------
   __device__ __forceinline__ void load_k_tile(int j, int stage) {
-    const int j0 = j * BN;
-    const char* src = (const char*)kbase;
     uint8_t* dst = sm.k[grp][stage];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = 4 * gwave + i;
-      // clamp rows past the block to its last row (masked off by position)
-      const int r = (k_ld_off[i] >> 8);
-      const int gr = min(j0 + r, n_k - 1);
-      const char* g = src + (size_t)gr * 256 + (k_ld_off[i] & 255);
-      __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(dst + b * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(dst + (gwave + 4 * i) * 1024), 16,
+                                               k_ld_off, j * BN * 256 + i * 4096, 0, 0);
   }
   __device__ __forceinline__ void load_v_tile(int j, int stage) {
-    const int j0 = j * BN;
-    const char* src = (const char*)vbase;
     uint8_t* dst = sm.v[grp][stage];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = 4 * gwave + i;
-      const int r = (v_ld_off >> 8) + 4 * i;
-      const int gr = min(j0 + r, n_k - 1);
-      const char* g = src + (size_t)gr * 256 + (v_ld_off & 255);
-      __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(dst + b * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(dst + (gwave + 4 * i) * 1024), 16,
+                                               v_ld_off, j * BN * 256 + i * 4096, 0, 0);
   }
   __device__ __forceinline__ int fetch_pos(int j) const {
     const int gk = j * BN + (tid & 63);
-    const int p = a.k_pos[min(gk, n_k - 1)];
+    const int p = __builtin_amdgcn_raw_buffer_load_b32(prs, (tid & 63) * 4, j * BN * 4, 0);
     return gk < n_k ? (causal ? p : kPosAlways) : kPosHidden;
   }
 
@@ -250,8 +241,14 @@ struct Step {
     }
   }
 
-  // One own tile i (global tile j = 2i + grp).  HAS_PREV: PV of own tile i-1
-  // is pending; HAS_NEXT: own tile i+1 exists.
+  // One own tile i (global tile j = 2i + grp).  HAS_PREV: PV of own tile
+  // i-1 is pending; HAS_NEXT: own tile i+1 exists.  The four phases below let
+  // every VALU step run beside MFMAs that do not depend on it, reusing the
+  // score and probability registers in place:
+  //   A: PV(i-1, keys 0-31)         | row max of tile i
+  //   B: PV(i-1, keys 32-63)        | P(i, keys 0-31)  (overwrites pp[0])
+  //   C: QK(i+1, keys 0-31) -> sc[0] | P(i, keys 32-63) (overwrites pp[1])
+  //   D: QK(i+1, keys 32-63) -> sc[1]
   template <bool HAS_PREV, bool HAS_NEXT>
   __device__ __forceinline__ void iteration(int i) {
     apply_pending_rescale();
@@ -275,40 +272,35 @@ struct Step {
     }
     if (skip || !full || ragged) {
       const int qpe = skip ? kPosRowNone : qp;
-      mask(s_cur[0], pos, 0, qpe);
-      mask(s_cur[1], pos, 1, qpe);
+      mask(sc[0], pos, 0, qpe);
+      mask(sc[1], pos, 1, qpe);
     }
 
+    // A
+    if (HAS_PREV) pv((i - 1) & 1, 0, pp[0]);
     float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s_cur[0][r], s_cur[1][r]));
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[0][r], sc[1][r]));
     const float mloc = half_swap_max(mx) * c2;
     need_rescale = __ballot(mloc > m2) != 0;
     const float mnew = fmaxf(m2, mloc);
     alpha_pending = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mnew);
     m2 = mnew;
     const float muse = (m2 == -INFINITY) ? 0.f : m2;
-
-    if (HAS_PREV) {
-      pv((i - 1) & 1, 0, p_prev[0]);
-      pv((i - 1) & 1, 1, p_prev[1]);
-    }
-    if (HAS_NEXT) {
-      s_next[0] = qk((i + 1) & 1, 0);
-      s_next[1] = qk((i + 1) & 1, 1);
-    }
     lsum *= alpha_pending;
-    exp_pack(s_cur[0], muse, p_prev[0]);
-    exp_pack(s_cur[1], muse, p_prev[1]);
+    // B
+    if (HAS_PREV) pv((i - 1) & 1, 1, pp[1]);
+    exp_pack(sc[0], muse, pp[0]);
+    // C
+    if (HAS_NEXT) sc[0] = qk((i + 1) & 1, 0);
+    exp_pack(sc[1], muse, pp[1]);
+    // D
+    if (HAS_NEXT) sc[1] = qk((i + 1) & 1, 1);
 
     sm.pos[grp][(i + 2) % 3][tid & 63] = next_pos;
     // this wave's LDS loads must land before the barrier publishes them
-    __builtin_amdgcn_s_waitcnt(0x0f70 /* vmcnt(0) */ & 0xffff);
+    __builtin_amdgcn_s_waitcnt(0x0f70 /* vmcnt(0) */);
     __syncthreads();
-    if (HAS_NEXT) {
-      s_cur[0] = s_next[0];
-      s_cur[1] = s_next[1];
-    }
   }
 
   __device__ void run(int qt, int head) {
@@ -345,6 +337,9 @@ struct Step {
     qp = row < n_q ? (causal ? a.q_pos[row] : kPosRowAll) : kPosRowNone;
     kbase = (const uint16_t*)a.k + ((size_t)kvh * n_k) * D;
     vbase = (const uint16_t*)a.v + ((size_t)kvh * n_k) * D;
+    krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, n_k * D * 2, kBufferFlags);
+    vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, n_k * D * 2, kBufferFlags);
+    prs = __builtin_amdgcn_make_buffer_rsrc((void*)a.k_pos, (short)0, n_k * 4, kBufferFlags);
     {
       const uint16_t* qb = (const uint16_t*)a.q + ((size_t)head * n_q) * D;
 #pragma unroll
@@ -393,8 +388,8 @@ struct Step {
       __builtin_amdgcn_s_waitcnt(0x0f70 & 0xffff);
       __syncthreads();
       if (n_own > 0) {
-        s_cur[0] = qk(0, 0);
-        s_cur[1] = qk(0, 1);
+        sc[0] = qk(0, 0);
+        sc[1] = qk(0, 1);
       }
       __syncthreads();  // K stage 0 is refilled in own iteration 0
 
@@ -411,8 +406,8 @@ struct Step {
       }
       if (n_own > 0) {
         apply_pending_rescale();
-        pv((n_own - 1) & 1, 0, p_prev[0]);
-        pv((n_own - 1) & 1, 1, p_prev[1]);
+        pv((n_own - 1) & 1, 0, pp[0]);
+        pv((n_own - 1) & 1, 1, pp[1]);
       }
     }
 
