@@ -93,7 +93,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // Byte offset of 16-byte chunk c of row r inside a K tile / a V tile.
 __device__ __forceinline__ int k_chunk_off(int r, int c) { return r * 256 + 16 * (c ^ (r & 15)); }
-__device__ __forceinline__ int v_chunk_off(int r, int c) { return r * 256 + 16 * (c ^ (2 * (r & 3))); }
+__device__ __forceinline__ int v_chunk_off(int r, int c) { return r * 256 + 16 * (c ^ (4 * (r & 3))); }
 
 template <bool READ, bool FINAL>
 struct Step {
@@ -137,12 +137,12 @@ struct Step {
     // hence each lane's swizzle is the same for all four instructions, which
     // then differ only by a scalar 4 KiB offset.  Lane L writes physical
     // chunk L%16, holding logical chunk (L%16) ^ (row & 15) for K and
-    // (L%16) ^ 2(row & 3) for V.
+    // (L%16) ^ 4(row & 3) for V.
     {
       const int L = lane;
       const int r = 4 * gwave + L / 16;
       k_ld_off = r * 256 + 16 * ((L % 16) ^ (r & 15));
-      v_ld_off = r * 256 + 16 * ((L % 16) ^ (2 * (r & 3)));
+      v_ld_off = r * 256 + 16 * ((L % 16) ^ (4 * (r & 3)));
     }
     // K reads: row sigma(col) (+32 kb), logical chunk 2ks + h.
     {
@@ -150,12 +150,14 @@ struct Step {
       const int x = r & 15;
       k_rd = r * 256 + 16 * (h ^ (x & 1)) + 32 * (x >> 1);  // ^ (32 ks) gives chunk 2ks+h
     }
-    // V reads (transposing): 16-lane group g4, lane i in the group.
+    // V reads (transposing): 16-lane group g4, lane i in the group reads row
+    // 8h + rho (+ tile offsets) at 8-byte piece 4(i&3) of d block db.  With
+    // the 4(row&3) swizzle the 32 lanes of a half-wave touch 16 distinct
+    // chunks, i.e. all 64 banks once.
     {
       const int g4 = lane >> 4, i = lane & 15;
       const int hh = g4 >> 1, dgrp = g4 & 1, rho = i >> 2, b = (i & 3) >> 1, half = i & 1;
-      const int T = (32 * dgrp + 16 * b) ^ (32 * rho);
-      v_rd = (8 * hh + rho) * 256 + 8 * half + T;  // ^ (64 db) selects the d block
+      v_rd = (8 * hh + rho) * 256 + 64 * rho + 32 * dgrp + 16 * b + 8 * half;  // ^ (64 db)
     }
   }
 
@@ -353,10 +355,14 @@ struct Step {
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db] = f32x16{};
     const size_t srow = (size_t)head * n_q + row;
-    // Group 0 carries the incoming state; group 1 starts empty.
-    if (READ && grp == 0 && row < n_q) {
+    // Group 0 carries the incoming state.  Group 1 starts with empty sums but
+    // the same reference max, so its first tiles do not trigger rescales
+    // (any reference at or above the scores seen gives the same softmax).
+    if (READ && row < n_q) {
       m_nat0 = a.m_in[srow];
       m2 = m_nat0 * kLog2e;
+    }
+    if (READ && grp == 0 && row < n_q) {
       lsum = h == 0 ? a.l_in[srow] : 0.f;
       const float* orow = a.o_in + srow * D;
 #pragma unroll
