@@ -5,14 +5,12 @@
 // "distributed/context-expert", section "Splitting the sequence, and the one
 // layer that objects"), organised for CDNA4 throughput:
 //
-//  * Two waves per SIMD.  A single wave issues VALU work at about half rate
-//    on gfx950, so the softmax only keeps up with the MFMA pipe when two
-//    waves share each SIMD.  A workgroup is 8 waves: two groups of 4 waves
+//  * Two waves per SIMD.  A workgroup is 8 waves: two groups of 4 waves
 //    on the same 128 query rows (32 per wave).  Group g takes the key tiles
 //    j = g, g+2, g+4, ... of the block; the two partial states are folded
 //    together through LDS at the end (the same online-softmax fold).
 //  * No staging registers.  K and V tiles go from HBM straight into LDS with
-//    global_load_lds_dwordx4, in row-major 256-byte rows whose 16-byte chunks
+//    buffer_load_dwordx4 ... lds, in row-major 256-byte rows whose 16-byte chunks
 //    are XOR-swizzled by row, so both read patterns below are free of bank
 //    conflicts.  That leaves each wave under 256 registers.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K rows are the A operand
@@ -24,12 +22,15 @@
 //  * The V^T operand comes from row-major V with ds_read_b64_tr_b16: within
 //    each 16-lane group, lane j receives element j of the 4 rows the group
 //    addressed, i.e. 4 consecutive keys of one d column.
-//  * Pipeline per wave, on its own tile j: the MFMA pipe runs PV of its
-//    previous tile and QK of its next tile while the VALU does the softmax
-//    of tile j, in four phases that reuse the score and probability
-//    registers in place; O is rescaled (only when some row's max moved) at
-//    the top of the next iteration.  K tiles are fetched two own-tiles ahead,
-//    V tiles one ahead; one barrier per tile pair.
+//  * Ping-pong between the two groups.  Each group alternates a softmax
+//    phase (VALU: classify, mask, row max, rescale, exponentials) and a GEMM
+//    phase (MFMA: P V of that tile, then S^T of its next tile), with a
+//    workgroup barrier after every phase.  Group 1 runs one phase behind
+//    group 0, so on each SIMD one wave keeps the matrix pipe busy while the
+//    other runs the softmax, and every barrier swaps the roles.
+//  * Loads are DMA issued three phases before their use and waited for with
+//    explicit vmcnt counts; K and V tiles have two stages per group,
+//    positions three.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -55,8 +56,6 @@ constexpr int THREADS = 512;                // 8 waves: 2 groups of 4
 constexpr int TILE_BYTES = BN * D * 2;      // 16 KiB
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kPosHidden = 0x7fffffff;
-constexpr int kPosAlways = (int)0x80000000;
 constexpr int kPosRowNone = (int)0x80000000;
 constexpr int kPosRowAll = 0x7ffffffe;
 // Word 3 of a raw (untyped, stride-0) buffer resource on gfx9: 32-bit data
@@ -91,6 +90,40 @@ __device__ __forceinline__ int wave_sum_i(int x) {
 }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Raw buffer resource (gfx9 layout): 48-bit base, stride 0, size in bytes,
+// 32-bit untyped data; every word is wave-uniform.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int bytes) {
+  const uint64_t b = (uint64_t)base;
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
+               __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32) & 0xffff),
+               __builtin_amdgcn_readfirstlane(bytes), kBufferFlags};
+}
+
+// One 16-byte-per-lane buffer load from HBM straight into LDS: lane L's 16
+// bytes land at lds + 16 L.  Bytes at or past the resource size read as zero.
+// Issued as inline asm so the compiler does not track it: it cannot tell that
+// the stage being filled is not the one being read, and would otherwise wait
+// for the load before the very next LDS read.  Callers wait (vmcnt(0)) before
+// the barrier that publishes the stage.  M0 carries the LDS address; the nop
+// is the required wait state between writing M0 and the LDS-DMA that reads it.
+__device__ __forceinline__ void dma_to_lds(const i32x4& rsrc, const void* lds, int voff, int soff) {
+  const int m0v = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void*)lds);
+  const int so = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(rsrc), "s"(so)
+               : "m0");
+}
+// Same for 4 bytes per lane (lane L's word lands at lds + 4 L).
+__device__ __forceinline__ void dma4_to_lds(const i32x4& rsrc, const void* lds, int voff, int soff) {
+  const int m0v = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void*)lds);
+  const int so = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(rsrc), "s"(so)
+               : "m0");
+}
+
 // Byte offset of 16-byte chunk c of row r inside a K tile / a V tile.
 __device__ __forceinline__ int k_chunk_off(int r, int c) { return r * 256 + 16 * (c ^ (r & 15)); }
 __device__ __forceinline__ int v_chunk_off(int r, int c) { return r * 256 + 16 * (c ^ (4 * (r & 3))); }
@@ -111,7 +144,7 @@ struct Step {
 
   // Buffer resources of this head's K, V and key positions: loads past the
   // block's end return zeros, so ragged tiles need no clamping.
-  __amdgpu_buffer_rsrc_t krs, vrs, prs;
+  i32x4 krs, vrs, prs;
   // per-lane offsets (loop invariant)
   int k_ld_off;      // byte offset in a K tile of this lane's first load (+4 KiB per instruction)
   int v_ld_off;      // ditto for V
@@ -122,10 +155,8 @@ struct Step {
   f32x16 o[4];
   float m2 = -INFINITY, lsum = 0.f;
   int cnt_full = 0, cnt_masked = 0;
-  f32x16 sc[2];        // scores of the current own tile, overwritten by the next
-  bf16x8 pp[2][2];      // probabilities of the previous own tile, then the current
-  bool need_rescale = false;
-  float alpha_pending = 1.f;
+  f32x16 sc[2];        // scores of one own tile (S^T, two 32-key halves)
+  bf16x8 pp[2][2];      // its probabilities, bf16
 
   __device__ Step(const StepArgs& a_, Smem& sm_, int tid_)
       : a(a_), sm(sm_), tid(tid_), lane(tid_ & 63),
@@ -162,24 +193,49 @@ struct Step {
   }
 
   // ---- tile staging (direct to LDS) --------------------------------------
+  // Own tile i of this group (global key tile 2i + grp) lives in K stage
+  // i & 1, V stage i & 1 and position stage i % 3.  The softmax phase of own
+  // tile s issues one batch -- K and positions of own tile s+2, V of own tile
+  // s+1 -- and waits, at its end, for the batch of the previous softmax
+  // phase, which the GEMM phase right after it reads.  Every load is an
+  // untracked DMA (dma_to_lds), so these explicit waits are the only ones.
   __device__ __forceinline__ void load_k_tile(int j, int stage) {
     uint8_t* dst = sm.k[grp][stage];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(dst + (gwave + 4 * i) * 1024), 16,
-                                               k_ld_off, j * BN * 256 + i * 4096, 0, 0);
+      dma_to_lds(krs, dst + (gwave + 4 * i) * 1024, k_ld_off, j * BN * 256 + i * 4096);
   }
   __device__ __forceinline__ void load_v_tile(int j, int stage) {
     uint8_t* dst = sm.v[grp][stage];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(dst + (gwave + 4 * i) * 1024), 16,
-                                               v_ld_off, j * BN * 256 + i * 4096, 0, 0);
+      dma_to_lds(vrs, dst + (gwave + 4 * i) * 1024, v_ld_off, j * BN * 256 + i * 4096);
   }
-  __device__ __forceinline__ int fetch_pos(int j) const {
-    const int gk = j * BN + (tid & 63);
-    const int p = __builtin_amdgcn_raw_buffer_load_b32(prs, (tid & 63) * 4, j * BN * 4, 0);
-    return gk < n_k ? (causal ? p : kPosAlways) : kPosHidden;
+  // All four waves of the group write the same 256 bytes (identical data),
+  // which keeps every wave's count of outstanding loads the same.
+  __device__ __forceinline__ void load_pos(int j, int stage) {
+    dma4_to_lds(prs, sm.pos[grp][stage], lane * 4, j * BN * 4);
+  }
+  // Issues the batch of the softmax phase of own tile s; returns how many
+  // DMA instructions this wave issued (9, 4 or 0).
+  __device__ __forceinline__ int issue_batch(int s) {
+    if (s + 2 < n_own) {
+      load_k_tile(2 * (s + 2) + grp, s & 1);
+      load_pos(2 * (s + 2) + grp, (s + 2) % 3);
+      load_v_tile(2 * (s + 1) + grp, (s + 1) & 1);
+      return 9;
+    }
+    if (s + 1 < n_own) {
+      load_v_tile(2 * (s + 1) + grp, (s + 1) & 1);
+      return 4;
+    }
+    return 0;
+  }
+  // Waits until at most n of this wave's DMA loads are outstanding.
+  __device__ __forceinline__ static void wait_loads(int n) {
+    if (n == 9) __builtin_amdgcn_s_waitcnt(0x0f79);       // vmcnt(9)
+    else if (n == 4) __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
+    else __builtin_amdgcn_s_waitcnt(0x0f70);              // vmcnt(0)
   }
 
   // ---- MFMA pieces --------------------------------------------------------
@@ -209,15 +265,22 @@ struct Step {
       }
   }
 
-  // Masks hidden keys of one 32-key half to -inf.  Accumulator register r of
-  // half kb holds tile key 32kb + 8h + 16(r/8) + r%8.
-  __device__ __forceinline__ void mask(f32x16& s, const int32_t* pos, int kb, int qpe) const {
+  // Masks keys of one 32-key half to -inf: those after the query (position
+  // above qpe) and those past the block's end (tile index >= nvalid, whose
+  // loaded positions read as zero).  Accumulator register r of half kb holds
+  // tile key 32kb + 8h + 16(r/8) + r%8.
+  __device__ __forceinline__ void mask(f32x16& s, const int32_t* pos, int kb, int qpe,
+                                       int nvalid) const {
     i32x4 kp4[4];
 #pragma unroll
     for (int x = 0; x < 4; ++x)
       kp4[x] = *(const i32x4*)&pos[32 * kb + 8 * h + 16 * (x >> 1) + 4 * (x & 1)];
+    const int kbase_idx = 32 * kb + 8 * h;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = (kp4[r >> 2][r & 3] <= qpe) ? s[r] : -INFINITY;
+    for (int r = 0; r < 16; ++r) {
+      const bool vis = kp4[r >> 2][r & 3] <= qpe && kbase_idx + 16 * (r >> 3) + (r & 7) < nvalid;
+      s[r] = vis ? s[r] : -INFINITY;
+    }
   }
 
   __device__ __forceinline__ void exp_pack(const f32x16& s, float muse, bf16x8 (&p)[2]) {
@@ -236,73 +299,66 @@ struct Step {
     lsum += acc0 + acc1;
   }
 
-  __device__ __forceinline__ void apply_pending_rescale() {
-    if (need_rescale) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha_pending;
-    }
+  // Workgroup barrier that also stops the compiler from moving any
+  // instruction across it, so each phase keeps its own work.
+  __device__ __forceinline__ static void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // One own tile i (global tile j = 2i + grp).  HAS_PREV: PV of own tile
-  // i-1 is pending; HAS_NEXT: own tile i+1 exists.  The four phases below let
-  // every VALU step run beside MFMAs that do not depend on it, reusing the
-  // score and probability registers in place:
-  //   A: PV(i-1, keys 0-31)         | row max of tile i
-  //   B: PV(i-1, keys 32-63)        | P(i, keys 0-31)  (overwrites pp[0])
-  //   C: QK(i+1, keys 0-31) -> sc[0] | P(i, keys 32-63) (overwrites pp[1])
-  //   D: QK(i+1, keys 32-63) -> sc[1]
-  template <bool HAS_PREV, bool HAS_NEXT>
-  __device__ __forceinline__ void iteration(int i) {
-    apply_pending_rescale();
-    const int j = 2 * i + grp;
-    // Stage K of own tile i+2 (clamped to the last own tile: a repeat lands
-    // in a stage nobody reads) and V of own tile i.
-    const int i2 = min(i + 2, n_own - 1);
-    load_k_tile(2 * i2 + grp, i & 1);
-    load_v_tile(j, i & 1);
-    const int next_pos = fetch_pos(2 * i2 + grp);
-
-    const int32_t* pos = sm.pos[grp][i % 3];
-    const int j0 = j * BN;
-    const int last_valid = min(j0 + BN, n_k) - 1 - j0;
-    const int kmin = pos[0], kmax = pos[last_valid];
-    const bool ragged = j0 + BN > n_k;
+  // ---- the two phases -----------------------------------------------------
+  // Softmax of own tile s: classify the tile, mask, fold its row maximum into
+  // the running maximum (rescaling O and l only when some row's maximum
+  // rose), and turn the scores into bf16 probabilities.
+  __device__ __forceinline__ void sm_phase(int s) {
+    const int nb = issue_batch(s);
+    const int j0 = (2 * s + grp) * BN;
+    const int32_t* pos = sm.pos[grp][s % 3];
+    const int nvalid = min(BN, n_k - j0);
+    const int kmin = __builtin_amdgcn_readfirstlane(pos[0]);
+    const int kmax = __builtin_amdgcn_readfirstlane(pos[nvalid - 1]);
     const bool skip = !wave_valid || kmin > qmax_w;
     const bool full = kmax <= qmin_w;
     if (!skip) {
       if (full) ++cnt_full; else ++cnt_masked;
     }
-    if (skip || !full || ragged) {
+    if (skip || !full || nvalid < BN) {
       const int qpe = skip ? kPosRowNone : qp;
-      mask(sc[0], pos, 0, qpe);
-      mask(sc[1], pos, 1, qpe);
+      mask(sc[0], pos, 0, qpe, nvalid);
+      mask(sc[1], pos, 1, qpe, nvalid);
     }
-
-    // A
-    if (HAS_PREV) pv((i - 1) & 1, 0, pp[0]);
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[0][r], sc[1][r]));
     const float mloc = half_swap_max(mx) * c2;
-    need_rescale = __ballot(mloc > m2) != 0;
-    const float mnew = fmaxf(m2, mloc);
-    alpha_pending = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mnew);
-    m2 = mnew;
+    if (__ballot(mloc > m2) != 0) {
+      const float mnew = fmaxf(m2, mloc);
+      const float alpha = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mnew);
+      m2 = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= alpha;
+    }
     const float muse = (m2 == -INFINITY) ? 0.f : m2;
-    lsum *= alpha_pending;
-    // B
-    if (HAS_PREV) pv((i - 1) & 1, 1, pp[1]);
     exp_pack(sc[0], muse, pp[0]);
-    // C
-    if (HAS_NEXT) sc[0] = qk((i + 1) & 1, 0);
     exp_pack(sc[1], muse, pp[1]);
-    // D
-    if (HAS_NEXT) sc[1] = qk((i + 1) & 1, 1);
+    wait_loads(nb);
+  }
 
-    sm.pos[grp][(i + 2) % 3][tid & 63] = next_pos;
-    // this wave's LDS loads must land before the barrier publishes them
-    __builtin_amdgcn_s_waitcnt(0x0f70 /* vmcnt(0) */);
-    __syncthreads();
+  // GEMM phase after the softmax of own tile s: O += P(s) V(s) and the
+  // scores of own tile s+1 (S^T = K Q^T).  s = -1 computes only the scores
+  // of own tile 0; the last phase only PV.
+  template <bool PV, bool QK>
+  __device__ __forceinline__ void gemm_phase(int s) {
+    if (QK) {
+      sc[0] = qk((s + 1) & 1, 0);
+      sc[1] = qk((s + 1) & 1, 1);
+    }
+    if (PV) {
+      pv(s & 1, 0, pp[0]);
+      pv(s & 1, 1, pp[1]);
+    }
   }
 
   __device__ void run(int qt, int head) {
@@ -315,7 +371,7 @@ struct Step {
       const int qmax_wg = a.q_pos[min(row0_wg + ROWS, n_q) - 1];
       int cnt = 0;
       for (int j = lane; j < n_kt; j += 64) cnt += (a.k_pos[j * BN] <= qmax_wg) ? 1 : 0;
-      n_iter = wave_sum_i(cnt);
+      n_iter = __builtin_amdgcn_readfirstlane(wave_sum_i(cnt));
     }
     wave_valid = row0 < n_q;
     const bool count = a.work != nullptr && head == 0 && wave_valid;
@@ -330,8 +386,8 @@ struct Step {
     if (!wave_valid) {
       qmin_w = qmax_w = kPosRowNone;
     } else if (causal) {
-      qmin_w = a.q_pos[row0];
-      qmax_w = a.q_pos[min(row0 + WAVE_ROWS, n_q) - 1];
+      qmin_w = __builtin_amdgcn_readfirstlane(a.q_pos[row0]);
+      qmax_w = __builtin_amdgcn_readfirstlane(a.q_pos[min(row0 + WAVE_ROWS, n_q) - 1]);
     } else {
       qmin_w = qmax_w = kPosRowAll;
     }
@@ -339,9 +395,9 @@ struct Step {
     qp = row < n_q ? (causal ? a.q_pos[row] : kPosRowAll) : kPosRowNone;
     kbase = (const uint16_t*)a.k + ((size_t)kvh * n_k) * D;
     vbase = (const uint16_t*)a.v + ((size_t)kvh * n_k) * D;
-    krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, n_k * D * 2, kBufferFlags);
-    vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, n_k * D * 2, kBufferFlags);
-    prs = __builtin_amdgcn_make_buffer_rsrc((void*)a.k_pos, (short)0, n_k * 4, kBufferFlags);
+    krs = buffer_rsrc(kbase, n_k * D * 2);
+    vrs = buffer_rsrc(vbase, n_k * D * 2);
+    prs = buffer_rsrc(a.k_pos, n_k * 4);
     {
       const uint16_t* qb = (const uint16_t*)a.q + ((size_t)head * n_q) * D;
 #pragma unroll
@@ -377,44 +433,43 @@ struct Step {
     const float m2_0 = m2;
     c2 = a.c2;
     cnt_full = cnt_masked = 0;
-    need_rescale = false;
 
-    const int n_super = (n_iter + 1) / 2;
-    if (n_super > 0) {
-      // Prologue: K of own tiles 0 and 1 and their positions, then S^T of
-      // own tile 0.  Both groups run every barrier.
+    // Ping-pong schedule.  Each group alternates softmax phases (VALU) and
+    // GEMM phases (MFMA) on its own tiles, one workgroup barrier after each
+    // phase.  Group 1 starts one phase later, so on every SIMD one wave feeds
+    // the matrix pipe while the other runs the softmax, and each barrier
+    // swaps their roles.  Group g passes g + 1 + 2 n_own barriers after the
+    // prologue and pads to the larger count of the two.
+    if (n_iter > 0) {
       if (n_own > 0) {
         load_k_tile(grp, 0);
-        sm.pos[grp][0][tid & 63] = fetch_pos(grp);
+        load_pos(grp, 0);
+        load_v_tile(grp, 0);
       }
       if (n_own > 1) {
         load_k_tile(2 + grp, 1);
-        sm.pos[grp][1][tid & 63] = fetch_pos(2 + grp);
+        load_pos(2 + grp, 1);
       }
-      __builtin_amdgcn_s_waitcnt(0x0f70 & 0xffff);
-      __syncthreads();
-      if (n_own > 0) {
-        sc[0] = qk(0, 0);
-        sc[1] = qk(0, 1);
-      }
-      __syncthreads();  // K stage 0 is refilled in own iteration 0
-
-      for (int si = 0; si < n_super; ++si) {
-        if (si >= 1 && si + 1 < n_own) {
-          iteration<true, true>(si);
-        } else if (si < n_own) {
-          if (si == 0 && n_own > 1) iteration<false, true>(si);
-          else if (si == 0) iteration<false, false>(si);
-          else iteration<true, false>(si);
-        } else {
-          __syncthreads();  // this group has no tile in this round
-        }
+      wait_loads(0);
+      phase_barrier();
+      if (grp == 1) phase_barrier();
+      if (n_own > 0) gemm_phase<false, true>(-1);
+      phase_barrier();
+      for (int s = 0; s + 1 < n_own; ++s) {
+        sm_phase(s);
+        phase_barrier();
+        gemm_phase<true, true>(s);
+        phase_barrier();
       }
       if (n_own > 0) {
-        apply_pending_rescale();
-        pv((n_own - 1) & 1, 0, pp[0]);
-        pv((n_own - 1) & 1, 1, pp[1]);
+        sm_phase(n_own - 1);
+        phase_barrier();
+        gemm_phase<true, false>(n_own - 1);
+        phase_barrier();
       }
+      const int n0 = (n_iter + 1) / 2, n1 = n_iter / 2;
+      const int n_bar = max(2 * n0 + 1, 2 * n1 + 2);
+      for (int b = grp + 1 + 2 * n_own; b < n_bar; ++b) phase_barrier();
     }
 
     if (count && lane == 0) {
