@@ -32,6 +32,7 @@
 //    explicit vmcnt counts; K and V tiles have two stages per group,
 //    positions three.
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "ra_internal.h"
@@ -99,24 +100,32 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int bytes) {
                __builtin_amdgcn_readfirstlane(bytes), kBufferFlags};
 }
 
-// One 16-byte-per-lane buffer load from HBM straight into LDS: lane L's 16
-// bytes land at lds + 16 L.  Bytes at or past the resource size read as zero.
-// Issued as inline asm so the compiler does not track it: it cannot tell that
-// the stage being filled is not the one being read, and would otherwise wait
-// for the load before the very next LDS read.  Callers wait (vmcnt(0)) before
-// the barrier that publishes the stage.  M0 carries the LDS address; the nop
-// is the required wait state between writing M0 and the LDS-DMA that reads it.
-__device__ __forceinline__ void dma_to_lds(const i32x4& rsrc, const void* lds, int voff, int soff) {
-  const int m0v = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void*)lds);
+// Four 16-byte-per-lane buffer loads from HBM straight into LDS (4 KiB):
+// load i of lane L reads global byte soff + 1024 i + voff_i and lands at LDS
+// byte lds + 1024 i + 16 L (the instruction offset moves both addresses).
+// Bytes at or past the resource size read as zero.  Issued as inline asm so
+// the compiler does not track them: it cannot tell that the stage being
+// filled is not the one being read, and would otherwise wait for the load
+// before the very next LDS read.  Callers wait (vmcnt) before the barrier
+// that publishes the stage.  M0 carries the LDS address; the nop is the
+// required wait state between writing M0 and the LDS-DMA that reads it.
+__device__ __forceinline__ void dma_tile_to_lds(const i32x4& rsrc, uint32_t lds, int v0, int v1,
+                                                int v2, int v3, int soff) {
+  const int m0v = __builtin_amdgcn_readfirstlane((int)lds);
   const int so = __builtin_amdgcn_readfirstlane(soff);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(m0v), "v"(voff), "s"(rsrc), "s"(so)
-               : "m0");
+  asm volatile(
+      "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %5, %6 offen lds\n\t"
+      "buffer_load_dwordx4 %2, %5, %6 offen offset:1024 lds\n\t"
+      "buffer_load_dwordx4 %3, %5, %6 offen offset:2048 lds\n\t"
+      "buffer_load_dwordx4 %4, %5, %6 offen offset:3072 lds"
+      :
+      : "s"(m0v), "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(rsrc), "s"(so)
+      : "m0");
 }
-// Same for 4 bytes per lane (lane L's word lands at lds + 4 L).
-__device__ __forceinline__ void dma4_to_lds(const i32x4& rsrc, const void* lds, int voff, int soff) {
-  const int m0v = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void*)lds);
+// One 4-byte-per-lane load into LDS (lane L's word lands at lds + 4 L).
+__device__ __forceinline__ void dma_words_to_lds(const i32x4& rsrc, uint32_t lds, int voff, int soff) {
+  const int m0v = __builtin_amdgcn_readfirstlane((int)lds);
   const int so = __builtin_amdgcn_readfirstlane(soff);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                :
@@ -146,8 +155,9 @@ struct Step {
   // block's end return zeros, so ragged tiles need no clamping.
   i32x4 krs, vrs, prs;
   // per-lane offsets (loop invariant)
-  int k_ld_off;      // byte offset in a K tile of this lane's first load (+4 KiB per instruction)
-  int v_ld_off;      // ditto for V
+  uint32_t lds_k, lds_v, lds_pos;  // LDS byte addresses of this group's stages
+  int k_ld_off[4];   // byte offset in a K tile of this lane's load i (relative to 1024 i)
+  int v_ld_off;      // ditto for V (the same for every i)
   int k_rd;          // K read base, XOR'ed with 32*ks
   int v_rd;          // V read base, XOR'ed with 64*db
 
@@ -155,6 +165,9 @@ struct Step {
   f32x16 o[4];
   float m2 = -INFINITY, lsum = 0.f;
   int cnt_full = 0, cnt_masked = 0;
+  int n_full_w = 0, n_vis_w = 0;  // key tiles this wave sees fully / at all
+  bool resc = false;   // O must be scaled by alpha before the next PV
+  float alpha = 1.f;
   f32x16 sc[2];        // scores of one own tile (S^T, two 32-key halves)
   bf16x8 pp[2][2];      // its probabilities, bf16
 
@@ -163,17 +176,21 @@ struct Step {
         gwave(__builtin_amdgcn_readfirstlane((tid_ >> 6) & 3)),
         grp(__builtin_amdgcn_readfirstlane(tid_ >> 8)), h((tid_ & 63) >> 5), col(tid_ & 31),
         n_q(a_.n_q), n_k(a_.n_k), causal(a_.causal != 0), kbase(nullptr), vbase(nullptr) {
-    // Tile loads: instruction i of this wave fills LDS rows 4b..4b+3 with
-    // b = gwave + 4i (rows 4*gwave + 16i + L/16 for lane L), so row & 15 and
-    // hence each lane's swizzle is the same for all four instructions, which
-    // then differ only by a scalar 4 KiB offset.  Lane L writes physical
-    // chunk L%16, holding logical chunk (L%16) ^ (row & 15) for K and
-    // (L%16) ^ 4(row & 3) for V.
+    // Tile loads: wave w fills rows 16w .. 16w+15 of a tile, load i rows
+    // 16w + 4i + L/16 for lane L, which writes physical chunk L%16 of its
+    // row: logical chunk (L%16) ^ (row & 15) for K, (L%16) ^ 4(row & 3) for V.
     {
       const int L = lane;
-      const int r = 4 * gwave + L / 16;
-      k_ld_off = r * 256 + 16 * ((L % 16) ^ (r & 15));
-      v_ld_off = r * 256 + 16 * ((L % 16) ^ (4 * (r & 3)));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + L / 16;  // row within the wave's 16 (same & 15)
+        k_ld_off[i] = (L / 16) * 256 + 16 * ((L % 16) ^ (r & 15));
+      }
+      v_ld_off = (L / 16) * 256 + 16 * ((L % 16) ^ (4 * ((L / 16) & 3)));
+      const uint32_t base = (uint32_t)(uintptr_t)(lds_void*)&sm_;
+      lds_k = base + (uint32_t)offsetof(Smem, k) + grp * 2 * TILE_BYTES;
+      lds_v = base + (uint32_t)offsetof(Smem, v) + grp * 2 * TILE_BYTES;
+      lds_pos = base + (uint32_t)offsetof(Smem, pos) + grp * 3 * BN * 4;
     }
     // K reads: row sigma(col) (+32 kb), logical chunk 2ks + h.
     {
@@ -198,38 +215,19 @@ struct Step {
   // tile s issues one batch -- K and positions of own tile s+2, V of own tile
   // s+1 -- and waits, at its end, for the batch of the previous softmax
   // phase, which the GEMM phase right after it reads.  Every load is an
-  // untracked DMA (dma_to_lds), so these explicit waits are the only ones.
+  // untracked DMA (dma_tile_to_lds), so these explicit waits are the only ones.
   __device__ __forceinline__ void load_k_tile(int j, int stage) {
-    uint8_t* dst = sm.k[grp][stage];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      dma_to_lds(krs, dst + (gwave + 4 * i) * 1024, k_ld_off, j * BN * 256 + i * 4096);
+    dma_tile_to_lds(krs, lds_k + stage * TILE_BYTES + 4096 * gwave, k_ld_off[0], k_ld_off[1],
+                    k_ld_off[2], k_ld_off[3], j * BN * 256 + 4096 * gwave);
   }
   __device__ __forceinline__ void load_v_tile(int j, int stage) {
-    uint8_t* dst = sm.v[grp][stage];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      dma_to_lds(vrs, dst + (gwave + 4 * i) * 1024, v_ld_off, j * BN * 256 + i * 4096);
+    dma_tile_to_lds(vrs, lds_v + stage * TILE_BYTES + 4096 * gwave, v_ld_off, v_ld_off, v_ld_off,
+                    v_ld_off, j * BN * 256 + 4096 * gwave);
   }
   // All four waves of the group write the same 256 bytes (identical data),
   // which keeps every wave's count of outstanding loads the same.
   __device__ __forceinline__ void load_pos(int j, int stage) {
-    dma4_to_lds(prs, sm.pos[grp][stage], lane * 4, j * BN * 4);
-  }
-  // Issues the batch of the softmax phase of own tile s; returns how many
-  // DMA instructions this wave issued (9, 4 or 0).
-  __device__ __forceinline__ int issue_batch(int s) {
-    if (s + 2 < n_own) {
-      load_k_tile(2 * (s + 2) + grp, s & 1);
-      load_pos(2 * (s + 2) + grp, (s + 2) % 3);
-      load_v_tile(2 * (s + 1) + grp, (s + 1) & 1);
-      return 9;
-    }
-    if (s + 1 < n_own) {
-      load_v_tile(2 * (s + 1) + grp, (s + 1) & 1);
-      return 4;
-    }
-    return 0;
+    dma_words_to_lds(prs, lds_pos + stage * BN * 4, lane * 4, j * BN * 4);
   }
   // Waits until at most n of this wave's DMA loads are outstanding.
   __device__ __forceinline__ static void wait_loads(int n) {
@@ -275,10 +273,12 @@ struct Step {
 #pragma unroll
     for (int x = 0; x < 4; ++x)
       kp4[x] = *(const i32x4*)&pos[32 * kb + 8 * h + 16 * (x >> 1) + 4 * (x & 1)];
-    const int kbase_idx = 32 * kb + 8 * h;
+    // key index 32kb + 8h + c_r < nvalid  <=>  8h < nvalid - 32kb - c_r
+    const int h8 = 8 * h;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const bool vis = kp4[r >> 2][r & 3] <= qpe && kbase_idx + 16 * (r >> 3) + (r & 7) < nvalid;
+      const int lim = nvalid - 32 * kb - (16 * (r >> 3) + (r & 7));
+      const bool vis = kp4[r >> 2][r & 3] <= qpe && h8 < lim;
       s[r] = vis ? s[r] : -INFINITY;
     }
   }
@@ -299,6 +299,23 @@ struct Step {
     lsum += acc0 + acc1;
   }
 
+  // Empty asm statements that make the phase's results exist at this point:
+  // without them the compiler sinks pure arithmetic (exponentials, MFMAs)
+  // into the next phase, next to its first use, and the phases blur.
+  __device__ __forceinline__ void pin_softmax() {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) asm volatile("" : "+v"(pp[t][u]));
+    asm volatile("" : "+v"(lsum), "+v"(m2), "+v"(alpha));
+  }
+  __device__ __forceinline__ void pin_gemm() {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(sc[kb]));
+#pragma unroll
+    for (int db = 0; db < 4; ++db) asm volatile("" : "+v"(o[db]));
+  }
+
   // Workgroup barrier that also stops the compiler from moving any
   // instruction across it, so each phase keeps its own work.
   __device__ __forceinline__ static void phase_barrier() {
@@ -312,43 +329,61 @@ struct Step {
   // the running maximum (rescaling O and l only when some row's maximum
   // rose), and turn the scores into bf16 probabilities.
   __device__ __forceinline__ void sm_phase(int s) {
-    const int nb = issue_batch(s);
-    const int j0 = (2 * s + grp) * BN;
-    const int32_t* pos = sm.pos[grp][s % 3];
-    const int nvalid = min(BN, n_k - j0);
-    const int kmin = __builtin_amdgcn_readfirstlane(pos[0]);
-    const int kmax = __builtin_amdgcn_readfirstlane(pos[nvalid - 1]);
-    const bool skip = !wave_valid || kmin > qmax_w;
-    const bool full = kmax <= qmin_w;
+    // The batch's DMA instructions are spread over the phase: a wave that
+    // issues them back to back stalls on the CU's load path (64 B/clk).
+    const bool has_k = s + 2 < n_own, has_v = s + 1 < n_own;
+    if (has_k) load_k_tile(2 * (s + 2) + grp, s & 1);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const int j = 2 * s + grp;
+    const int nvalid = min(BN, n_k - j * BN);
+    const bool skip = j >= n_vis_w;
+    const bool full = j < n_full_w;
     if (!skip) {
       if (full) ++cnt_full; else ++cnt_masked;
     }
-    if (skip || !full || nvalid < BN) {
-      const int qpe = skip ? kPosRowNone : qp;
-      mask(sc[0], pos, 0, qpe, nvalid);
-      mask(sc[1], pos, 1, qpe, nvalid);
-    }
-    float mx = -INFINITY;
+    if (skip) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sc[0][r], sc[1][r]));
+      for (int r = 0; r < 16; ++r) sc[0][r] = sc[1][r] = -INFINITY;
+    } else if (!full || nvalid < BN) {
+      const int32_t* pos = sm.pos[grp][s % 3];
+      mask(sc[0], pos, 0, qp, nvalid);
+      mask(sc[1], pos, 1, qp, nvalid);
+    }
+    float mx4[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) mx4[x] = fmaxf(sc[0][x], sc[1][x]);
+#pragma unroll
+    for (int r = 4; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], fmaxf(sc[0][r], sc[1][r]));
+    const float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
     const float mloc = half_swap_max(mx) * c2;
-    if (__ballot(mloc > m2) != 0) {
+    // O is rescaled in the next GEMM phase, where the VALU is otherwise idle.
+    resc = __ballot(mloc > m2) != 0;
+    if (resc) {
       const float mnew = fmaxf(m2, mloc);
-      const float alpha = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mnew);
+      alpha = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mnew);
       m2 = mnew;
       lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= alpha;
     }
     const float muse = (m2 == -INFINITY) ? 0.f : m2;
+    __builtin_amdgcn_sched_barrier(0);
+    if (has_v) load_v_tile(2 * (s + 1) + grp, (s + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
     exp_pack(sc[0], muse, pp[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (has_k) load_pos(2 * (s + 2) + grp, (s + 2) % 3);
+    __builtin_amdgcn_sched_barrier(0);
     exp_pack(sc[1], muse, pp[1]);
-    wait_loads(nb);
+    pin_softmax();
+    wait_loads(has_k ? 9 : has_v ? 4 : 0);
   }
 
   // GEMM phase after the softmax of own tile s: O += P(s) V(s) and the
   // scores of own tile s+1 (S^T = K Q^T).  s = -1 computes only the scores
   // of own tile 0; the last phase only PV.
+  // GEMM phase after the softmax of own tile s: the scores of own tile s+1
+  // (S^T = K Q^T) and O += P(s) V(s).  s = -1 computes only the scores of
+  // own tile 0; the last phase only PV.
   template <bool PV, bool QK>
   __device__ __forceinline__ void gemm_phase(int s) {
     if (QK) {
@@ -356,9 +391,14 @@ struct Step {
       sc[1] = qk((s + 1) & 1, 1);
     }
     if (PV) {
+      if (resc) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] *= alpha;
+      }
       pv(s & 1, 0, pp[0]);
       pv(s & 1, 1, pp[1]);
     }
+    pin_gemm();
   }
 
   __device__ void run(int qt, int head) {
@@ -390,6 +430,22 @@ struct Step {
       qmax_w = __builtin_amdgcn_readfirstlane(a.q_pos[min(row0 + WAVE_ROWS, n_q) - 1]);
     } else {
       qmin_w = qmax_w = kPosRowAll;
+    }
+    // Positions increase, so the key tiles this wave sees completely form a
+    // prefix of the block (n_full_w tiles), and so do those it sees at all
+    // (n_vis_w); every other tile is skipped.
+    if (!wave_valid) {
+      n_full_w = n_vis_w = 0;
+    } else if (!causal) {
+      n_full_w = n_vis_w = n_kt;
+    } else {
+      int cf = 0, cv = 0;
+      for (int j = lane; j < n_kt; j += 64) {
+        cf += a.k_pos[min(j * BN + BN, n_k) - 1] <= qmin_w ? 1 : 0;
+        cv += a.k_pos[j * BN] <= qmax_w ? 1 : 0;
+      }
+      n_full_w = __builtin_amdgcn_readfirstlane(wave_sum_i(cf));
+      n_vis_w = __builtin_amdgcn_readfirstlane(wave_sum_i(cv));
     }
     const int row = row0 + col;
     qp = row < n_q ? (causal ? a.q_pos[row] : kPosRowAll) : kPosRowNone;
@@ -433,6 +489,7 @@ struct Step {
     const float m2_0 = m2;
     c2 = a.c2;
     cnt_full = cnt_masked = 0;
+    resc = false;
 
     // Ping-pong schedule.  Each group alternates softmax phases (VALU) and
     // GEMM phases (MFMA) on its own tiles, one workgroup barrier after each
