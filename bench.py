@@ -13,8 +13,10 @@ n_cp=16 zigzag, 16 query heads and 1 key/value head of width 128, bf16, rank 0
 """
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -31,6 +33,47 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_F32_TFLOPS = 157.3
 HBM_GBPS = 8000.0
 METRIC = "causal attention TFLOP/s per rank-share and % of bf16 MFMA peak (1 GPU)"
+
+
+KERNEL_SOURCE = os.path.join(ROOT, "ring_attention_rank_amd", "csrc", "ra_fast.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_step_kernel_fast_llama405b_stage_share.md")
+
+
+def kernel_source_sha256():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def committed_traffic(workload):
+    """HBM bytes per step launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (calibrated on a plain copy), or None when there is no summary for this
+    workload or the kernel source changed since it was taken."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    fields = dict(re.findall(r"^- ([a-z_0-9]+): (\S+)$", text, re.M))
+    if fields.get("workload") != workload or fields.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib, reps):
+    """A plain device-to-device copy of known size, to scale the FETCH_SIZE and
+    WRITE_SIZE counters (run under rocprofv3 --pmc)."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "reps": reps}), flush=True)
 
 
 def visible_pairs(q_pos, k_pos):
@@ -104,6 +147,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-side-stream", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -113,6 +158,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 5)
+        return
 
     case = synth.case_by_name(args.config)
     ranks = case.ranks if args.rank is None else (args.rank,)
@@ -183,8 +232,9 @@ def main():
         "per_rank": per_rank,
         "roofline": {
             "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-            "frac": achieved / peak, "traffic": None,
-            "kernel": "step_kernel (bf16 MFMA 32x32x16)",
+            "frac": achieved / peak, "traffic": committed_traffic(case.name),
+            "kernel": ("step_kernel_fast (bf16 MFMA 32x32x16)" if case.dtype == "bf16" and case.d_k == 128
+                       else "step_kernel (generic)"),
             "avg_launch_ms": avg_launch_ms, "launches_per_step": n_launch,
             "event_median_ms_per_step": float(np.median(step_ms)),
         },
