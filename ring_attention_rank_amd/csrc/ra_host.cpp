@@ -278,8 +278,13 @@ ra_status ra_forward(const ra_problem* p, int32_t n_cp, const void* q, const int
              ev_start = nullptr;
   ra_status result = RA_OK;
   int64_t staged = 0;
+  // The events only order work between two streams of this device; the copy
+  // kernels' completion and the step kernels' launch carry their own memory
+  // fences, so the events skip the system-scope fence (a cache writeback and
+  // invalidate that cost several microseconds between steps).
   auto mk = [](hipEvent_t* e) {
-    return hipEventCreateWithFlags(e, hipEventDisableTiming) == hipSuccess;
+    return hipEventCreateWithFlags(e, hipEventDisableTiming | hipEventDisableSystemFence) ==
+           hipSuccess;
   };
   if (use_side && n_cp > 1) {
     if (!mk(&ev_start) || !mk(&ev_staged[0]) || !mk(&ev_staged[1]) || !mk(&ev_used[0]) ||
