@@ -406,14 +406,37 @@ struct Step {
     const int row0_wg = qt * ROWS;
     const int row0 = row0_wg + gwave * WAVE_ROWS;
     const int n_kt = (n_k + BN - 1) / BN;
+    wave_valid = row0 < n_q;
+    // Tile classes from one pass over the key positions (all loads issued
+    // together).  Positions increase, so the key tiles the workgroup sees
+    // form a prefix of the block (n_iter tiles), and so do the tiles this
+    // wave sees completely (n_full_w) and at all (n_vis_w).
     n_iter = n_kt;
+    if (!wave_valid) {
+      qmin_w = qmax_w = kPosRowNone;
+    } else if (!causal) {
+      qmin_w = qmax_w = kPosRowAll;
+    }
     if (causal) {
       const int qmax_wg = a.q_pos[min(row0_wg + ROWS, n_q) - 1];
-      int cnt = 0;
-      for (int j = lane; j < n_kt; j += 64) cnt += (a.k_pos[j * BN] <= qmax_wg) ? 1 : 0;
-      n_iter = __builtin_amdgcn_readfirstlane(wave_sum_i(cnt));
+      if (wave_valid) {
+        qmin_w = __builtin_amdgcn_readfirstlane(a.q_pos[row0]);
+        qmax_w = __builtin_amdgcn_readfirstlane(a.q_pos[min(row0 + WAVE_ROWS, n_q) - 1]);
+      }
+      int ci = 0, cf = 0, cv = 0;
+      for (int j = lane; j < n_kt; j += 64) {
+        const int kf = a.k_pos[j * BN];
+        const int kl = a.k_pos[min(j * BN + BN, n_k) - 1];
+        ci += kf <= qmax_wg ? 1 : 0;
+        cf += kl <= qmin_w ? 1 : 0;
+        cv += kf <= qmax_w ? 1 : 0;
+      }
+      n_iter = __builtin_amdgcn_readfirstlane(wave_sum_i(ci));
+      n_full_w = __builtin_amdgcn_readfirstlane(wave_sum_i(cf));
+      n_vis_w = __builtin_amdgcn_readfirstlane(wave_sum_i(cv));
+    } else {
+      n_full_w = n_vis_w = wave_valid ? n_kt : 0;
     }
-    wave_valid = row0 < n_q;
     const bool count = a.work != nullptr && head == 0 && wave_valid;
     // tiles of this group among all key tiles, and among the visited ones
     const int n_kt_g = (n_kt - grp + 1) / 2;
@@ -421,31 +444,6 @@ struct Step {
     if (READ && !FINAL && n_iter == 0) {
       if (count && lane == 0) atomicAdd(a.work + 2, (unsigned long long)n_kt_g);
       return;
-    }
-
-    if (!wave_valid) {
-      qmin_w = qmax_w = kPosRowNone;
-    } else if (causal) {
-      qmin_w = __builtin_amdgcn_readfirstlane(a.q_pos[row0]);
-      qmax_w = __builtin_amdgcn_readfirstlane(a.q_pos[min(row0 + WAVE_ROWS, n_q) - 1]);
-    } else {
-      qmin_w = qmax_w = kPosRowAll;
-    }
-    // Positions increase, so the key tiles this wave sees completely form a
-    // prefix of the block (n_full_w tiles), and so do those it sees at all
-    // (n_vis_w); every other tile is skipped.
-    if (!wave_valid) {
-      n_full_w = n_vis_w = 0;
-    } else if (!causal) {
-      n_full_w = n_vis_w = n_kt;
-    } else {
-      int cf = 0, cv = 0;
-      for (int j = lane; j < n_kt; j += 64) {
-        cf += a.k_pos[min(j * BN + BN, n_k) - 1] <= qmin_w ? 1 : 0;
-        cv += a.k_pos[j * BN] <= qmax_w ? 1 : 0;
-      }
-      n_full_w = __builtin_amdgcn_readfirstlane(wave_sum_i(cf));
-      n_vis_w = __builtin_amdgcn_readfirstlane(wave_sum_i(cv));
     }
     const int row = row0 + col;
     qp = row < n_q ? (causal ? a.q_pos[row] : kPosRowAll) : kPosRowNone;
