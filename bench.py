@@ -147,6 +147,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-side-stream", action="store_true")
+    ap.add_argument("--no-allgather", action="store_true",
+                    help="skip timing the all-gather form (every block resident, one launch)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -240,6 +242,25 @@ def main():
         },
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
+    if not args.no_allgather:
+        # The all-gather form of the same share: every block resident, one
+        # launch (bf16 d_k=128), the state in registers.  Context only; the
+        # headline value is the ring with side-stream staging above.
+        ag = ra.AllGather(share["gq"], share["gq_pos"], share["gk"], share["gv"], share["gk_pos"])
+        for _ in range(args.warmup):
+            ag()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            ag()
+        torch.cuda.synchronize()
+        ag_s = (time.perf_counter() - t0) / args.steps
+        result["allgather"] = {
+            "value": flops / ag_s / 1e12, "unit": "TFLOP/s", "ms_per_step": ag_s * 1e3,
+            "pct_of_bf16_peak": 100.0 * flops / ag_s / 1e12 / PEAK_BF16_TFLOPS,
+            "launches_per_step": 1 if case.dtype == "bf16" and case.d_k == 128 else case.n_cp,
+            "rank": ranks[-1],
+        }
     if not args.no_cpu_baseline and len(ranks) >= 1:
         out, lse = fwd.out, fwd.lse
         result["cpu_baseline"] = cpu_baseline(case, share, out, lse, args.cpu_rows)

@@ -126,6 +126,30 @@ ra_status ra_forward(const ra_problem* p, int32_t n_cp, const void* q, const int
                      float* out, float* lse, int64_t* work, int64_t* staged_bytes,
                      void* main_stream, void* side_stream);
 
+/* Bytes of device workspace ra_forward_allgather needs: 0 for bfloat16 with
+ * d_k = 128 (the state stays in registers), else the running state (m, l, o). */
+size_t ra_forward_allgather_workspace_bytes(const ra_problem* p);
+
+/*
+ * The rank share in its all-gather form (Zero to Frontier,
+ * "distributed/context-expert": section "Splitting the sequence, and the one
+ * layer that objects" gathers every key/value block before one attention pass
+ * over the local queries, and "What context parallelism communicates"
+ * contrasts it with the ring: same bytes, all moved first, full K and V
+ * held).  All n_cp blocks are resident: k_blocks, v_blocks, k_pos_blocks are
+ * HOST arrays of n_cp device pointers, 1 <= n_cp <= 64; the result does not
+ * depend on their order.  bfloat16 with d_k = 128 runs one launch that folds
+ * every block into a register-resident state and writes out/lse; other shapes
+ * run one step launch per block against the state kept in the workspace
+ * (ra_forward_allgather_workspace_bytes; workspace may be NULL when that is 0).
+ * out, lse and work as in ra_forward.  Asynchronous on stream.
+ */
+ra_status ra_forward_allgather(const ra_problem* p, int32_t n_cp, const void* q,
+                               const int32_t* q_pos, const void* const* k_blocks,
+                               const void* const* v_blocks, const int32_t* const* k_pos_blocks,
+                               void* workspace, size_t ws_bytes, float* out, float* lse,
+                               int64_t* work, void* stream);
+
 /* Query-tile rows (bm) and key-tile columns (bn) the tile counters use. */
 ra_status ra_tile_shape(const ra_problem* p, int32_t* bm, int32_t* bn);
 

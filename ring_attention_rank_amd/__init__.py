@@ -24,6 +24,7 @@ RA_BF16, RA_F32 = 0, 1
 
 SYMBOLS = (
     "ra_state_init", "ra_step", "ra_finalize", "ra_forward_workspace_bytes", "ra_forward",
+    "ra_forward_allgather_workspace_bytes", "ra_forward_allgather",
     "ra_tile_shape", "ra_status_string", "ra_abi_version",
 )
 
@@ -64,6 +65,10 @@ def lib():
     L.ra_forward.argtypes = [P, i32, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
                              ctypes.POINTER(vp), vp, ctypes.c_size_t, vp, vp, vp,
                              ctypes.POINTER(ctypes.c_int64), vp, vp]
+    L.ra_forward_allgather_workspace_bytes.argtypes = [P]
+    L.ra_forward_allgather_workspace_bytes.restype = ctypes.c_size_t
+    L.ra_forward_allgather.argtypes = [P, i32, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                       ctypes.POINTER(vp), vp, ctypes.c_size_t, vp, vp, vp, vp]
     L.ra_tile_shape.argtypes = [P, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.ra_status_string.argtypes = [i32]
     L.ra_status_string.restype = ctypes.c_char_p
@@ -212,6 +217,50 @@ class Forward:
             ctypes.c_void_p(side.cuda_stream) if side is not None else ctypes.c_void_p(0)),
             "ra_forward")
         return self.out, self.lse
+
+
+def allgather_workspace_bytes(p):
+    return int(lib().ra_forward_allgather_workspace_bytes(ctypes.byref(p)))
+
+
+class AllGather:
+    """A prepared ra_forward_allgather call (every key/value block resident)."""
+
+    def __init__(self, q, q_pos, k_blocks, v_blocks, k_pos_blocks, causal=True, scale=None,
+                 count_work=True):
+        _need_gpu(q, q_pos, *k_blocks, *v_blocks, *k_pos_blocks)
+        n_cp = len(k_blocks)
+        if not (n_cp == len(v_blocks) == len(k_pos_blocks)) or n_cp < 1:
+            raise ValueError("need n_cp >= 1 blocks of k, v and k_pos")
+        self.p = _problem_from(q, k_blocks[0], causal, scale)
+        self.n_cp = n_cp
+        dev = q.device
+        self.keep = (q, q_pos, list(k_blocks), list(v_blocks), list(k_pos_blocks))
+        arr = ctypes.c_void_p * n_cp
+        self.kp = arr(*[t.data_ptr() for t in k_blocks])
+        self.vp = arr(*[t.data_ptr() for t in v_blocks])
+        self.pp = arr(*[t.data_ptr() for t in k_pos_blocks])
+        nbytes = allgather_workspace_bytes(self.p)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+        self.out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
+        self.work = torch.zeros(3, dtype=torch.int64, device=dev) if count_work else None
+
+    def __call__(self, stream=None):
+        q, q_pos = self.keep[0], self.keep[1]
+        _check(lib().ra_forward_allgather(
+            ctypes.byref(self.p), self.n_cp, _ptr(q), _ptr(q_pos), self.kp, self.vp, self.pp,
+            _ptr(self.ws), ctypes.c_size_t(self.ws.numel() if self.ws is not None else 0),
+            _ptr(self.out), _ptr(self.lse), _ptr(self.work), _stream(stream)),
+            "ra_forward_allgather")
+        return self.out, self.lse
+
+
+def forward_allgather(q, q_pos, k_blocks, v_blocks, k_pos_blocks, causal=True, scale=None):
+    """The rank share with every block resident: returns (out, lse, work[3] tensor)."""
+    f = AllGather(q, q_pos, k_blocks, v_blocks, k_pos_blocks, causal, scale)
+    out, lse = f()
+    return out, lse, f.work
 
 
 def forward(q, q_pos, k_blocks, v_blocks, k_pos_blocks, causal=True, scale=None, side=True):

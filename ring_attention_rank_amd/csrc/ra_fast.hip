@@ -401,70 +401,73 @@ struct Step {
     pin_gemm();
   }
 
-  __device__ void run(int qt, int head) {
-    const int kvh = head / (a.h_q / a.h_kv);
+  // ---- one run: a query tile (128 rows of one head) against blocks --------
+  int row = 0, n_kt = 0, n_kt_g = 0, qmax_wg = 0;
+  size_t srow = 0;
+  float m_nat0 = -INFINITY, m2_0 = -INFINITY;
+  bool count = false;
+
+  // Query positions of the tile: the wave's first and last position and the
+  // workgroup's last (positions increase within the array).
+  __device__ __forceinline__ void positions(int qt, int head) {
     const int row0_wg = qt * ROWS;
     const int row0 = row0_wg + gwave * WAVE_ROWS;
-    const int n_kt = (n_k + BN - 1) / BN;
     wave_valid = row0 < n_q;
-    // Tile classes from one pass over the key positions (all loads issued
-    // together).  Positions increase, so the key tiles the workgroup sees
-    // form a prefix of the block (n_iter tiles), and so do the tiles this
-    // wave sees completely (n_full_w) and at all (n_vis_w).
-    n_iter = n_kt;
+    row = row0 + col;
     if (!wave_valid) {
       qmin_w = qmax_w = kPosRowNone;
     } else if (!causal) {
       qmin_w = qmax_w = kPosRowAll;
+    } else {
+      qmin_w = __builtin_amdgcn_readfirstlane(a.q_pos[row0]);
+      qmax_w = __builtin_amdgcn_readfirstlane(a.q_pos[min(row0 + WAVE_ROWS, n_q) - 1]);
     }
+    qmax_wg = causal ? a.q_pos[min(row0_wg + ROWS, n_q) - 1] : kPosRowAll;
+    qp = row < n_q ? (causal ? a.q_pos[row] : kPosRowAll) : kPosRowNone;
+    count = a.work != nullptr && head == 0 && wave_valid;
+    srow = (size_t)head * n_q + row;
+  }
+
+  // Tile classes of one key block from one pass over its positions.
+  // Positions increase, so the key tiles the workgroup sees form a prefix of
+  // the block (n_iter tiles), and so do the tiles this wave sees completely
+  // (n_full_w) and at all (n_vis_w).
+  __device__ __forceinline__ void classify(const int32_t* k_pos) {
+    n_kt = (n_k + BN - 1) / BN;
+    n_iter = n_kt;
     if (causal) {
-      const int qmax_wg = a.q_pos[min(row0_wg + ROWS, n_q) - 1];
-      if (wave_valid) {
-        qmin_w = __builtin_amdgcn_readfirstlane(a.q_pos[row0]);
-        qmax_w = __builtin_amdgcn_readfirstlane(a.q_pos[min(row0 + WAVE_ROWS, n_q) - 1]);
-      }
       int ci = 0, cf = 0, cv = 0;
       for (int j = lane; j < n_kt; j += 64) {
-        const int kf = a.k_pos[j * BN];
-        const int kl = a.k_pos[min(j * BN + BN, n_k) - 1];
+        const int kf = k_pos[j * BN];
+        const int kl = k_pos[min(j * BN + BN, n_k) - 1];
         ci += kf <= qmax_wg ? 1 : 0;
         cf += kl <= qmin_w ? 1 : 0;
         cv += kf <= qmax_w ? 1 : 0;
       }
       n_iter = __builtin_amdgcn_readfirstlane(wave_sum_i(ci));
-      n_full_w = __builtin_amdgcn_readfirstlane(wave_sum_i(cf));
-      n_vis_w = __builtin_amdgcn_readfirstlane(wave_sum_i(cv));
+      n_full_w = wave_valid ? __builtin_amdgcn_readfirstlane(wave_sum_i(cf)) : 0;
+      n_vis_w = wave_valid ? __builtin_amdgcn_readfirstlane(wave_sum_i(cv)) : 0;
     } else {
       n_full_w = n_vis_w = wave_valid ? n_kt : 0;
     }
-    const bool count = a.work != nullptr && head == 0 && wave_valid;
     // tiles of this group among all key tiles, and among the visited ones
-    const int n_kt_g = (n_kt - grp + 1) / 2;
+    n_kt_g = (n_kt - grp + 1) / 2;
     n_own = (n_iter - grp + 1) / 2;
-    if (READ && !FINAL && n_iter == 0) {
-      if (count && lane == 0) atomicAdd(a.work + 2, (unsigned long long)n_kt_g);
-      return;
-    }
-    const int row = row0 + col;
-    qp = row < n_q ? (causal ? a.q_pos[row] : kPosRowAll) : kPosRowNone;
-    kbase = (const uint16_t*)a.k + ((size_t)kvh * n_k) * D;
-    vbase = (const uint16_t*)a.v + ((size_t)kvh * n_k) * D;
-    krs = buffer_rsrc(kbase, n_k * D * 2);
-    vrs = buffer_rsrc(vbase, n_k * D * 2);
-    prs = buffer_rsrc(a.k_pos, n_k * 4);
+  }
+
+  // Q into registers and the incoming state (READ) or the empty one.
+  __device__ __forceinline__ void load_state(int head) {
     {
       const uint16_t* qb = (const uint16_t*)a.q + ((size_t)head * n_q) * D;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
         q[ks] = row < n_q ? *(const bf16x8*)(qb + (size_t)row * D + ks * 16 + h * 8) : bf16x8{};
     }
-
-    float m_nat0 = -INFINITY;
+    m_nat0 = -INFINITY;
     m2 = -INFINITY;
     lsum = 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db) o[db] = f32x16{};
-    const size_t srow = (size_t)head * n_q + row;
     // Group 0 carries the incoming state.  Group 1 starts with empty sums but
     // the same reference max, so its first tiles do not trigger rescales
     // (any reference at or above the scores seen gives the same softmax).
@@ -484,18 +487,28 @@ struct Step {
           for (int e = 0; e < 4; ++e) o[db][4 * g + e] = x[e];
         }
     }
-    const float m2_0 = m2;
+    m2_0 = m2;
     c2 = a.c2;
-    cnt_full = cnt_masked = 0;
     resc = false;
+  }
 
-    // Ping-pong schedule.  Each group alternates softmax phases (VALU) and
-    // GEMM phases (MFMA) on its own tiles, one workgroup barrier after each
-    // phase.  Group 1 starts one phase later, so on every SIMD one wave feeds
-    // the matrix pipe while the other runs the softmax, and each barrier
-    // swaps their roles.  Group g passes g + 1 + 2 n_own barriers after the
-    // prologue and pads to the larger count of the two.
+  // Folds one key/value block (already classified) into the running state.
+  // Ping-pong schedule.  Each group alternates softmax phases (VALU) and
+  // GEMM phases (MFMA) on its own tiles, one workgroup barrier after each
+  // phase.  Group 1 starts one phase later, so on every SIMD one wave feeds
+  // the matrix pipe while the other runs the softmax, and each barrier
+  // swaps their roles.  Group g passes g + 1 + 2 n_own barriers after the
+  // prologue and pads to the larger count of the two.  Every wave of the
+  // workgroup takes the same branches (n_iter is workgroup-uniform).
+  __device__ __forceinline__ void fold_block(const void* k, const void* v, const int32_t* k_pos,
+                                             int kvh) {
+    cnt_full = cnt_masked = 0;
     if (n_iter > 0) {
+      kbase = (const uint16_t*)k + ((size_t)kvh * n_k) * D;
+      vbase = (const uint16_t*)v + ((size_t)kvh * n_k) * D;
+      krs = buffer_rsrc(kbase, n_k * D * 2);
+      vrs = buffer_rsrc(vbase, n_k * D * 2);
+      prs = buffer_rsrc(k_pos, n_k * 4);
       if (n_own > 0) {
         load_k_tile(grp, 0);
         load_pos(grp, 0);
@@ -526,14 +539,16 @@ struct Step {
       const int n_bar = max(2 * n0 + 1, 2 * n1 + 2);
       for (int b = grp + 1 + 2 * n_own; b < n_bar; ++b) phase_barrier();
     }
-
     if (count && lane == 0) {
       atomicAdd(a.work + 0, (unsigned long long)cnt_full);
       atomicAdd(a.work + 1, (unsigned long long)cnt_masked);
       atomicAdd(a.work + 2, (unsigned long long)(n_kt_g - cnt_full - cnt_masked));
     }
+  }
 
-    // Fold group 1's partial state into group 0's through LDS.
+  // Folds group 1's partial state into group 0's through LDS and writes the
+  // result: normalised out/lse (FINAL) or the running state.
+  __device__ __forceinline__ void finish() {
     __syncthreads();  // every wave is done with the K/V stages
     float* mo = (float*)&sm.k[0][0][0];            // [wave][reg][lane] O^T values
     float* ml = mo + 4 * 64 * 64;                  // [wave][lane] m2, then lsum
@@ -596,6 +611,33 @@ struct Step {
       }
     }
   }
+
+  // One ring step: the query tile against the block in a.k / a.v.
+  __device__ void run(int qt, int head) {
+    positions(qt, head);
+    classify(a.k_pos);
+    if (READ && !FINAL && n_iter == 0) {
+      // nothing visible: the state stays as it is
+      if (count && lane == 0) atomicAdd(a.work + 2, (unsigned long long)n_kt_g);
+      return;
+    }
+    load_state(head);
+    fold_block(a.k, a.v, a.k_pos, head / (a.h_q / a.h_kv));
+    finish();
+  }
+
+  // All blocks resident: the query tile against every block in turn, the
+  // running state staying in registers between them.
+  __device__ void run_all(const MultiArgs& ma, int qt, int head) {
+    positions(qt, head);
+    load_state(head);
+    const int kvh = head / (a.h_q / a.h_kv);
+    for (int b = 0; b < ma.n_blocks; ++b) {
+      classify(ma.k_pos[b]);
+      fold_block(ma.k[b], ma.v[b], ma.k_pos[b], kvh);
+    }
+    finish();
+  }
 };
 
 template <bool READ, bool FINAL>
@@ -615,7 +657,30 @@ void step_kernel_fast(const StepArgs a) {
   }
 }
 
+// All-gather form: every key/value block resident, one launch.
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void allgather_kernel_fast(const MultiArgs ma) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x;
+  const int u = blockIdx.x;
+  const int head = ma.s.head_of[u % ma.s.h_q];
+  const int p = u / ma.s.h_q;
+  const int t_hi = ma.s.n_qt - 1 - p, t_lo = p;
+  Step<false, true> s(ma.s, sm, tid);
+  s.run_all(ma, t_hi, head);
+  if (t_lo < t_hi) {
+    __syncthreads();
+    s.run_all(ma, t_lo, head);
+  }
+}
+
 }  // namespace fast
+
+hipError_t launch_allgather_fast(const MultiArgs& ma, hipStream_t stream) {
+  dim3 grid((unsigned)(ma.s.n_pairs * ma.s.h_q)), block(fast::THREADS);
+  hipLaunchKernelGGL(fast::allgather_kernel_fast, grid, block, 0, stream, ma);
+  return hipGetLastError();
+}
 
 hipError_t launch_step_fast(const StepArgs& a, bool read, bool final_, hipStream_t stream) {
   dim3 grid((unsigned)(a.n_pairs * a.h_q)), block(fast::THREADS);

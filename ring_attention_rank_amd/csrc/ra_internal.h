@@ -12,6 +12,7 @@ constexpr int kRowsPerWave = 32;   // query rows a wave owns (one 32-row MFMA bl
 constexpr int kRowsPerGroup = kWavesPerGroup * kRowsPerWave;  // 128
 constexpr int kKeysPerTile = 64;   // keys per LDS tile
 constexpr int kMaxHeads = 256;
+constexpr int kMaxBlocks = 64;     // key/value blocks of one all-gather launch
 
 // Arguments of one ring-step launch (one key/value block against all local
 // queries of all heads).  READ selects whether the state is read (else it
@@ -39,10 +40,22 @@ struct StepArgs {
   uint8_t head_of[kMaxHeads];  // launch-order slot -> query head (L2 locality)
 };
 
+// All key/value blocks resident (the all-gather form): one launch folds them
+// all, in order, into a register-resident state and writes out/lse.
+struct MultiArgs {
+  StepArgs s;  // q, q_pos, out, lse, work, sizes; s.k, s.v, s.k_pos unused
+  int32_t n_blocks;
+  const void* k[kMaxBlocks];
+  const void* v[kMaxBlocks];
+  const int32_t* k_pos[kMaxBlocks];
+};
+
 hipError_t launch_step(const StepArgs& a, int dtype, int d_k, bool read, bool final_,
                        hipStream_t stream);
 // bfloat16, d_k = 128: the 8-wave kernel with direct-to-LDS staging.
 hipError_t launch_step_fast(const StepArgs& a, bool read, bool final_, hipStream_t stream);
+// bfloat16, d_k = 128 only.
+hipError_t launch_allgather_fast(const MultiArgs& ma, hipStream_t stream);
 hipError_t launch_state_init(float* m, float* l, float* o, int64_t rows, int d_k,
                              hipStream_t stream);
 hipError_t launch_finalize(const float* m, const float* l, const float* o, float* out,

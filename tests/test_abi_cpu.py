@@ -8,6 +8,8 @@ import re
 
 import pytest
 
+import torch
+
 import ring_attention_rank_amd as ra
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -110,3 +112,28 @@ def test_forward_checks():
     bad = (ctypes.c_void_p * 2)(FAKE, 0)
     assert L.ra_forward(ctypes.byref(p), 2, v, v, bad, arr, arr, v, need, v, v, None,
                         ctypes.byref(staged), None, None) == NULL
+
+
+def test_allgather_checks():
+    L = ra.lib()
+    v = ctypes.c_void_p(FAKE)
+    arr = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    p = good()  # bf16, d_k 128: the register-resident path needs no workspace
+    assert ra.allgather_workspace_bytes(p) == 0
+    args = lambda p, ncp, ws, wsb: (ctypes.byref(p), ncp, v, v, arr, arr, arr, ws, wsb, v, v,
+                                    None, None)
+    assert L.ra_forward_allgather(*args(p, 0, None, 0)) == SHAPE
+    assert L.ra_forward_allgather(*args(p, 65, None, 0)) == SHAPE
+    bad = (ctypes.c_void_p * 2)(FAKE, 0)
+    assert L.ra_forward_allgather(ctypes.byref(p), 2, v, v, arr, bad, arr, None, 0, v, v,
+                                  None, None) == NULL
+    odd = (ctypes.c_void_p * 2)(FAKE, FAKE + 8)
+    assert L.ra_forward_allgather(ctypes.byref(p), 2, v, v, odd, arr, arr, None, 0, v, v,
+                                  None, None) == ALIGN
+    # other shapes keep the running state in the workspace
+    pf = ra.problem(256, 256, 4, 2, 64, torch.float32)
+    need = ra.allgather_workspace_bytes(pf)
+    assert need >= 4 * 256 * 4 * 2 + 4 * 256 * 64 * 4
+    assert L.ra_forward_allgather(*args(pf, 2, None, need)) == NULL
+    assert L.ra_forward_allgather(*args(pf, 2, v, need - 1)) == WORKSPACE
+    assert L.ra_forward_allgather(*args(pf, 2, ctypes.c_void_p(FAKE + 4), need)) == ALIGN
