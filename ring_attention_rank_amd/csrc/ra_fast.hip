@@ -236,6 +236,19 @@ struct Step {
     else __builtin_amdgcn_s_waitcnt(0x0f70);              // vmcnt(0)
   }
 
+  // The first two K tiles and position tiles of a block (own tiles 0 and 1),
+  // into K stages 0, 1 and position stages 0, 1.
+  __device__ __forceinline__ void load_block_head(int n_own_b) {
+    if (n_own_b > 0) {
+      load_k_tile(grp, 0);
+      load_pos(grp, 0);
+    }
+    if (n_own_b > 1) {
+      load_k_tile(2 + grp, 1);
+      load_pos(2 + grp, 1);
+    }
+  }
+
   // ---- MFMA pieces --------------------------------------------------------
   __device__ __forceinline__ f32x16 qk(int stage, int kb) const {
     const uint8_t* base = sm.k[grp][stage] + kb * 32 * 256;
@@ -386,6 +399,7 @@ struct Step {
   // own tile 0; the last phase only PV.
   template <bool PV, bool QK>
   __device__ __forceinline__ void gemm_phase(int s) {
+    if (PV && !QK) prefetch_next_head();
     if (QK) {
       sc[0] = qk((s + 1) & 1, 0);
       sc[1] = qk((s + 1) & 1, 1);
@@ -432,27 +446,58 @@ struct Step {
   // Positions increase, so the key tiles the workgroup sees form a prefix of
   // the block (n_iter tiles), and so do the tiles this wave sees completely
   // (n_full_w) and at all (n_vis_w).
-  __device__ __forceinline__ void classify(const int32_t* k_pos) {
-    n_kt = (n_k + BN - 1) / BN;
-    n_iter = n_kt;
+  struct Classes {
+    int n_iter, n_full_w, n_vis_w;
+  };
+  __device__ __forceinline__ Classes classes_of(const int32_t* k_pos) const {
+    const int nkt = (n_k + BN - 1) / BN;
+    Classes c{nkt, 0, 0};
     if (causal) {
       int ci = 0, cf = 0, cv = 0;
-      for (int j = lane; j < n_kt; j += 64) {
+      for (int j = lane; j < nkt; j += 64) {
         const int kf = k_pos[j * BN];
         const int kl = k_pos[min(j * BN + BN, n_k) - 1];
         ci += kf <= qmax_wg ? 1 : 0;
         cf += kl <= qmin_w ? 1 : 0;
         cv += kf <= qmax_w ? 1 : 0;
       }
-      n_iter = __builtin_amdgcn_readfirstlane(wave_sum_i(ci));
-      n_full_w = wave_valid ? __builtin_amdgcn_readfirstlane(wave_sum_i(cf)) : 0;
-      n_vis_w = wave_valid ? __builtin_amdgcn_readfirstlane(wave_sum_i(cv)) : 0;
+      c.n_iter = __builtin_amdgcn_readfirstlane(wave_sum_i(ci));
+      c.n_full_w = wave_valid ? __builtin_amdgcn_readfirstlane(wave_sum_i(cf)) : 0;
+      c.n_vis_w = wave_valid ? __builtin_amdgcn_readfirstlane(wave_sum_i(cv)) : 0;
     } else {
-      n_full_w = n_vis_w = wave_valid ? n_kt : 0;
+      c.n_full_w = c.n_vis_w = wave_valid ? nkt : 0;
     }
+    return c;
+  }
+  // This group's own tiles among n_iter visited key tiles.
+  __device__ __forceinline__ int own_tiles(int n_it) const { return (n_it - grp + 1) / 2; }
+  __device__ __forceinline__ void use_classes(const Classes& c) {
+    n_kt = (n_k + BN - 1) / BN;
+    n_iter = c.n_iter;
+    n_full_w = c.n_full_w;
+    n_vis_w = c.n_vis_w;
     // tiles of this group among all key tiles, and among the visited ones
     n_kt_g = (n_kt - grp + 1) / 2;
-    n_own = (n_iter - grp + 1) / 2;
+    n_own = own_tiles(n_iter);
+  }
+  __device__ __forceinline__ void classify(const int32_t* k_pos) { use_classes(classes_of(k_pos)); }
+
+  // Next block of an all-gather run: its buffers and tile classes, and
+  // whether this group already issued the loads of its first tiles.
+  const void* nxt_k = nullptr;
+  const int32_t* nxt_pos = nullptr;
+  int nxt_own = 0, nxt_kvh = 0;
+  bool head_issued = false;
+
+  // Issued by the last GEMM phase of a block (PV only: the K stages are idle
+  // and the position stages were last read by the softmax phase before it):
+  // K and positions of the next block's first two own tiles.
+  __device__ __forceinline__ void prefetch_next_head() {
+    if (nxt_k == nullptr || nxt_own == 0) return;
+    krs = buffer_rsrc((const uint16_t*)nxt_k + ((size_t)nxt_kvh * n_k) * D, n_k * D * 2);
+    prs = buffer_rsrc(nxt_pos, n_k * 4);
+    load_block_head(nxt_own);
+    head_issued = true;
   }
 
   // Q into registers and the incoming state (READ) or the empty one.
@@ -509,16 +554,16 @@ struct Step {
       krs = buffer_rsrc(kbase, n_k * D * 2);
       vrs = buffer_rsrc(vbase, n_k * D * 2);
       prs = buffer_rsrc(k_pos, n_k * 4);
+      if (!head_issued) load_block_head(n_own);
+      head_issued = false;
+      // V of own tile 0 is first read two phases on; the softmax phase of
+      // own tile 0 waits for it.  Everything older must land now.
       if (n_own > 0) {
-        load_k_tile(grp, 0);
-        load_pos(grp, 0);
         load_v_tile(grp, 0);
+        wait_loads(4);
+      } else {
+        wait_loads(0);
       }
-      if (n_own > 1) {
-        load_k_tile(2 + grp, 1);
-        load_pos(2 + grp, 1);
-      }
-      wait_loads(0);
       phase_barrier();
       if (grp == 1) phase_barrier();
       if (n_own > 0) gemm_phase<false, true>(-1);
@@ -632,10 +677,26 @@ struct Step {
     positions(qt, head);
     load_state(head);
     const int kvh = head / (a.h_q / a.h_kv);
+    head_issued = false;
+    nxt_kvh = kvh;
+    Classes cur = ma.n_blocks > 0 ? classes_of(ma.k_pos[0]) : Classes{0, 0, 0};
     for (int b = 0; b < ma.n_blocks; ++b) {
-      classify(ma.k_pos[b]);
+      use_classes(cur);
+      // the next block's classes (their loads overlap this block) and what
+      // its first tiles need
+      if (b + 1 < ma.n_blocks) {
+        cur = classes_of(ma.k_pos[b + 1]);
+        nxt_k = ma.k[b + 1];
+        nxt_pos = ma.k_pos[b + 1];
+        nxt_own = own_tiles(cur.n_iter);
+      } else {
+        nxt_k = nullptr;
+        nxt_pos = nullptr;
+        nxt_own = 0;
+      }
       fold_block(ma.k[b], ma.v[b], ma.k_pos[b], kvh);
     }
+    nxt_k = nullptr;
     finish();
   }
 };
