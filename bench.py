@@ -142,7 +142,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="llama405b_stage_share",
-                    choices=[c.name for c in synth.CASES])
+                    choices=[c.name for c in synth.CASES + synth.ULYSSES_CASES])
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)

@@ -19,7 +19,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-from .configs import CASES, Case, case_by_name  # noqa: F401
+from .configs import CASES, ULYSSES_CASES, Case, case_by_name  # noqa: F401
 
 CHUNK = 4096
 TENSOR_Q, TENSOR_K, TENSOR_V = 0, 1, 2

@@ -52,8 +52,21 @@ CASES = (
 )
 
 
+# Ulysses local shares (heads split across the group, every GPU attends its
+# heads over the whole sequence): one block of all T keys, positions 0..T-1.
+# 8B-like: 32 q / 8 kv heads over 4 GPUs -> 8 q / 2 kv heads each.
+# 405B stage after tensor parallelism: 16 q / 1 kv heads over 16 GPUs -> one
+# query head each, the single key/value head replicated.
+ULYSSES_CASES = (
+    Case("llama8b_ulysses_share", T=32768, n_cp=1, layout="contiguous", ranks=(0,),
+         h_q=8, h_kv=2, d_k=128, dtype="bf16", seed=1006),
+    Case("llama405b_ulysses_share", T=131072, n_cp=1, layout="contiguous", ranks=(0,),
+         h_q=1, h_kv=1, d_k=128, dtype="bf16", seed=1007),
+)
+
+
 def case_by_name(name):
-    for c in CASES:
+    for c in CASES + ULYSSES_CASES:
         if c.name == name:
             return c
     raise KeyError(name)
