@@ -42,6 +42,11 @@ from .ring import (  # noqa: F401
     brute_attention,
     default_scale,
 )
+from .backward import (  # noqa: F401
+    backward_prep_ref,
+    block_backward_ref,
+    ring_backward_ref,
+)
 from .counts import (  # noqa: F401
     chunk_assignment,
     causal_work,
