@@ -150,6 +150,33 @@ ra_status ra_forward_allgather(const ra_problem* p, int32_t n_cp, const void* q,
                                void* workspace, size_t ws_bytes, float* out, float* lse,
                                int64_t* work, void* stream);
 
+/*
+ * Backward of the rank share (Zero to Frontier, "distributed/context-expert",
+ * section "Splitting the sequence, and the one layer that objects": the
+ * backward mirrors the forward; each GPU computes, from its own queries, the
+ * gradients of every key/value block it sees, returned to the block's owner
+ * as a second circulating block in the ring or by a reduce-scatter in the
+ * all-gather form).  bfloat16 with d_k = 128 only (RA_ERR_DTYPE /
+ * RA_ERR_SHAPE otherwise).  With s = scale q.k over visible pairs and the
+ * forward's lse (natural log, over all blocks): p = exp(s - lse),
+ * delta = rowsum(dout * out), ds = p (dout.v - delta).
+ *
+ * ra_backward_prep: delta[h_q][n_q] (fp32) from out[h_q][n_q][d_k] (fp32, the
+ * forward's output) and dout[h_q][n_q][d_k] (bf16).
+ * ra_backward_step: one key/value block.  dq[h_q][n_q][d_k] (fp32) is
+ * ACCUMULATED (+= scale * sum_j ds k_j; zero it before the first block);
+ * dk, dv[h_kv][n_k][d_k] (fp32) are OVERWRITTEN with this block's gradients
+ * (dk = scale * sum_i ds q_i, dv = sum_i p dout_i, summed over the query heads
+ * that read each key/value head).  q, k, v, dout 16-byte aligned, as the
+ * forward's; dq, dk, dv 16-byte aligned.  Asynchronous on stream.
+ */
+ra_status ra_backward_prep(const ra_problem* p, const float* out, const void* dout,
+                           float* delta, void* stream);
+ra_status ra_backward_step(const ra_problem* p, const void* q, const int32_t* q_pos,
+                           const void* k, const void* v, const int32_t* k_pos, const void* dout,
+                           const float* lse, const float* delta, float* dq, float* dk, float* dv,
+                           void* stream);
+
 /* Query-tile rows (bm) and key-tile columns (bn) the tile counters use. */
 ra_status ra_tile_shape(const ra_problem* p, int32_t* bm, int32_t* bn);
 

@@ -6,7 +6,8 @@ in the library's HIP kernels.  There is no CPU fallback: when libra.so is
 missing or the device is not a GPU, calls raise.
 
 Entry points mirror include/ra.h: ``state_init``, ``step``, ``finalize``,
-``forward``, ``tile_shape``, ``workspace_bytes``.
+``forward``, ``forward_allgather``, ``backward_prep``, ``backward_step``,
+``backward``, ``tile_shape``, ``workspace_bytes``.
 """
 
 import ctypes
@@ -25,7 +26,7 @@ RA_BF16, RA_F32 = 0, 1
 SYMBOLS = (
     "ra_state_init", "ra_step", "ra_finalize", "ra_forward_workspace_bytes", "ra_forward",
     "ra_forward_allgather_workspace_bytes", "ra_forward_allgather",
-    "ra_tile_shape", "ra_status_string", "ra_abi_version",
+    "ra_backward_prep", "ra_backward_step", "ra_tile_shape", "ra_status_string", "ra_abi_version",
 )
 
 
@@ -69,11 +70,14 @@ def lib():
     L.ra_forward_allgather_workspace_bytes.restype = ctypes.c_size_t
     L.ra_forward_allgather.argtypes = [P, i32, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                        ctypes.POINTER(vp), vp, ctypes.c_size_t, vp, vp, vp, vp]
+    L.ra_backward_prep.argtypes = [P, vp, vp, vp, vp]
+    L.ra_backward_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.ra_tile_shape.argtypes = [P, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.ra_status_string.argtypes = [i32]
     L.ra_status_string.restype = ctypes.c_char_p
     L.ra_abi_version.argtypes = []
     for name in ("ra_state_init", "ra_step", "ra_finalize", "ra_forward", "ra_tile_shape",
+                 "ra_forward_allgather", "ra_backward_prep", "ra_backward_step",
                  "ra_abi_version"):
         getattr(L, name).restype = i32
     _lib = L
@@ -268,3 +272,47 @@ def forward(q, q_pos, k_blocks, v_blocks, k_pos_blocks, causal=True, scale=None,
     f = Forward(q, q_pos, k_blocks, v_blocks, k_pos_blocks, causal, scale, side)
     out, lse = f()
     return out, lse, f.work, f.staged.value
+
+
+def backward_prep(out, dout, delta=None, stream=None):
+    """delta[h_q][n_q] = rowsum(dout * out) (fp32) for the backward; ``out`` is
+    the forward's fp32 output, ``dout`` its gradient in the queries' dtype."""
+    _need_gpu(out, dout, delta)
+    h_q, n_q, d_k = out.shape
+    p = problem(n_q, 0, h_q, h_q, d_k, dout.dtype)
+    if delta is None:
+        delta = torch.empty((h_q, n_q), dtype=torch.float32, device=out.device)
+    _check(lib().ra_backward_prep(ctypes.byref(p), _ptr(out), _ptr(dout), _ptr(delta),
+                                  _stream(stream)), "ra_backward_prep")
+    return delta
+
+
+def backward_step(q, q_pos, k, v, k_pos, dout, lse, delta, dq, dk=None, dv=None, causal=True,
+                  scale=None, stream=None):
+    """One key/value block of the backward: adds this block's part to ``dq``
+    (fp32, in place) and returns (dk, dv), fp32 ``[h_kv][n_k][d_k]``."""
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=torch.float32, device=k.device)
+    if dv is None:
+        dv = torch.empty(v.shape, dtype=torch.float32, device=v.device)
+    _need_gpu(q, q_pos, k, v, k_pos, dout, lse, delta, dq, dk, dv)
+    p = _problem_from(q, k, causal, scale)
+    _check(lib().ra_backward_step(ctypes.byref(p), _ptr(q), _ptr(q_pos), _ptr(k), _ptr(v),
+                                  _ptr(k_pos), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq),
+                                  _ptr(dk), _ptr(dv), _stream(stream)), "ra_backward_step")
+    return dk, dv
+
+
+def backward(q, q_pos, k_blocks, v_blocks, k_pos_blocks, out, lse, dout, causal=True,
+             scale=None, stream=None):
+    """The rank share's backward over every block: returns (dq, dks, dvs), fp32,
+    one (dk, dv) per block in the order given."""
+    delta = backward_prep(out, dout, stream=stream)
+    dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+    dks, dvs = [], []
+    for k, v, kp in zip(k_blocks, v_blocks, k_pos_blocks):
+        dk, dv = backward_step(q, q_pos, k, v, kp, dout, lse, delta, dq, causal=causal,
+                               scale=scale, stream=stream)
+        dks.append(dk)
+        dvs.append(dv)
+    return dq, dks, dvs

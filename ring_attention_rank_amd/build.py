@@ -13,6 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libra.so")
 SOURCES = [os.path.join(CSRC, "ra_kernels.hip"), os.path.join(CSRC, "ra_fast.hip"),
+           os.path.join(CSRC, "ra_bwd.hip"),
            os.path.join(CSRC, "ra_host.cpp")]
 ARCH = "gfx950"
 

@@ -360,6 +360,58 @@ cleanup:
   return result;
 }
 
+ra_status ra_backward_prep(const ra_problem* p, const float* out, const void* dout,
+                           float* delta, void* stream) {
+  ra_status st = check_problem(p);
+  if (st != RA_OK) return st;
+  if (!fast_path(p)) return p->dtype != RA_BF16 ? RA_ERR_DTYPE : RA_ERR_SHAPE;
+  const int64_t rows = (int64_t)p->h_q * p->n_q;
+  if (rows == 0) return RA_OK;
+  if (!out || !dout || !delta) return RA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(dout) || !aligned4(delta)) return RA_ERR_ALIGN;
+  hipError_t e = ra::launch_backward_delta(out, dout, delta, rows, (hipStream_t)stream);
+  return e == hipSuccess ? RA_OK : RA_ERR_HIP;
+}
+
+ra_status ra_backward_step(const ra_problem* p, const void* q, const int32_t* q_pos,
+                           const void* k, const void* v, const int32_t* k_pos, const void* dout,
+                           const float* lse, const float* delta, float* dq, float* dk, float* dv,
+                           void* stream) {
+  ra_status st = check_problem(p);
+  if (st != RA_OK) return st;
+  if (!fast_path(p)) return p->dtype != RA_BF16 ? RA_ERR_DTYPE : RA_ERR_SHAPE;
+  if (p->n_q > 0 && (!q || !q_pos || !dout || !lse || !delta || !dq)) return RA_ERR_NULL;
+  if (p->n_k > 0 && (!k || !v || !k_pos || !dk || !dv)) return RA_ERR_NULL;
+  if (p->n_q > 0 && (!aligned16(q) || !aligned4(q_pos) || !aligned16(dout) || !aligned4(lse) ||
+                     !aligned4(delta) || !aligned16(dq)))
+    return RA_ERR_ALIGN;
+  if (p->n_k > 0 && (!aligned16(k) || !aligned16(v) || !aligned4(k_pos) || !aligned16(dk) ||
+                     !aligned16(dv)))
+    return RA_ERR_ALIGN;
+  if (p->n_q == 0 && p->n_k == 0) return RA_OK;
+  ra::BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.q_pos = q_pos;
+  a.k = k;
+  a.v = v;
+  a.k_pos = k_pos;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.n_q = p->n_q;
+  a.n_k = p->n_k;
+  a.h_q = p->h_q;
+  a.h_kv = p->h_kv;
+  a.causal = p->causal;
+  a.scale = softmax_scale(p);
+  a.c2 = a.scale * 1.4426950408889634f;
+  return ra::launch_backward(a, (hipStream_t)stream) == hipSuccess ? RA_OK : RA_ERR_HIP;
+}
+
 size_t ra_forward_allgather_workspace_bytes(const ra_problem* p) {
   if (check_problem(p) != RA_OK) return 0;
   return allgather_ws_bytes(p);

@@ -54,6 +54,28 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d_k, bool read, bool fi
                        hipStream_t stream);
 // bfloat16, d_k = 128: the 8-wave kernel with direct-to-LDS staging.
 hipError_t launch_step_fast(const StepArgs& a, bool read, bool final_, hipStream_t stream);
+// Backward of one key/value block (bfloat16, d_k = 128): dq += this block's
+// part, dk and dv = this block's gradients (fp32, summed over the query heads
+// of each key/value head).
+struct BwdArgs {
+  const void* q;
+  const int32_t* q_pos;
+  const void* k;
+  const void* v;
+  const int32_t* k_pos;
+  const void* dout;
+  const float* lse;    // [h_q][n_q], natural log, from the forward
+  const float* delta;  // [h_q][n_q] = rowsum(dout * out)
+  float* dq;           // [h_q][n_q][128], accumulated
+  float* dk;           // [h_kv][n_k][128], written
+  float* dv;
+  int32_t n_q, n_k, h_q, h_kv, causal;
+  float scale, c2;
+};
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_backward_delta(const float* out, const void* dout, float* delta, int64_t rows,
+                                 hipStream_t stream);
+
 // bfloat16, d_k = 128 only.
 hipError_t launch_allgather_fast(const MultiArgs& ma, hipStream_t stream);
 hipError_t launch_state_init(float* m, float* l, float* o, int64_t rows, int d_k,

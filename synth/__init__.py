@@ -7,7 +7,7 @@ layout (contiguous, zigzag, striped) slices the same global sequence.  The
 caller computes the positions itself.
 
 Recipe: values are drawn per 4096-token global chunk.  Chunk c of tensor t
-(0 = Q, 1 = K, 2 = V) of a workload with seed S is
+(0 = Q, 1 = K, 2 = V, 3 = the output gradient dO of the backward) of a workload with seed S is
 ``numpy.random.Generator(PCG64(SeedSequence([S, t, c]))).standard_normal(
 (heads, 4096, d_k), float32)``, multiplied by the tensor's amplitude (1 or 2,
 both exact), and for 16-bit workloads rounded once to bfloat16 with
@@ -22,7 +22,7 @@ import numpy as np
 from .configs import CASES, ULYSSES_CASES, Case, case_by_name  # noqa: F401
 
 CHUNK = 4096
-TENSOR_Q, TENSOR_K, TENSOR_V = 0, 1, 2
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_DOUT = 0, 1, 2, 3
 _THREADS = 8
 
 
@@ -97,3 +97,10 @@ def case_inputs(case, q_pos, k_pos_blocks):
         v_blocks.append(np.ascontiguousarray(vv[:, o:o + n]))
         o += n
     return q, k_blocks, v_blocks
+
+
+def case_dout(case, q_pos):
+    """Output gradient rows (amplitude 1) at the local query positions,
+    ``[h_q][len(q_pos)][d_k]`` float32 holding values of the workload's dtype."""
+    return global_rows(case.seed, TENSOR_DOUT, case.h_q, case.d_k, q_pos, 1.0,
+                       case.dtype == "bf16")

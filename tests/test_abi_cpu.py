@@ -137,3 +137,31 @@ def test_allgather_checks():
     assert L.ra_forward_allgather(*args(pf, 2, None, need)) == NULL
     assert L.ra_forward_allgather(*args(pf, 2, v, need - 1)) == WORKSPACE
     assert L.ra_forward_allgather(*args(pf, 2, ctypes.c_void_p(FAKE + 4), need)) == ALIGN
+
+
+def test_backward_checks():
+    L = ra.lib()
+    v = ctypes.c_void_p(FAKE)
+    odd = ctypes.c_void_p(FAKE + 4)
+    step = lambda p, *ptrs: L.ra_backward_step(ctypes.byref(p), *ptrs, None)
+    full = [v] * 11
+    # bfloat16 with d_k = 128 only
+    assert step(good(dtype=ra.RA_F32), *full) == DTYPE
+    assert step(good(d_k=64), *full) == SHAPE
+    assert step(good(h_q=3), *full) == SHAPE
+    assert L.ra_backward_prep(ctypes.byref(good(dtype=ra.RA_F32)), v, v, v, None) == DTYPE
+    # every pointer of a non-empty side is required
+    for i in range(11):
+        ptrs = list(full)
+        ptrs[i] = None
+        assert step(good(), *ptrs) == NULL, i
+    # q, k, v, dout, dq, dk, dv 16-byte aligned; positions, lse, delta 4-byte
+    for i in (0, 2, 3, 5, 8, 9, 10):
+        ptrs = list(full)
+        ptrs[i] = odd
+        assert step(good(), *ptrs) == ALIGN, i
+    # nothing to do: no pointer is needed (the empty sides run on the GPU tests)
+    assert step(good(n_q=0, n_k=0), *([None] * 11)) == OK
+    assert L.ra_backward_prep(ctypes.byref(good()), None, v, v, None) == NULL
+    assert L.ra_backward_prep(ctypes.byref(good()), v, odd, v, None) == ALIGN
+    assert L.ra_backward_prep(ctypes.byref(good(n_q=0)), None, None, None, None) == OK
