@@ -168,14 +168,22 @@ ra_status ra_forward_allgather(const ra_problem* p, int32_t n_cp, const void* q,
  * dk, dv[h_kv][n_k][d_k] (fp32) are OVERWRITTEN with this block's gradients
  * (dk = scale * sum_i ds q_i, dv = sum_i p dout_i, summed over the query heads
  * that read each key/value head).  q, k, v, dout 16-byte aligned, as the
- * forward's; dq, dk, dv 16-byte aligned.  Asynchronous on stream.
+ * forward's; dq, dk, dv 16-byte aligned.  When few key/value heads leave the
+ * dk/dv grid small, the query heads of each group are split across
+ * workgroups: each split writes partial sums into the caller's workspace
+ * (ra_backward_workspace_bytes(p) bytes, 16-byte aligned, device memory,
+ * contents unspecified after the call) and they are added in a fixed order,
+ * so results do not depend on scheduling.  A call that needs no workspace
+ * (the size is 0) accepts NULL.  Returns RA_ERR_WORKSPACE when it is too
+ * small.  Asynchronous on stream; calls sharing a workspace must be ordered.
  */
 ra_status ra_backward_prep(const ra_problem* p, const float* out, const void* dout,
                            float* delta, void* stream);
+size_t ra_backward_workspace_bytes(const ra_problem* p);
 ra_status ra_backward_step(const ra_problem* p, const void* q, const int32_t* q_pos,
                            const void* k, const void* v, const int32_t* k_pos, const void* dout,
                            const float* lse, const float* delta, float* dq, float* dk, float* dv,
-                           void* stream);
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Query-tile rows (bm) and key-tile columns (bn) the tile counters use. */
 ra_status ra_tile_shape(const ra_problem* p, int32_t* bm, int32_t* bn);

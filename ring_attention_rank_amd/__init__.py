@@ -26,7 +26,7 @@ RA_BF16, RA_F32 = 0, 1
 SYMBOLS = (
     "ra_state_init", "ra_step", "ra_finalize", "ra_forward_workspace_bytes", "ra_forward",
     "ra_forward_allgather_workspace_bytes", "ra_forward_allgather",
-    "ra_backward_prep", "ra_backward_step", "ra_tile_shape", "ra_status_string", "ra_abi_version",
+    "ra_backward_prep", "ra_backward_workspace_bytes", "ra_backward_step", "ra_tile_shape", "ra_status_string", "ra_abi_version",
 )
 
 
@@ -71,7 +71,10 @@ def lib():
     L.ra_forward_allgather.argtypes = [P, i32, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                        ctypes.POINTER(vp), vp, ctypes.c_size_t, vp, vp, vp, vp]
     L.ra_backward_prep.argtypes = [P, vp, vp, vp, vp]
-    L.ra_backward_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.ra_backward_workspace_bytes.argtypes = [P]
+    L.ra_backward_workspace_bytes.restype = ctypes.c_size_t
+    L.ra_backward_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                   ctypes.c_size_t, vp]
     L.ra_tile_shape.argtypes = [P, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.ra_status_string.argtypes = [i32]
     L.ra_status_string.restype = ctypes.c_char_p
@@ -287,19 +290,30 @@ def backward_prep(out, dout, delta=None, stream=None):
     return delta
 
 
+def backward_workspace_bytes(p):
+    return int(lib().ra_backward_workspace_bytes(ctypes.byref(p)))
+
+
 def backward_step(q, q_pos, k, v, k_pos, dout, lse, delta, dq, dk=None, dv=None, causal=True,
-                  scale=None, stream=None):
+                  scale=None, stream=None, workspace=None):
     """One key/value block of the backward: adds this block's part to ``dq``
-    (fp32, in place) and returns (dk, dv), fp32 ``[h_kv][n_k][d_k]``."""
+    (fp32, in place) and returns (dk, dv), fp32 ``[h_kv][n_k][d_k]``.
+    ``workspace`` is a uint8 device tensor of at least
+    ``backward_workspace_bytes`` bytes (allocated here when None)."""
     if dk is None:
         dk = torch.empty(k.shape, dtype=torch.float32, device=k.device)
     if dv is None:
         dv = torch.empty(v.shape, dtype=torch.float32, device=v.device)
-    _need_gpu(q, q_pos, k, v, k_pos, dout, lse, delta, dq, dk, dv)
+    _need_gpu(q, q_pos, k, v, k_pos, dout, lse, delta, dq, dk, dv, workspace)
     p = _problem_from(q, k, causal, scale)
+    if workspace is None:
+        need = backward_workspace_bytes(p)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    wsb = workspace.numel() if workspace is not None else 0
     _check(lib().ra_backward_step(ctypes.byref(p), _ptr(q), _ptr(q_pos), _ptr(k), _ptr(v),
                                   _ptr(k_pos), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq),
-                                  _ptr(dk), _ptr(dv), _stream(stream)), "ra_backward_step")
+                                  _ptr(dk), _ptr(dv), _ptr(workspace), wsb, _stream(stream)),
+           "ra_backward_step")
     return dk, dv
 
 
@@ -310,9 +324,12 @@ def backward(q, q_pos, k_blocks, v_blocks, k_pos_blocks, out, lse, dout, causal=
     delta = backward_prep(out, dout, stream=stream)
     dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
     dks, dvs = [], []
+    need = max([backward_workspace_bytes(_problem_from(q, k, causal, scale)) for k in k_blocks],
+               default=0)
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
     for k, v, kp in zip(k_blocks, v_blocks, k_pos_blocks):
         dk, dv = backward_step(q, q_pos, k, v, kp, dout, lse, delta, dq, causal=causal,
-                               scale=scale, stream=stream)
+                               scale=scale, stream=stream, workspace=ws)
         dks.append(dk)
         dvs.append(dv)
     return dq, dks, dvs

@@ -1,0 +1,142 @@
+// Shared pieces of the backward kernels (bfloat16, d_k = 128, gfx950): MFMA
+// operand layouts, LDS swizzles and tile staging.  Included by the dq and
+// the dk/dv translation units, which are compiled with different register
+// forms for the MFMA accumulators.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "ra_internal.h"
+
+namespace ra {
+namespace bwd {
+
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int D = 128;
+constexpr int ROWS = 128;      // rows a workgroup owns (4 waves x 32)
+constexpr int TILE = 64;       // rows of a staged tile
+constexpr int THREADS = 256;
+constexpr int TILE_BYTES = TILE * D * 2;  // 16 KiB
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int sigma(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+__device__ __forceinline__ float exp2f_(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Physical byte offset of 16-byte chunk c of row r: "row" swizzle for
+// ds_read_b128 row reads, "tr" swizzle for the transposing reads.
+__device__ __forceinline__ int off_row(int r, int c) { return r * 256 + 16 * (c ^ (r & 15)); }
+__device__ __forceinline__ int off_tr(int r, int c) { return r * 256 + 16 * (c ^ (4 * (r & 3))); }
+
+// Per-lane read bases (see the forward kernel): row reads of half kb take row
+// sigma(col) + 32 kb, logical chunk 2 ks + h; transposing reads give the
+// 32 x 16 operand of d block db and row group t of half kb.
+struct Lanes {
+  int rd_row, rd_tr, h, col;
+  __device__ Lanes(int lane) {
+    h = lane >> 5;
+    col = lane & 31;
+    const int r = sigma(col), x = r & 15;
+    rd_row = r * 256 + 16 * (h ^ (x & 1)) + 32 * (x >> 1);  // ^ (32 ks)
+    const int g4 = lane >> 4, i = lane & 15;
+    const int hh = g4 >> 1, dgrp = g4 & 1, rho = i >> 2, b = (i & 3) >> 1, half = i & 1;
+    rd_tr = (8 * hh + rho) * 256 + 64 * rho + 32 * dgrp + 16 * b + 8 * half;  // ^ (64 db)
+  }
+};
+
+__device__ __forceinline__ bf16x8 row_operand(const uint8_t* tile, const Lanes& L, int kb, int ks) {
+  return *(const bf16x8*)(tile + kb * 32 * 256 + (L.rd_row ^ (32 * ks)));
+}
+__device__ __forceinline__ bf16x8 tr_operand(const uint8_t* tile, const Lanes& L, int kb, int t,
+                                             int db) {
+  const uint8_t* base = tile + kb * 32 * 256 + (L.rd_tr ^ (64 * db)) + t * 16 * 256;
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)base);
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 4 * 256));
+  // whole-vector assembly: element-wise __bf16 inserts were mis-lowered
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Global -> register half of the tile staging: rows [r0, r0 + 64) of a
+// [n][128] bf16 matrix, 4 chunks of 16 bytes per thread, zeros past n.  The
+// loads are issued one tile ahead and their latency hides behind the current
+// tile's MFMAs.
+__device__ __forceinline__ void fetch(const uint16_t* src, int r0, int n, u32x4 (&x)[4], int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = tid + THREADS * i;
+    const int r = id >> 4, c = id & 15;
+    x[i] = u32x4{0u, 0u, 0u, 0u};
+    if (r0 + r < n) x[i] = *(const u32x4*)(src + (size_t)(r0 + r) * D + c * 8);
+  }
+}
+
+// Register -> LDS half: one or two swizzled copies of the tile.
+__device__ __forceinline__ void put(const u32x4 (&x)[4], uint8_t* t_row, uint8_t* t_tr, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = tid + THREADS * i;
+    const int r = id >> 4, c = id & 15;
+    if (t_row) *(u32x4*)(t_row + off_row(r, c)) = x[i];
+    if (t_tr) *(u32x4*)(t_tr + off_tr(r, c)) = x[i];
+  }
+}
+
+// Register value r of half kb of an S^T or S accumulator belongs to tile row
+// 32 kb + 8 h + 16 (r / 8) + r % 8.
+__device__ __forceinline__ int acc_row(int kb, int h, int r) {
+  return 32 * kb + 8 * h + 16 * (r >> 3) + (r & 7);
+}
+
+__device__ __forceinline__ void pack(const f32x16& x, bf16x8 (&p)[2]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[t][e] = (__bf16)x[8 * t + e];
+}
+
+// Stores a 128-wide accumulator (O^T layout: 4 d blocks, lane column = row)
+// to row `row` of an fp32 [.][128] matrix, times `mul`, adding the old value
+// when ADD.
+template <bool ADD>
+__device__ __forceinline__ void store_rows(float* dst, const f32x16 (&acc)[4], int h, float mul) {
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * g + e] * mul;
+      float* p = dst + db * 32 + 8 * g + 4 * h;
+      if (ADD) x += *(const f32x4*)p;
+      *(f32x4*)p = x;
+    }
+}
+
+// The 16 values of a per-row (or per-key) LDS array that belong to the
+// accumulator registers of half kb: rows 32 kb + 8 h + {0..7, 16..23}.
+template <typename T4, typename E>
+__device__ __forceinline__ void read_half(const E* arr, int kb, int h, T4 (&x)[4]) {
+  const E* b = arr + 32 * kb + 8 * h;
+  x[0] = *(const T4*)(b);
+  x[1] = *(const T4*)(b + 4);
+  x[2] = *(const T4*)(b + 16);
+  x[3] = *(const T4*)(b + 20);
+}
+
+// Scheduling fence: the tile loops below are written in the order they
+// should issue (each MFMA with the LDS reads four MFMAs ahead and a slice of
+// the other half's VALU work) and the compiler keeps that order.
+#define RA_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+}  // namespace bwd
+}  // namespace ra

@@ -373,13 +373,24 @@ ra_status ra_backward_prep(const ra_problem* p, const float* out, const void* do
   return e == hipSuccess ? RA_OK : RA_ERR_HIP;
 }
 
+size_t ra_backward_workspace_bytes(const ra_problem* p) {
+  if (check_problem(p) != RA_OK || !fast_path(p)) return 0;
+  return ra::backward_ws_bytes(p->n_k, p->h_q, p->h_kv);
+}
+
 ra_status ra_backward_step(const ra_problem* p, const void* q, const int32_t* q_pos,
                            const void* k, const void* v, const int32_t* k_pos, const void* dout,
                            const float* lse, const float* delta, float* dq, float* dk, float* dv,
-                           void* stream) {
+                           void* workspace, size_t workspace_bytes, void* stream) {
   ra_status st = check_problem(p);
   if (st != RA_OK) return st;
   if (!fast_path(p)) return p->dtype != RA_BF16 ? RA_ERR_DTYPE : RA_ERR_SHAPE;
+  const size_t need = ra::backward_ws_bytes(p->n_k, p->h_q, p->h_kv);
+  if (need > 0 && p->n_k > 0) {
+    if (!workspace) return RA_ERR_NULL;
+    if (workspace_bytes < need) return RA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return RA_ERR_ALIGN;
+  }
   if (p->n_q > 0 && (!q || !q_pos || !dout || !lse || !delta || !dq)) return RA_ERR_NULL;
   if (p->n_k > 0 && (!k || !v || !k_pos || !dk || !dv)) return RA_ERR_NULL;
   if (p->n_q > 0 && (!aligned16(q) || !aligned4(q_pos) || !aligned16(dout) || !aligned4(lse) ||
@@ -407,6 +418,8 @@ ra_status ra_backward_step(const ra_problem* p, const void* q, const int32_t* q_
   a.h_q = p->h_q;
   a.h_kv = p->h_kv;
   a.causal = p->causal;
+  a.n_split = ra::backward_splits(p->n_k, p->h_q, p->h_kv);
+  a.ws = (float*)workspace;
   a.scale = softmax_scale(p);
   a.c2 = a.scale * 1.4426950408889634f;
   return ra::launch_backward(a, (hipStream_t)stream) == hipSuccess ? RA_OK : RA_ERR_HIP;

@@ -69,10 +69,15 @@ struct BwdArgs {
   float* dq;           // [h_q][n_q][128], accumulated
   float* dk;           // [h_kv][n_k][128], written
   float* dv;
-  int32_t n_q, n_k, h_q, h_kv, causal;
+  float* ws;           // [2][n_split][h_kv][n_k][128] partial sums when n_split > 1
+  int32_t n_q, n_k, h_q, h_kv, causal, n_split;
   float scale, c2;
 };
+// Splits of each head group in the dk/dv kernel, and the workspace they need.
+int backward_splits(int n_k, int h_q, int h_kv);
+size_t backward_ws_bytes(int n_k, int h_q, int h_kv);
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_backward_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_backward_delta(const float* out, const void* dout, float* delta, int64_t rows,
                                  hipStream_t stream);
 

@@ -143,7 +143,7 @@ def test_backward_checks():
     L = ra.lib()
     v = ctypes.c_void_p(FAKE)
     odd = ctypes.c_void_p(FAKE + 4)
-    step = lambda p, *ptrs: L.ra_backward_step(ctypes.byref(p), *ptrs, None)
+    step = lambda p, *ptrs: L.ra_backward_step(ctypes.byref(p), *ptrs, v, 1 << 40, None)
     full = [v] * 11
     # bfloat16 with d_k = 128 only
     assert step(good(dtype=ra.RA_F32), *full) == DTYPE
@@ -165,3 +165,13 @@ def test_backward_checks():
     assert L.ra_backward_prep(ctypes.byref(good()), None, v, v, None) == NULL
     assert L.ra_backward_prep(ctypes.byref(good()), v, odd, v, None) == ALIGN
     assert L.ra_backward_prep(ctypes.byref(good(n_q=0)), None, None, None, None) == OK
+    # a head group split across workgroups needs the workspace
+    p = good(n_k=8192, h_q=16, h_kv=1)
+    need = L.ra_backward_workspace_bytes(ctypes.byref(p))
+    assert need > 0 and need % (2 * 8192 * 128 * 4) == 0
+    assert L.ra_backward_workspace_bytes(ctypes.byref(good(n_k=8192, h_q=8, h_kv=8))) == 0
+    assert L.ra_backward_workspace_bytes(ctypes.byref(good(dtype=ra.RA_F32))) == 0
+    ws = lambda w, b: L.ra_backward_step(ctypes.byref(p), *full, w, b, None)
+    assert ws(None, need) == NULL
+    assert ws(v, need - 1) == WORKSPACE
+    assert ws(odd, need) == ALIGN
