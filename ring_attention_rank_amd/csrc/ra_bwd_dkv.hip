@@ -14,7 +14,7 @@ struct SmemKV {
   uint8_t g_row[TILE_BYTES];
   uint8_t g_tr[TILE_BYTES];
   int32_t pos[TILE];
-  float lse2[TILE];
+  float lse2[TILE];  // lse * log2(e); +inf where the row contributes nothing
   float delta[TILE];
   int32_t tile_ok;  // every query of the tile valid with a finite lse
 };
@@ -75,7 +75,10 @@ void dkv_kernel(const BwdArgs a) {
       const bool ok = iq < n_q;
       const size_t sr = (size_t)head * n_q + iq;
       ppos = ok ? (a.causal ? a.q_pos[iq] : 0x7ffffffe) : (int)0x80000000;
-      plse2 = ok ? a.lse[sr] * kLog2e : -INFINITY;
+      // log2-domain lse; +inf for rows past n_q and rows that saw no key, so
+      // that their probabilities come out as exp2(-inf) = 0
+      const float l = ok ? a.lse[sr] : -INFINITY;
+      plse2 = l != -INFINITY ? l * kLog2e : INFINITY;
       pdelta = ok ? a.delta[sr] : 0.f;
     }
   };
@@ -93,115 +96,103 @@ void dkv_kernel(const BwdArgs a) {
       sm.delta[tid] = pdelta;
     }
     if (wave == 0) {  // wave 0 holds the tile's 64 rows, one per lane
-      const bool ok = __builtin_amdgcn_ballot_w64(plse2 != -INFINITY) == ~0ull;
+      const bool ok = __builtin_amdgcn_ballot_w64(plse2 != INFINITY) == ~0ull;
       if (lane == 0) sm.tile_ok = ok ? 1 : 0;
     }
     if (i + 1 < total) fetch_tile(i + 1);
     __syncthreads();
-    // no mask when every query of the tile is valid with a finite lse and
-    // sees every key of the wave (the tile's first query and the wave's last
-    // key decide)
+    // no causal mask when every query of the tile is valid with a finite lse
+    // and sees every key of the wave (the tile's first query and the wave's
+    // last key decide)
     const bool full = __builtin_amdgcn_readfirstlane(sm.tile_ok) &&
                       kmax_w <= __builtin_amdgcn_readfirstlane(sm.pos[0]);
-    auto body = [&](auto masked) {
-      // A[qb][2 ks] = Q rows, A[qb][2 ks + 1] = dout rows of half qb;
-      // TG/TQ[qb][4 t + db] = transposed dout / Q for dV^T += dout^T P and
-      // dK^T += Q^T dS.
-      bf16x8 A[2][16], TG[2][8], TQ[2][8];
-      i32x4 pz[2][4];
-      f32x4 lz[2][4], dz[2][4];
-      f32x16 S[2] = {}, P[2] = {};
-      bf16x8 pp[2][2], ds[2][2];
-      auto rdA = [&](int qb, int i) {
-        A[qb][i] = row_operand((i & 1) ? sm.g_row : sm.q_row, L, qb, i >> 1);
-      };
-      auto rdT = [&](int qb, int i) {
-        const int j = i >> 1;
-        if (i & 1)
-          TQ[qb][j] = tr_operand(sm.q_tr, L, qb, j >> 2, j & 3);
-        else
-          TG[qb][j] = tr_operand(sm.g_tr, L, qb, j >> 2, j & 3);
-      };
-      // per-row values of accumulator registers 4 g .. 4 g + 3 of half qb
-      auto rd_grp = [&](int qb, int g) {
-        const int o = 32 * qb + 8 * L.h + 4 * (g & 1) + 16 * (g >> 1);
-        if constexpr (decltype(masked)::value) pz[qb][g] = *(const i32x4*)(sm.pos + o);
-        lz[qb][g] = *(const f32x4*)(sm.lse2 + o);
-        dz[qb][g] = *(const f32x4*)(sm.delta + o);
-      };
-      auto mA = [&](int qb, int i) {
-        if (i & 1)
-          P[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[qb][i], vr[i >> 1], P[qb], 0, 0, 0);
-        else
-          S[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[qb][i], kr[i >> 1], S[qb], 0, 0, 0);
-      };
-      auto mT = [&](int qb, int i) {
-        const int j = i >> 1;
-        if (i & 1)
-          dk[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TQ[qb][j], ds[qb][j >> 2], dk[j & 3],
-                                                              0, 0, 0);
-        else
-          dv[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TG[qb][j], pp[qb][j >> 2], dv[j & 3],
-                                                              0, 0, 0);
-      };
-      // p and ds of registers 2 j, 2 j + 1 of half qb, converted to bf16 as a
-      // pair
-      auto valu2 = [&](int qb, int j) {
+    // A[qb][2 ks] = Q rows, A[qb][2 ks + 1] = dout rows of half qb;
+    // TG/TQ[qb][4 t + db] = transposed dout / Q for dV^T += dout^T P and
+    // dK^T += Q^T dS.
+    bf16x8 A[2][16], TG[2][8], TQ[2][8];
+    i32x4 pz[2][4];
+    f32x4 lz[2][4], dz[2][4];
+    f32x16 S[2] = {}, P[2] = {};
+    bf16x8 pp[2][2], ds[2][2];
+    auto rdA = [&](int qb, int i) {
+      A[qb][i] = row_operand((i & 1) ? sm.g_row : sm.q_row, L, qb, i >> 1);
+    };
+    auto rdT = [&](int qb, int i) {
+      const int j = i >> 1;
+      if (i & 1)
+        TQ[qb][j] = tr_operand(sm.q_tr, L, qb, j >> 2, j & 3);
+      else
+        TG[qb][j] = tr_operand(sm.g_tr, L, qb, j >> 2, j & 3);
+    };
+    // per-row values of accumulator registers 4 g .. 4 g + 3 of half qb
+    auto rd_grp = [&](int qb, int g) {
+      const int o = 32 * qb + 8 * L.h + 4 * (g & 1) + 16 * (g >> 1);
+      pz[qb][g] = *(const i32x4*)(sm.pos + o);
+      lz[qb][g] = *(const f32x4*)(sm.lse2 + o);
+      dz[qb][g] = *(const f32x4*)(sm.delta + o);
+    };
+    auto mA = [&](int qb, int i) {
+      if (i & 1)
+        P[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[qb][i], vr[i >> 1], P[qb], 0, 0, 0);
+      else
+        S[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[qb][i], kr[i >> 1], S[qb], 0, 0, 0);
+    };
+    auto mT = [&](int qb, int i) {
+      const int j = i >> 1;
+      if (i & 1)
+        dk[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TQ[qb][j], ds[qb][j >> 2], dk[j & 3],
+                                                            0, 0, 0);
+      else
+        dv[j & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(TG[qb][j], pp[qb][j >> 2], dv[j & 3],
+                                                            0, 0, 0);
+    };
+    // p and ds of registers 2 j, 2 j + 1 of half qb, converted to bf16 as a
+    // pair
+    auto valu2 = [&](int qb, int j) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = 2 * j + u;
-          const float l2 = lz[qb][r >> 2][r & 3];
-          float p;
-          if constexpr (decltype(masked)::value) {
-            // rows past n_q and rows that saw no key have lse = -inf: p = 0
-            const bool vis = kp <= pz[qb][r >> 2][r & 3] && l2 != -INFINITY;
-            p = vis ? exp2f_(__builtin_fmaf(S[qb][r], a.c2, -l2)) : 0.f;
-          } else {
-            p = exp2f_(__builtin_fmaf(S[qb][r], a.c2, -l2));
-          }
-          pp[qb][r >> 3][r & 7] = (__bf16)p;
-          ds[qb][r >> 3][r & 7] = (__bf16)(p * (P[qb][r] - dz[qb][r >> 2][r & 3]));
-        }
-      };
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rdA(0, i);
-      rd_grp(0, 0);
-      RA_FENCE();
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {  // S, dP of half 0
-        mA(0, i);
-        if (i + 4 < 16) rdA(0, i + 4); else rdA(1, i - 12);
-        RA_FENCE();
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {  // S, dP of half 1; P, dS of half 0
-        mA(1, i);
-        if (i + 4 < 16) rdA(1, i + 4); else rdT(0, i - 12);
-        if ((i & 3) == 1) {  // starting row group i / 4: fetch the next one
-          if (i < 12) rd_grp(0, (i >> 2) + 1); else rd_grp(1, 0);
-        }
-        if (i & 1) valu2(0, i >> 1);
-        RA_FENCE();
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {  // dV, dK from half 0; P, dS of half 1
-        mT(0, i);
-        if (i + 4 < 16) rdT(0, i + 4); else rdT(1, i - 12);
-        if ((i & 3) == 1 && i < 12) rd_grp(1, (i >> 2) + 1);
-        if (i & 1) valu2(1, i >> 1);
-        RA_FENCE();
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {  // dV, dK from half 1
-        mT(1, i);
-        if (i + 4 < 16) rdT(1, i + 4);
-        RA_FENCE();
+      for (int u = 0; u < 2; ++u) {
+        const int r = 2 * j + u;
+        // rows past n_q and rows that saw no key carry l2 = +inf: p = 0
+        float p = exp2f_(__builtin_fmaf(S[qb][r], a.c2, -lz[qb][r >> 2][r & 3]));
+        if (!full && kp > pz[qb][r >> 2][r & 3]) p = 0.f;
+        pp[qb][r >> 3][r & 7] = (__bf16)p;
+        ds[qb][r >> 3][r & 7] = (__bf16)(p * (P[qb][r] - dz[qb][r >> 2][r & 3]));
       }
     };
-    if (full)
-      body(std::false_type{});
-    else
-      body(std::true_type{});
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rdA(0, i);
+    rd_grp(0, 0);
+    RA_FENCE();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {  // S, dP of half 0
+      mA(0, i);
+      if (i + 4 < 16) rdA(0, i + 4); else rdA(1, i - 12);
+      RA_FENCE();
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {  // S, dP of half 1; P, dS of half 0
+      mA(1, i);
+      if (i + 4 < 16) rdA(1, i + 4); else rdT(0, i - 12);
+      if ((i & 3) == 1) {  // starting row group i / 4: fetch the next one
+        if (i < 12) rd_grp(0, (i >> 2) + 1); else rd_grp(1, 0);
+      }
+      if (i & 1) valu2(0, i >> 1);
+      RA_FENCE();
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {  // dV, dK from half 0; P, dS of half 1
+      mT(0, i);
+      if (i + 4 < 16) rdT(0, i + 4); else rdT(1, i - 12);
+      if ((i & 3) == 1 && i < 12) rd_grp(1, (i >> 2) + 1);
+      if (i & 1) valu2(1, i >> 1);
+      RA_FENCE();
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {  // dV, dK from half 1
+      mT(1, i);
+      if (i + 4 < 16) rdT(1, i + 4);
+      RA_FENCE();
+    }
   }
   if (kv) {
     float* ddk = a.dk;
