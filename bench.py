@@ -136,6 +136,45 @@ def cpu_baseline(case, share, out, lse, budget_rows):
     }
 
 
+def time_backward(share, fwd, fwd_flops, steps, warmup, rank):
+    """One backward step of the share: delta = rowsum(dout * out), then one
+    block step per key/value block (dq accumulated, dk and dv per block).
+    Its algorithmic flops are five GEMMs over the visible pairs (S, dP, dQ,
+    dK, dV), 2.5 times the forward's; the dq kernel recomputes S and dP, which
+    is not counted."""
+    g = torch.Generator(device="cuda").manual_seed(2024)
+    q, gk = share["gq"], share["gk"]
+    dout = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
+    out, lse = fwd.out, fwd.lse
+    delta = torch.empty(lse.shape, dtype=torch.float32, device="cuda")
+    dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dks = [torch.empty(k.shape, dtype=torch.float32, device="cuda") for k in gk]
+    dvs = [torch.empty(k.shape, dtype=torch.float32, device="cuda") for k in gk]
+    need = max(ra.backward_workspace_bytes(ra._problem_from(q, k, True, None)) for k in gk)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        ra.backward_prep(out, dout, delta)
+        dq.zero_()
+        for b in range(len(gk)):
+            ra.backward_step(q, share["gq_pos"], gk[b], share["gv"][b], share["gk_pos"][b], dout,
+                             lse, delta, dq, dks[b], dvs[b], workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    flops = 2.5 * fwd_flops
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "ms_per_step": dt * 1e3,
+            "pct_of_bf16_peak": 100.0 * flops / dt / 1e12 / PEAK_BF16_TFLOPS,
+            "flops_per_step": flops, "flops_counted": "S, dP, dQ, dK, dV over visible pairs",
+            "launches_per_step": 2 + len(gk) * (3 if need else 2), "rank": rank}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +188,8 @@ def main():
     ap.add_argument("--no-side-stream", action="store_true")
     ap.add_argument("--no-allgather", action="store_true",
                     help="skip timing the all-gather form (every block resident, one launch)")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing the backward of the share (bf16, d_k = 128)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -261,6 +302,8 @@ def main():
             "launches_per_step": 1 if case.dtype == "bf16" and case.d_k == 128 else case.n_cp,
             "rank": ranks[-1],
         }
+    if not args.no_backward and case.dtype == "bf16" and case.d_k == 128:
+        result["backward"] = time_backward(share, fwd, flops, args.steps, args.warmup, ranks[-1])
     if not args.no_cpu_baseline and len(ranks) >= 1:
         out, lse = fwd.out, fwd.lse
         result["cpu_baseline"] = cpu_baseline(case, share, out, lse, args.cpu_rows)

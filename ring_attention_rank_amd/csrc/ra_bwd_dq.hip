@@ -18,15 +18,19 @@
 //    the A operands), dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T (K read
 //    transposed, dS^T packed to bf16 as the B operand straight from the
 //    accumulators, as P^T feeds V^T P^T in the forward).
-//  * dk/dv kernel: the mirror image.  A wave owns 32 keys (K and V rows in
-//    registers) and walks every query head of its key/value head and the
-//    64-query tiles that see those keys: S = Q K^T and dP = dout V^T (Q and
-//    dout rows the A operands), dS = P (dP - delta), dV^T += dout^T P and
-//    dK^T += Q^T dS (dout and Q read transposed).
+//  * dk/dv kernel (ra_bwd_dkv.hip): the mirror image.  A wave owns 32 keys
+//    (K and V rows in registers) and walks the query heads of its split of
+//    the key/value head's group and the 64-query tiles that see those keys:
+//    S = Q K^T and dP = dout V^T (Q and dout rows the A operands),
+//    dS = P (dP - delta), dV^T += dout^T P and dK^T += Q^T dS (dout and Q
+//    read transposed).
 //
-// One wave per SIMD (up to 512 registers); tiles are staged through LDS with
-// ordinary loads, in two XOR swizzles per tensor (one for row reads, one for
-// the transposing ds_read_b64_tr_b16 reads), both free of bank conflicts.
+// One wave per SIMD (up to 512 registers).  Each 64-row tile is loaded into
+// registers one tile ahead, then written to LDS in two XOR swizzles per
+// tensor (one for row reads, one for the transposing ds_read_b64_tr_b16
+// reads), both free of bank conflicts.  Inside a tile the instructions are
+// fenced in issue order: every MFMA goes out with the LDS operand reads four
+// MFMAs ahead and a slice of the other half-tile's VALU work.
 //
 // This unit: the dq kernel and delta = rowsum(dout * out).  Its MFMA
 // accumulators live in ordinary VGPRs (built with the VGPR form), so the
