@@ -138,7 +138,7 @@ def cpu_baseline(case, share, out, lse, budget_rows):
 
 def time_backward(share, fwd, fwd_flops, steps, warmup, rank):
     """One backward step of the share: delta = rowsum(dout * out), then one
-    block step per key/value block (dq accumulated, dk and dv per block).
+    block step per key/value block (dq, and each block's dk and dv, accumulated).
     Its algorithmic flops are five GEMMs over the visible pairs (S, dP, dQ,
     dK, dV), 2.5 times the forward's; the dq kernel recomputes S and dP, which
     is not counted."""
@@ -148,8 +148,10 @@ def time_backward(share, fwd, fwd_flops, steps, warmup, rank):
     out, lse = fwd.out, fwd.lse
     delta = torch.empty(lse.shape, dtype=torch.float32, device="cuda")
     dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
-    dks = [torch.empty(k.shape, dtype=torch.float32, device="cuda") for k in gk]
-    dvs = [torch.empty(k.shape, dtype=torch.float32, device="cuda") for k in gk]
+    # dk and dv accumulate (the travelling gradients of the ring); the timed
+    # steps keep adding to these buffers
+    dks = [torch.zeros(k.shape, dtype=torch.float32, device="cuda") for k in gk]
+    dvs = [torch.zeros(k.shape, dtype=torch.float32, device="cuda") for k in gk]
     need = max(ra.backward_workspace_bytes(ra._problem_from(q, k, True, None)) for k in gk)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
 

@@ -163,11 +163,13 @@ ra_status ra_forward_allgather(const ra_problem* p, int32_t n_cp, const void* q,
  *
  * ra_backward_prep: delta[h_q][n_q] (fp32) from out[h_q][n_q][d_k] (fp32, the
  * forward's output) and dout[h_q][n_q][d_k] (bf16).
- * ra_backward_step: one key/value block.  dq[h_q][n_q][d_k] (fp32) is
- * ACCUMULATED (+= scale * sum_j ds k_j; zero it before the first block);
- * dk, dv[h_kv][n_k][d_k] (fp32) are OVERWRITTEN with this block's gradients
- * (dk = scale * sum_i ds q_i, dv = sum_i p dout_i, summed over the query heads
- * that read each key/value head).  q, k, v, dout 16-byte aligned, as the
+ * ra_backward_step: one key/value block.  All three gradients are
+ * ACCUMULATED: dq[h_q][n_q][d_k] (fp32) += scale * sum_j ds k_j (zero it
+ * before the first block); dk, dv[h_kv][n_k][d_k] (fp32) += this rank's part
+ * of the block's gradients, dk = scale * sum_i ds q_i and dv = sum_i p dout_i,
+ * summed over the query heads that read each key/value head (pass zeros for a
+ * block's own gradients, or the block's travelling gradients received from
+ * the ring neighbour).  q, k, v, dout 16-byte aligned, as the
  * forward's; dq, dk, dv 16-byte aligned.  When few key/value heads leave the
  * dk/dv grid small, the query heads of each group are split across
  * workgroups: each split writes partial sums into the caller's workspace

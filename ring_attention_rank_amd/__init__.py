@@ -296,14 +296,15 @@ def backward_workspace_bytes(p):
 
 def backward_step(q, q_pos, k, v, k_pos, dout, lse, delta, dq, dk=None, dv=None, causal=True,
                   scale=None, stream=None, workspace=None):
-    """One key/value block of the backward: adds this block's part to ``dq``
-    (fp32, in place) and returns (dk, dv), fp32 ``[h_kv][n_k][d_k]``.
-    ``workspace`` is a uint8 device tensor of at least
-    ``backward_workspace_bytes`` bytes (allocated here when None)."""
+    """One key/value block of the backward: adds this block's part to ``dq``,
+    ``dk`` and ``dv`` (fp32, in place; dk and dv are zero-filled here when
+    None) and returns (dk, dv), fp32 ``[h_kv][n_k][d_k]``.  ``workspace`` is a
+    uint8 device tensor of at least ``backward_workspace_bytes`` bytes
+    (allocated here when None)."""
     if dk is None:
-        dk = torch.empty(k.shape, dtype=torch.float32, device=k.device)
+        dk = torch.zeros(k.shape, dtype=torch.float32, device=k.device)
     if dv is None:
-        dv = torch.empty(v.shape, dtype=torch.float32, device=v.device)
+        dv = torch.zeros(v.shape, dtype=torch.float32, device=v.device)
     _need_gpu(q, q_pos, k, v, k_pos, dout, lse, delta, dq, dk, dv, workspace)
     p = _problem_from(q, k, causal, scale)
     if workspace is None:

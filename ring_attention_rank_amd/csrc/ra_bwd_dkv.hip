@@ -22,7 +22,7 @@ struct SmemKV {
 // dk/dv kernel: one workgroup = 128 keys of one key/value head and one split
 // of the query heads that read it; grid (n_kt128, h_kv * n_split).  Walks the
 // split's heads and, per head, the query tiles that see these keys.  With one
-// split it writes dk, dv; with several, each split writes its partial sums
+// split it adds to dk, dv; with several, each split writes its partial sums
 // to the workspace and a reduction adds them in a fixed order.
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dkv_kernel(const BwdArgs a) {
@@ -202,12 +202,17 @@ void dkv_kernel(const BwdArgs a) {
       ddk = a.ws + (size_t)split * part;
       ddv = a.ws + (size_t)(n_split + split) * part;
     }
-    store_rows<false>(ddk + skey * D, dk, L.h, a.scale);
-    store_rows<false>(ddv + skey * D, dv, L.h, 1.f);
+    if (n_split > 1) {
+      store_rows<false>(ddk + skey * D, dk, L.h, a.scale);
+      store_rows<false>(ddv + skey * D, dv, L.h, 1.f);
+    } else {  // added to the caller's (travelling) dk, dv
+      store_rows<true>(ddk + skey * D, dk, L.h, a.scale);
+      store_rows<true>(ddv + skey * D, dv, L.h, 1.f);
+    }
   }
 }
 
-// dk, dv = sums of the splits' partials, split 0 first.
+// dk, dv += sums of the splits' partials, split 0 first.
 __global__ __launch_bounds__(256) void reduce_kernel(const float* ws, float* dk, float* dv,
                                                      int64_t n4, int n_split) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -218,8 +223,9 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* ws, float* dk,
     sk += w[(int64_t)s * n4 + i];
     sv += w[(int64_t)(n_split + s) * n4 + i];
   }
-  ((f32x4*)dk)[i] = sk;
-  ((f32x4*)dv)[i] = sv;
+  // the block's part is summed first, then added once to the caller's value
+  ((f32x4*)dk)[i] = ((const f32x4*)dk)[i] + sk;
+  ((f32x4*)dv)[i] = ((const f32x4*)dv)[i] + sv;
 }
 
 }  // namespace bwd

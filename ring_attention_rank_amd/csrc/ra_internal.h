@@ -54,8 +54,8 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d_k, bool read, bool fi
                        hipStream_t stream);
 // bfloat16, d_k = 128: the 8-wave kernel with direct-to-LDS staging.
 hipError_t launch_step_fast(const StepArgs& a, bool read, bool final_, hipStream_t stream);
-// Backward of one key/value block (bfloat16, d_k = 128): dq += this block's
-// part, dk and dv = this block's gradients (fp32, summed over the query heads
+// Backward of one key/value block (bfloat16, d_k = 128): dq, dk and dv
+// (fp32) each get this block's part added (dk, dv summed over the query heads
 // of each key/value head).
 struct BwdArgs {
   const void* q;
@@ -67,7 +67,7 @@ struct BwdArgs {
   const float* lse;    // [h_q][n_q], natural log, from the forward
   const float* delta;  // [h_q][n_q] = rowsum(dout * out)
   float* dq;           // [h_q][n_q][128], accumulated
-  float* dk;           // [h_kv][n_k][128], written
+  float* dk;           // [h_kv][n_k][128], accumulated
   float* dv;
   float* ws;           // [2][n_split][h_kv][n_k][128] partial sums when n_split > 1
   int32_t n_q, n_k, h_q, h_kv, causal, n_split;

@@ -164,7 +164,7 @@ def test_empty_sides():
     dk, dv = ra.backward_step(sh.gq, sh.gq_pos, k0, k0, kp0, gdout, g(lse32), delta, dq)
     torch.cuda.synchronize()
     assert torch.all(dq == 0.25) and dk.numel() == 0 and dv.numel() == 0
-    # no queries: dk and dv are zero
+    # no queries: dk and dv keep what they held
     q0 = sh.gq[:, :0].contiguous()
     e = torch.empty((4, 0), dtype=torch.float32, device="cuda")
     dq0 = torch.empty((4, 0, 128), dtype=torch.float32, device="cuda")
@@ -173,7 +173,33 @@ def test_empty_sides():
     ra.backward_step(q0, sh.gq_pos[:0].contiguous(), sh.gk[0], sh.gv[0], sh.gk_pos[0],
                      gdout[:, :0].contiguous(), e, e, dq0, dk, dv)
     torch.cuda.synchronize()
-    assert torch.all(dk == 0) and torch.all(dv == 0)
+    assert torch.all(dk == 7.0) and torch.all(dv == 7.0)
+
+
+@pytest.mark.parametrize("h_q,h_kv,n_k", [(4, 2, 200), (16, 1, 256)])
+def test_dk_dv_accumulate(h_q, h_kv, n_k):
+    """dk and dv are added to what the caller passes (the travelling
+    gradients of the ring), with and without the head-group split."""
+    rng = np.random.default_rng(h_q * 31 + n_k)
+    sh = _custom_share(rng, "bf16", 128, h_q, h_kv, 160, n_k, 1)
+    out32, lse32, dout = fwd_inputs(sh)
+    g = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    gdout = g(dout).to(torch.bfloat16)
+    delta = ra.backward_prep(g(out32), gdout)
+    p = ra._problem_from(sh.gq, sh.gk[0], True, None)
+    print(f"[backward] accumulate h{h_q}/{h_kv} nk{n_k} workspace "
+          f"{ra.backward_workspace_bytes(p)}", flush=True)
+    dq = torch.zeros(sh.gq.shape, dtype=torch.float32, device="cuda")
+    dk0, dv0 = ra.backward_step(sh.gq, sh.gq_pos, sh.gk[0], sh.gv[0], sh.gk_pos[0], gdout,
+                                g(lse32), delta, dq)
+    base_k = torch.from_numpy(rng.standard_normal(dk0.shape).astype(np.float32)).cuda()
+    base_v = torch.from_numpy(rng.standard_normal(dv0.shape).astype(np.float32)).cuda()
+    dk, dv = base_k.clone(), base_v.clone()
+    ra.backward_step(sh.gq, sh.gq_pos, sh.gk[0], sh.gv[0], sh.gk_pos[0], gdout, g(lse32), delta,
+                     torch.zeros_like(dq), dk, dv)
+    torch.cuda.synchronize()
+    # one float32 addition per element, in the kernel as here
+    assert torch.equal(dk, base_k + dk0) and torch.equal(dv, base_v + dv0)
 
 
 def test_unsupported_shapes_refused():
