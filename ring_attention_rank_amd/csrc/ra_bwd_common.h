@@ -80,6 +80,16 @@ __device__ __forceinline__ void fetch(const uint16_t* src, int r0, int n, u32x4 
   }
 }
 
+// Register -> LDS, one chunk: the i-th 16-byte chunk a thread holds, into
+// one or two swizzled copies of the tile.
+__device__ __forceinline__ void put_one(const u32x4& x, uint8_t* t_row, uint8_t* t_tr, int tid,
+                                        int i) {
+  const int id = tid + THREADS * i;
+  const int r = id >> 4, c = id & 15;
+  if (t_row) *(u32x4*)(t_row + off_row(r, c)) = x;
+  if (t_tr) *(u32x4*)(t_tr + off_tr(r, c)) = x;
+}
+
 // Register -> LDS half: one or two swizzled copies of the tile.
 __device__ __forceinline__ void put(const u32x4 (&x)[4], uint8_t* t_row, uint8_t* t_tr, int tid) {
 #pragma unroll

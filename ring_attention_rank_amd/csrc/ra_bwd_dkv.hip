@@ -8,7 +8,9 @@
 namespace ra {
 namespace bwd {
 
-struct SmemKV {
+// 1024-byte aligned: the second buffer keeps the 16-byte chunk alignment and
+// the bank mapping of the swizzles.
+struct __attribute__((aligned(1024))) TileKV {
   uint8_t q_row[TILE_BYTES];
   uint8_t q_tr[TILE_BYTES];
   uint8_t g_row[TILE_BYTES];
@@ -17,6 +19,11 @@ struct SmemKV {
   float lse2[TILE];  // lse * log2(e); +inf where the row contributes nothing
   float delta[TILE];
   int32_t tile_ok;  // every query of the tile valid with a finite lse
+};
+// Two tile buffers: tile i is read from t[i & 1] while tile i + 1 is written
+// into the other one, slice by slice between the MFMAs.
+struct SmemKV {
+  TileKV t[2];
 };
 
 // dk/dv kernel: one workgroup = 128 keys of one key/value head and one split
@@ -82,30 +89,46 @@ void dkv_kernel(const BwdArgs a) {
       pdelta = ok ? a.delta[sr] : 0.f;
     }
   };
-  if (total > 0) fetch_tile(0);
+  // slice w (0..16) of the registered tile into buffer b: Q and dout chunks
+  // (row and transposing copies), then the per-row values and the tile flag
+  auto put_slice = [&](TileKV& b, int w) {
+    if (w < 16) {
+      const u32x4& x = (w < 8) ? pq[(w & 7) >> 1] : pg[(w & 7) >> 1];
+      uint8_t* row = (w < 8) ? b.q_row : b.g_row;
+      uint8_t* tr = (w < 8) ? b.q_tr : b.g_tr;
+      put_one(x, (w & 1) ? nullptr : row, (w & 1) ? tr : nullptr, tid, (w & 7) >> 1);
+    } else {
+      if (tid < TILE) {
+        b.pos[tid] = ppos;
+        b.lse2[tid] = plse2;
+        b.delta[tid] = pdelta;
+      }
+      if (wave == 0) {  // wave 0 holds the tile's 64 rows, one per lane
+        const bool ok = __builtin_amdgcn_ballot_w64(plse2 != INFINITY) == ~0ull;
+        if (lane == 0) b.tile_ok = ok ? 1 : 0;
+      }
+    }
+  };
   f32x16 dk[4] = {}, dv[4] = {};
   const int kmax_w = __builtin_amdgcn_readlane(kp, 31);  // lane 31 holds the wave's last key
+  if (total > 0) {
+    fetch_tile(0);
+#pragma unroll
+    for (int w = 0; w < 17; ++w) put_slice(sm.t[0], w);
+    // a tile index past the split's last maps to another head: never fetched
+    if (total > 1) fetch_tile(1);
+  }
+  __syncthreads();
 
-  for (int i = 0; i < total; ++i) {
-    __syncthreads();
-    put(pq, sm.q_row, sm.q_tr, tid);
-    put(pg, sm.g_row, sm.g_tr, tid);
-    if (tid < TILE) {
-      sm.pos[tid] = ppos;
-      sm.lse2[tid] = plse2;
-      sm.delta[tid] = pdelta;
-    }
-    if (wave == 0) {  // wave 0 holds the tile's 64 rows, one per lane
-      const bool ok = __builtin_amdgcn_ballot_w64(plse2 != INFINITY) == ~0ull;
-      if (lane == 0) sm.tile_ok = ok ? 1 : 0;
-    }
-    if (i + 1 < total) fetch_tile(i + 1);
-    __syncthreads();
+  for (int i_tile = 0; i_tile < total; ++i_tile) {
+    TileKV& cur = sm.t[i_tile & 1];
+    TileKV& nxt = sm.t[(i_tile + 1) & 1];  // last read by the previous tile, before the barrier
+    const bool more = i_tile + 2 < total;
     // no causal mask when every query of the tile is valid with a finite lse
     // and sees every key of the wave (the tile's first query and the wave's
     // last key decide)
-    const bool full = __builtin_amdgcn_readfirstlane(sm.tile_ok) &&
-                      kmax_w <= __builtin_amdgcn_readfirstlane(sm.pos[0]);
+    const bool full = __builtin_amdgcn_readfirstlane(cur.tile_ok) &&
+                      kmax_w <= __builtin_amdgcn_readfirstlane(cur.pos[0]);
     // A[qb][2 ks] = Q rows, A[qb][2 ks + 1] = dout rows of half qb;
     // TG/TQ[qb][4 t + db] = transposed dout / Q for dV^T += dout^T P and
     // dK^T += Q^T dS.
@@ -115,21 +138,21 @@ void dkv_kernel(const BwdArgs a) {
     f32x16 S[2] = {}, P[2] = {};
     bf16x8 pp[2][2], ds[2][2];
     auto rdA = [&](int qb, int i) {
-      A[qb][i] = row_operand((i & 1) ? sm.g_row : sm.q_row, L, qb, i >> 1);
+      A[qb][i] = row_operand((i & 1) ? cur.g_row : cur.q_row, L, qb, i >> 1);
     };
     auto rdT = [&](int qb, int i) {
       const int j = i >> 1;
       if (i & 1)
-        TQ[qb][j] = tr_operand(sm.q_tr, L, qb, j >> 2, j & 3);
+        TQ[qb][j] = tr_operand(cur.q_tr, L, qb, j >> 2, j & 3);
       else
-        TG[qb][j] = tr_operand(sm.g_tr, L, qb, j >> 2, j & 3);
+        TG[qb][j] = tr_operand(cur.g_tr, L, qb, j >> 2, j & 3);
     };
     // per-row values of accumulator registers 4 g .. 4 g + 3 of half qb
     auto rd_grp = [&](int qb, int g) {
       const int o = 32 * qb + 8 * L.h + 4 * (g & 1) + 16 * (g >> 1);
-      pz[qb][g] = *(const i32x4*)(sm.pos + o);
-      lz[qb][g] = *(const f32x4*)(sm.lse2 + o);
-      dz[qb][g] = *(const f32x4*)(sm.delta + o);
+      pz[qb][g] = *(const i32x4*)(cur.pos + o);
+      lz[qb][g] = *(const f32x4*)(cur.lse2 + o);
+      dz[qb][g] = *(const f32x4*)(cur.delta + o);
     };
     auto mA = [&](int qb, int i) {
       if (i & 1)
@@ -164,15 +187,18 @@ void dkv_kernel(const BwdArgs a) {
     rd_grp(0, 0);
     RA_FENCE();
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {  // S, dP of half 0
+    for (int i = 0; i < 16; ++i) {  // S, dP of half 0; tile i + 1 into the other buffer
       mA(0, i);
       if (i + 4 < 16) rdA(0, i + 4); else rdA(1, i - 12);
+      put_slice(nxt, i);
       RA_FENCE();
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {  // S, dP of half 1; P, dS of half 0
       mA(1, i);
       if (i + 4 < 16) rdA(1, i + 4); else rdT(0, i - 12);
+      if (i == 0) put_slice(nxt, 16);
+      if (i == 1 && more) fetch_tile(i_tile + 2);
       if ((i & 3) == 1) {  // starting row group i / 4: fetch the next one
         if (i < 12) rd_grp(0, (i >> 2) + 1); else rd_grp(1, 0);
       }
@@ -193,6 +219,7 @@ void dkv_kernel(const BwdArgs a) {
       if (i + 4 < 16) rdT(1, i + 4);
       RA_FENCE();
     }
+    __syncthreads();  // tile i + 1 is in place; tile i's buffer is free
   }
   if (kv) {
     float* ddk = a.dk;

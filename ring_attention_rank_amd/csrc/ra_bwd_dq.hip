@@ -40,11 +40,18 @@
 namespace ra {
 namespace bwd {
 
-struct SmemQ {
+// 1024-byte aligned: the second buffer keeps the 16-byte chunk alignment and
+// the bank mapping of the swizzles.
+struct __attribute__((aligned(1024))) TileQ {
   uint8_t k_row[TILE_BYTES];
   uint8_t k_tr[TILE_BYTES];
   uint8_t v_row[TILE_BYTES];
   int32_t pos[TILE];
+};
+// Two tile buffers: tile j is read from t[j & 1] while tile j + 1 is written
+// into the other one, slice by slice between the MFMAs.
+struct SmemQ {
+  TileQ t[2];
 };
 
 // dq kernel: one workgroup = 128 query rows of one head; grid (n_qt, h_q).
@@ -102,21 +109,34 @@ void dq_kernel(const BwdArgs a) {
       ppos = gk < n_k ? (a.causal ? a.k_pos[gk] : (int)0x80000000) : 0x7fffffff;
     }
   };
-  if (n_iter > 0) fetch_tile(0);
+  // slice w (0..12) of the registered tile into buffer b: K chunks (row and
+  // transposing copies), then V chunks, then the key positions
+  auto put_slice = [&](TileQ& b, int w) {
+    if (w < 8) {
+      put_one(pk[w >> 1], (w & 1) ? nullptr : b.k_row, (w & 1) ? b.k_tr : nullptr, tid, w >> 1);
+    } else if (w < 12) {
+      put_one(pv[w - 8], b.v_row, nullptr, tid, w - 8);
+    } else if (tid < TILE) {
+      b.pos[tid] = ppos;
+    }
+  };
   f32x16 dq[4] = {};
   const bool wave_ok = __builtin_amdgcn_ballot_w64(!(rv && seen)) == 0;
   const int qmin = __builtin_amdgcn_readfirstlane(qp);  // lane 0 holds the wave's first row
+  if (n_iter > 0) {
+    fetch_tile(0);
+#pragma unroll
+    for (int w = 0; w < 13; ++w) put_slice(sm.t[0], w);
+    fetch_tile(1);  // past the last key tile every load is guarded off
+  }
+  __syncthreads();
 
   for (int j = 0; j < n_iter; ++j) {
-    __syncthreads();  // the previous tile's reads are done
-    put(pk, sm.k_row, sm.k_tr, tid);
-    put(pv, sm.v_row, nullptr, tid);
-    if (tid < TILE) sm.pos[tid] = ppos;
-    if (j + 1 < n_iter) fetch_tile(j + 1);
-    __syncthreads();
+    TileQ& cur = sm.t[j & 1];
+    TileQ& nxt = sm.t[(j + 1) & 1];  // last read by tile j - 1, before the barrier
     // no mask when every row of the wave is valid, saw some key, and sees the
     // whole tile (positions increase, so the tile's last key decides)
-    const bool full = wave_ok && __builtin_amdgcn_readfirstlane(sm.pos[TILE - 1]) <= qmin;
+    const bool full = wave_ok && __builtin_amdgcn_readfirstlane(cur.pos[TILE - 1]) <= qmin;
     auto body = [&](auto masked) {
       // A[kb][2 ks] = K rows, A[kb][2 ks + 1] = V rows of half kb; T[kb][4 t + db]
       // = transposed K for dQ^T += K^T dS^T.
@@ -126,9 +146,9 @@ void dq_kernel(const BwdArgs a) {
       float X[2][16];
       bf16x8 ds[2][2];
       auto rdA = [&](int kb, int i) {
-        A[kb][i] = row_operand((i & 1) ? sm.v_row : sm.k_row, L, kb, i >> 1);
+        A[kb][i] = row_operand((i & 1) ? cur.v_row : cur.k_row, L, kb, i >> 1);
       };
-      auto rdT = [&](int kb, int i) { T[kb][i] = tr_operand(sm.k_tr, L, kb, i >> 2, i & 3); };
+      auto rdT = [&](int kb, int i) { T[kb][i] = tr_operand(cur.k_tr, L, kb, i >> 2, i & 3); };
       auto mA = [&](int kb, int i) {
         if (i & 1)
           P[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[kb][i], dout[i >> 1], P[kb], 0, 0, 0);
@@ -150,23 +170,25 @@ void dq_kernel(const BwdArgs a) {
         X[kb][r] = p * (P[kb][r] - delta);
       };
       auto pack_ds = [&](int kb) {
-  #pragma unroll
+#pragma unroll
         for (int t = 0; t < 2; ++t)
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 8; ++e) ds[kb][t][e] = (__bf16)X[kb][8 * t + e];
       };
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < 4; ++i) rdA(0, i);
-      read_half(sm.pos, 0, L.h, pz[0]);
-      read_half(sm.pos, 1, L.h, pz[1]);
+      read_half(cur.pos, 0, L.h, pz[0]);
+      read_half(cur.pos, 1, L.h, pz[1]);
       RA_FENCE();
-  #pragma unroll
-      for (int i = 0; i < 16; ++i) {  // S, dP of half 0
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {  // S, dP of half 0; tile j + 1 into the other buffer
         mA(0, i);
         if (i + 4 < 16) rdA(0, i + 4); else rdA(1, i - 12);
+        if (i < 13) put_slice(nxt, i);
+        if (i == 13) fetch_tile(j + 2);
         RA_FENCE();
       }
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < 16; ++i) {  // S, dP of half 1; dS of half 0
         mA(1, i);
         if (i + 4 < 16) rdA(1, i + 4); else rdT(0, i - 12);
@@ -174,7 +196,7 @@ void dq_kernel(const BwdArgs a) {
         RA_FENCE();
       }
       pack_ds(0);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < 8; ++i) {  // dQ from half 0; dS of half 1
         mT(0, i);
         if (i + 4 < 8) rdT(0, i + 4); else rdT(1, i - 4);
@@ -183,7 +205,7 @@ void dq_kernel(const BwdArgs a) {
         RA_FENCE();
       }
       pack_ds(1);
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < 8; ++i) {  // dQ from half 1
         mT(1, i);
         if (i + 4 < 8) rdT(1, i + 4);
@@ -194,6 +216,7 @@ void dq_kernel(const BwdArgs a) {
       body(std::false_type{});
     else
       body(std::true_type{});
+    __syncthreads();  // tile j + 1 is in place; tile j's buffer is free
   }
   if (rv) store_rows<true>(a.dq + srow * D, dq, L.h, a.scale);
 }
