@@ -80,6 +80,22 @@ __device__ __forceinline__ void fetch(const uint16_t* src, int r0, int n, u32x4 
   }
 }
 
+// XCD-aware split of a one-dimensional grid of n_x * n_y workgroups into
+// (x, y).  Workgroup L runs on XCD L % 8 (8 XCDs, each with its own L2); when
+// n_y is a multiple of 8, XCD c gets the contiguous y range
+// [c n_y / 8, (c + 1) n_y / 8), so the workgroups that share data through y
+// (a key/value head, a head-group split) meet in one L2.
+__device__ __forceinline__ void xcd_split(int L, int n_y, int& x, int& y) {
+  if ((n_y & 7) == 0) {
+    const int per = n_y >> 3, rest = L >> 3;
+    y = (L & 7) * per + rest % per;
+    x = rest / per;
+  } else {
+    y = L % n_y;
+    x = L / n_y;
+  }
+}
+
 // Register -> LDS, one chunk: the i-th 16-byte chunk a thread holds, into
 // one or two swizzled copies of the tile.
 __device__ __forceinline__ void put_one(const u32x4& x, uint8_t* t_row, uint8_t* t_tr, int tid,

@@ -27,7 +27,8 @@ struct SmemKV {
 };
 
 // dk/dv kernel: one workgroup = 128 keys of one key/value head and one split
-// of the query heads that read it; grid (n_kt128, h_kv * n_split).  Walks the
+// of the query heads that read it; a one-dimensional grid of
+// n_kt128 * h_kv * n_split workgroups.  Walks the
 // split's heads and, per head, the query tiles that see these keys.  With one
 // split it adds to dk, dv; with several, each split writes its partial sums
 // to the workspace and a reduction adds them in a fixed order.
@@ -38,10 +39,12 @@ void dkv_kernel(const BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Lanes L(lane);
   const int n_split = a.n_split;
-  const int kvh = blockIdx.y / n_split, split = blockIdx.y % n_split;
+  int bx, by;  // one head-group split (its queries and dout) per XCD
+  xcd_split(blockIdx.x, a.h_kv * n_split, bx, by);
+  const int kvh = by / n_split, split = by % n_split;
   const int hps = a.h_q / a.h_kv / n_split;  // heads per split
   const int n_q = a.n_q, n_k = a.n_k;
-  const int key0_wg = blockIdx.x * ROWS, key0 = key0_wg + wave * 32;
+  const int key0_wg = bx * ROWS, key0 = key0_wg + wave * 32;
   const int key = key0 + L.col;
   const bool kv = key < n_k;
   const size_t skey = (size_t)kvh * n_k + key;
@@ -281,7 +284,7 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (a.n_k > 0) {
-    dim3 grid((unsigned)((a.n_k + bwd::ROWS - 1) / bwd::ROWS), (unsigned)(a.h_kv * a.n_split));
+    dim3 grid((unsigned)((a.n_k + bwd::ROWS - 1) / bwd::ROWS * a.h_kv * a.n_split));
     hipLaunchKernelGGL(bwd::dkv_kernel, grid, dim3(bwd::THREADS), 0, stream, a);
     if (a.n_split > 1) {
       const int64_t n4 = (int64_t)a.h_kv * a.n_k * bwd::D / 4;

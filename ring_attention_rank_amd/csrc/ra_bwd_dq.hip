@@ -54,16 +54,19 @@ struct SmemQ {
   TileQ t[2];
 };
 
-// dq kernel: one workgroup = 128 query rows of one head; grid (n_qt, h_q).
+// dq kernel: one workgroup = 128 query rows of one head; a one-dimensional
+// grid of n_qt128 * h_q workgroups.
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dq_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) SmemQ sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const Lanes L(lane);
-  const int head = blockIdx.y, kvh = head / (a.h_q / a.h_kv);
+  int bx, head;  // heads that share a key/value head on one XCD
+  xcd_split(blockIdx.x, a.h_q, bx, head);
+  const int kvh = head / (a.h_q / a.h_kv);
   const int n_q = a.n_q, n_k = a.n_k;
-  const int row0_wg = blockIdx.x * ROWS, row0 = row0_wg + wave * 32;
+  const int row0_wg = bx * ROWS, row0 = row0_wg + wave * 32;
   const int row = row0 + L.col;
   const bool rv = row < n_q;
   const size_t srow = (size_t)head * n_q + row;
@@ -253,7 +256,7 @@ hipError_t launch_backward_delta(const float* out, const void* dout, float* delt
 // dq kernel when there are queries, dk/dv kernel when there are keys (with no
 // queries it writes zeros).
 hipError_t launch_backward_dq(const BwdArgs& a, hipStream_t stream) {
-  dim3 grid((unsigned)((a.n_q + bwd::ROWS - 1) / bwd::ROWS), (unsigned)a.h_q);
+  dim3 grid((unsigned)((a.n_q + bwd::ROWS - 1) / bwd::ROWS * a.h_q));
   hipLaunchKernelGGL(bwd::dq_kernel, grid, dim3(bwd::THREADS), 0, stream, a);
   return hipGetLastError();
 }
