@@ -156,13 +156,15 @@ ra_status ra_forward_allgather(const ra_problem* p, int32_t n_cp, const void* q,
  * backward mirrors the forward; each GPU computes, from its own queries, the
  * gradients of every key/value block it sees, returned to the block's owner
  * as a second circulating block in the ring or by a reduce-scatter in the
- * all-gather form).  bfloat16 with d_k = 128 only (RA_ERR_DTYPE /
- * RA_ERR_SHAPE otherwise).  With s = scale q.k over visible pairs and the
+ * all-gather form).  Every shape the forward takes: bfloat16 with d_k = 128
+ * runs on MFMA kernels (p and ds rounded to bfloat16 as MFMA operands); fp32
+ * and bfloat16 with d_k = 64 run on plain per-row kernels in fp32 (correct,
+ * not tuned).  With s = scale q.k over visible pairs and the
  * forward's lse (natural log, over all blocks): p = exp(s - lse),
  * delta = rowsum(dout * out), ds = p (dout.v - delta).
  *
  * ra_backward_prep: delta[h_q][n_q] (fp32) from out[h_q][n_q][d_k] (fp32, the
- * forward's output) and dout[h_q][n_q][d_k] (bf16).
+ * forward's output) and dout[h_q][n_q][d_k] (the inputs' dtype).
  * ra_backward_step: one key/value block.  All three gradients are
  * ACCUMULATED: dq[h_q][n_q][d_k] (fp32) += scale * sum_j ds k_j (zero it
  * before the first block); dk, dv[h_kv][n_k][d_k] (fp32) += this rank's part

@@ -364,12 +364,14 @@ ra_status ra_backward_prep(const ra_problem* p, const float* out, const void* do
                            float* delta, void* stream) {
   ra_status st = check_problem(p);
   if (st != RA_OK) return st;
-  if (!fast_path(p)) return p->dtype != RA_BF16 ? RA_ERR_DTYPE : RA_ERR_SHAPE;
   const int64_t rows = (int64_t)p->h_q * p->n_q;
   if (rows == 0) return RA_OK;
   if (!out || !dout || !delta) return RA_ERR_NULL;
   if (!aligned16(out) || !aligned16(dout) || !aligned4(delta)) return RA_ERR_ALIGN;
-  hipError_t e = ra::launch_backward_delta(out, dout, delta, rows, (hipStream_t)stream);
+  hipError_t e = fast_path(p)
+                     ? ra::launch_backward_delta(out, dout, delta, rows, (hipStream_t)stream)
+                     : ra::launch_backward_delta_generic(out, dout, delta, rows, p->dtype, p->d_k,
+                                                         (hipStream_t)stream);
   return e == hipSuccess ? RA_OK : RA_ERR_HIP;
 }
 
@@ -384,8 +386,8 @@ ra_status ra_backward_step(const ra_problem* p, const void* q, const int32_t* q_
                            void* workspace, size_t workspace_bytes, void* stream) {
   ra_status st = check_problem(p);
   if (st != RA_OK) return st;
-  if (!fast_path(p)) return p->dtype != RA_BF16 ? RA_ERR_DTYPE : RA_ERR_SHAPE;
-  const size_t need = ra::backward_ws_bytes(p->n_k, p->h_q, p->h_kv);
+  const bool fast = fast_path(p);
+  const size_t need = fast ? ra::backward_ws_bytes(p->n_k, p->h_q, p->h_kv) : 0;
   if (need > 0 && p->n_k > 0) {
     if (!workspace) return RA_ERR_NULL;
     if (workspace_bytes < need) return RA_ERR_WORKSPACE;
@@ -418,11 +420,14 @@ ra_status ra_backward_step(const ra_problem* p, const void* q, const int32_t* q_
   a.h_q = p->h_q;
   a.h_kv = p->h_kv;
   a.causal = p->causal;
-  a.n_split = ra::backward_splits(p->n_k, p->h_q, p->h_kv);
+  a.n_split = fast ? ra::backward_splits(p->n_k, p->h_q, p->h_kv) : 1;
   a.ws = (float*)workspace;
   a.scale = softmax_scale(p);
   a.c2 = a.scale * 1.4426950408889634f;
-  return ra::launch_backward(a, (hipStream_t)stream) == hipSuccess ? RA_OK : RA_ERR_HIP;
+  const hipError_t e =
+      fast ? ra::launch_backward(a, (hipStream_t)stream)
+           : ra::launch_backward_generic(a, p->dtype, p->d_k, (hipStream_t)stream);
+  return e == hipSuccess ? RA_OK : RA_ERR_HIP;
 }
 
 size_t ra_forward_allgather_workspace_bytes(const ra_problem* p) {

@@ -78,6 +78,10 @@ int backward_splits(int n_k, int h_q, int h_kv);
 size_t backward_ws_bytes(int n_k, int h_q, int h_kv);
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_backward_dq(const BwdArgs& a, hipStream_t stream);
+// Plain per-row backward for the other supported shapes (fp32; bf16 d_k 64).
+hipError_t launch_backward_generic(const BwdArgs& a, int dtype, int d_k, hipStream_t stream);
+hipError_t launch_backward_delta_generic(const float* out, const void* dout, float* delta,
+                                         int64_t rows, int dtype, int d_k, hipStream_t stream);
 hipError_t launch_backward_delta(const float* out, const void* dout, float* delta, int64_t rows,
                                  hipStream_t stream);
 

@@ -145,11 +145,15 @@ def test_backward_checks():
     odd = ctypes.c_void_p(FAKE + 4)
     step = lambda p, *ptrs: L.ra_backward_step(ctypes.byref(p), *ptrs, v, 1 << 40, None)
     full = [v] * 11
-    # bfloat16 with d_k = 128 only
-    assert step(good(dtype=ra.RA_F32), *full) == DTYPE
-    assert step(good(d_k=64), *full) == SHAPE
+    # every shape the forward takes (fp32 and d_k 64 run the plain kernels):
+    # accepted up to the pointer checks; other shapes refused
+    assert step(good(dtype=ra.RA_F32), None, *full[1:]) == NULL
+    assert step(good(d_k=64), None, *full[1:]) == NULL
+    assert step(good(d_k=96), *full) == SHAPE
     assert step(good(h_q=3), *full) == SHAPE
-    assert L.ra_backward_prep(ctypes.byref(good(dtype=ra.RA_F32)), v, v, v, None) == DTYPE
+    assert step(good(dtype=7), *full) == DTYPE
+    assert L.ra_backward_prep(ctypes.byref(good(dtype=ra.RA_F32)), None, v, v, None) == NULL
+    assert L.ra_backward_prep(ctypes.byref(good(d_k=96)), v, v, v, None) == SHAPE
     # every pointer of a non-empty side is required
     for i in range(11):
         ptrs = list(full)

@@ -6,17 +6,19 @@ Both sides get the same inputs: q, k, v, dout (bfloat16 values), and the
 forward's out and lse from the oracle, rounded to float32 (the library's
 input types).
 
-Tolerance, per element.  Against the exact product, the HIP path rounds two
-things to bfloat16 before an MFMA reads them: p (for dv) and ds (for dq and
-dk); everything else is float32.  Rounding to nearest moves a value by at
-most 2^-8 of itself, so
+Tolerance, per element.  Against the exact product, the MFMA path (bfloat16,
+d_k = 128) rounds two things to bfloat16 before an MFMA reads them: p (for
+dv) and ds (for dq and dk); everything else is float32.  Rounding to nearest
+moves a value by at most 2^-8 of itself, so
 
     |dq_gpu - dq| <= scale (2^-8 |ds| + e p (A + |D|)) @ |k| + 1e-6
 
 (dk with q in place of k, dv with 2^-8 p @ |dout|), where
 A = |dout| @ |v|^T bounds the float32 error of dp, and e = 1e-4 covers the
 float32 errors of s, the exponential, dp and D (each under about 1e-5 of
-these magnitudes at d_k = 128).
+these magnitudes at d_k = 128).  The plain kernels for the other shapes
+(float32 inputs, bfloat16 with d_k = 64) round nothing to bfloat16: there
+the 2^-8 terms are 0.
 """
 
 import numpy as np
@@ -49,16 +51,23 @@ def fwd_inputs(sh, dout_seed_case=None):
 def run_gpu(sh, out32, lse32, dout, blocks=None):
     idx = range(len(sh.gk)) if blocks is None else blocks
     g = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    dt = torch.bfloat16 if sh.case.dtype == "bf16" else torch.float32
     dq, dks, dvs = ra.backward(sh.gq, sh.gq_pos, [sh.gk[i] for i in idx], [sh.gv[i] for i in idx],
-                               [sh.gk_pos[i] for i in idx], g(out32), g(lse32),
-                               g(dout).to(torch.bfloat16), causal=sh.case.causal)
+                               [sh.gk_pos[i] for i in idx], g(out32), g(lse32), g(dout).to(dt),
+                               causal=sh.case.causal)
     torch.cuda.synchronize()
     return dq.cpu().numpy(), [x.cpu().numpy() for x in dks], [x.cpu().numpy() for x in dvs]
 
 
-def bounds(q, q_pos, k, v, k_pos, dout, lse, D, causal):
+def rounding(case):
+    """Relative rounding of p and ds before the products: bf16 on the MFMA
+    path, none on the plain kernels."""
+    return U_BF16 if (case.dtype == "bf16" and case.d_k == 128) else 0.0
+
+
+def bounds(q, q_pos, k, v, k_pos, dout, lse, D, causal, u=U_BF16):
     """Per-element error bounds (dq, dk, dv) for one block (see the module
-    docstring)."""
+    docstring); ``u`` is the relative rounding of p and ds."""
     h_q, n_q, d = q.shape
     h_kv, n_k, _ = k.shape
     g = h_q // h_kv
@@ -77,10 +86,10 @@ def bounds(q, q_pos, k, v, k_pos, dout, lse, D, causal):
         dp = dout[h].astype(np.float64) @ v[kv].T.astype(np.float64)
         A = np.abs(dout[h]).astype(np.float64) @ np.abs(v[kv]).T.astype(np.float64)
         ads = np.abs(p * (dp - D[h][:, None]))
-        m = U_BF16 * ads + E_F32 * p * (A + np.abs(D[h])[:, None])
+        m = u * ads + E_F32 * p * (A + np.abs(D[h])[:, None])
         bq[h] = scale * (m @ np.abs(k[kv]))
         bk[kv] += scale * (m.T @ np.abs(q[h]))
-        bv[kv] += (U_BF16 + E_F32) * (p.T @ np.abs(dout[h]))
+        bv[kv] += (u + E_F32) * (p.T @ np.abs(dout[h]))
     return bq, bk, bv
 
 
@@ -105,7 +114,8 @@ def check_share(sh, label):
     D = oracle.backward_prep_ref(out32, dout)
     bq_tot = np.zeros(rq.shape)
     for b in range(len(sh.k)):
-        bq, bk, bv = bounds(sh.q, sh.q_pos, sh.k[b], sh.v[b], sh.k_pos[b], dout, lse32, D, causal)
+        bq, bk, bv = bounds(sh.q, sh.q_pos, sh.k[b], sh.v[b], sh.k_pos[b], dout, lse32, D, causal,
+                            rounding(sh.case))
         bq_tot += bq
         check_close(dks[b], rks[b], bk, f"{label} dk block {b}")
         check_close(dvs[b], rvs[b], bv, f"{label} dv block {b}")
@@ -202,13 +212,31 @@ def test_dk_dv_accumulate(h_q, h_kv, n_k):
     assert torch.equal(dk, base_k + dk0) and torch.equal(dv, base_v + dv0)
 
 
+@pytest.mark.parametrize("dtype,d_k", [("f32", 64), ("f32", 128), ("bf16", 64)])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("n_q,n_k,h_q,h_kv", [(300, 200, 4, 2), (1, 70, 3, 3), (130, 1, 2, 2)])
+def test_plain_kernels(dtype, d_k, n_q, n_k, h_q, h_kv, causal):
+    """The shapes outside the MFMA path run the plain float32 kernels."""
+    rng = np.random.default_rng(n_q * 11 + n_k + d_k)
+    sh = _custom_share(rng, dtype, d_k, h_q, h_kv, n_q, n_k, 3, causal=causal)
+    check_share(sh, f"plain {dtype} d{d_k} nq{n_q} nk{n_k} h{h_q}/{h_kv} causal={causal}")
+
+
+def test_plain_kernels_full_tile_share():
+    """A reduced ring share of the fp32 workload through the plain kernels."""
+    sh = Share(synth.case_by_name("tiny_f32_contiguous"), 2).to_gpu()
+    check_share(sh, "tiny_f32_contiguous r2")
+
+
 def test_unsupported_shapes_refused():
     rng = np.random.default_rng(3)
-    sh = _custom_share(rng, "f32", 64, 2, 2, 64, 64, 1)
+    sh = _custom_share(rng, "bf16", 128, 2, 2, 64, 64, 1)
+    q96 = torch.zeros((2, 64, 96), dtype=torch.bfloat16, device="cuda")
     z = torch.zeros((2, 64), dtype=torch.float32, device="cuda")
-    dq = torch.zeros(sh.gq.shape, dtype=torch.float32, device="cuda")
-    with pytest.raises(ra.RAError, match="dtype"):
-        ra.backward_step(sh.gq, sh.gq_pos, sh.gk[0], sh.gv[0], sh.gk_pos[0], sh.gq, z, z, dq)
+    dq = torch.zeros(q96.shape, dtype=torch.float32, device="cuda")
+    k96 = torch.zeros((2, 64, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ra.RAError, match="sizes"):
+        ra.backward_step(q96, sh.gq_pos, k96, k96, sh.gk_pos[0], q96, z, z, dq)
 
 
 def test_full_size_sampled():
