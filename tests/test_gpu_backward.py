@@ -239,17 +239,19 @@ def test_unsupported_shapes_refused():
         ra.backward_step(q96, sh.gq_pos, k96, k96, sh.gk_pos[0], q96, z, z, dq)
 
 
-def test_full_size_sampled():
-    """The 405B stage share at full size (8192 queries, 16 heads, 16 blocks of
-    8192 keys), in the launch configuration the benchmark times.  Sampled rows'
-    dq against the oracle (those rows get the oracle's out and lse; the other
-    rows take the library's forward, which only the sum rules below use).
-    Sum rules over all blocks: sum_j dv_j = sum over the group's heads of
-    sum_i dout_i (the probabilities of each row sum to one), and
-    sum_i q_i . dq_i = sum_j k_j . dk_j (both equal sum_ij ds_ij s_ij)."""
-    case = synth.case_by_name("llama405b_stage_share")
+@pytest.mark.parametrize("name", ["llama405b_stage_share", "million_striped_mha"])
+def test_full_size_sampled(name):
+    """A share at full size (405B stage: 8192 queries, 16 heads, 16 blocks of
+    8192 keys; striped MHA: 8 heads, 64 blocks), in the launch configuration
+    the benchmark times.  Sampled rows' dq against the oracle (those rows get
+    the oracle's out and lse; the other rows take the library's forward, which
+    only the sum rules below use).  Sum rules over all blocks: per key/value
+    head, sum_j dv_j = sum over the group's heads of sum_i dout_i (the
+    probabilities of each row sum to one), and sum_i q_i . dq_i =
+    sum_j k_j . dk_j (both equal sum_ij ds_ij s_ij)."""
+    case = synth.case_by_name(name)
     sh = Share(case, 0).to_gpu()
-    print("[backward] llama405b_stage_share full size", flush=True)
+    print(f"[backward] {name} full size", flush=True)
     out, lse, _, _ = ra.forward(sh.gq, sh.gq_pos, sh.gk, sh.gv, sh.gk_pos)
     rows = sample_rows(sh.q_pos, n_rand=24, seed=4)
     ro, rl = sh.oracle(rows)
@@ -274,9 +276,10 @@ def test_full_size_sampled():
 
     # sum_j dv_j = sum_i dout_i: p of a row sums to one up to the float32 lse
     # (1e-5 here) and the bfloat16 rounding of each p
-    sum_dv = sum(x.double().sum(dim=1) for x in dvs)[0].cpu().numpy()
-    want = dout.astype(np.float64).sum(axis=(0, 1))
-    lim = (U_BF16 + 1e-4) * np.abs(dout).astype(np.float64).sum(axis=(0, 1))
+    sum_dv = sum(x.double().sum(dim=1) for x in dvs).cpu().numpy()  # [h_kv][d]
+    grouped = dout.astype(np.float64).reshape(case.h_kv, case.h_q // case.h_kv, -1, case.d_k)
+    want = grouped.sum(axis=(1, 2))
+    lim = (U_BF16 + 1e-4) * np.abs(grouped).sum(axis=(1, 2))
     assert np.all(np.abs(sum_dv - want) <= lim), float(np.abs(sum_dv - want).max())
 
     # sum_i q_i . dq_i = sum_j k_j . dk_j, over the group's heads and all blocks
