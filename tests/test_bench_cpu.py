@@ -1,0 +1,37 @@
+"""bench.py's host logic, without a GPU: the single-GPU guard and the rule
+that the committed HBM traffic figure is reported only for its own workload
+and while the kernel source still has the hash it was measured at."""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_traffic_figure_matches_its_workload_only():
+    value = bench.committed_traffic("llama405b_stage_share")
+    assert value is not None and 1e8 < value < 1e9
+    assert bench.committed_traffic("llama70b_stage_share") is None
+
+
+def test_traffic_figure_dropped_when_the_kernel_changes(monkeypatch):
+    monkeypatch.setattr(bench, "kernel_source_sha256", lambda: "0" * 64)
+    assert bench.committed_traffic("llama405b_stage_share") is None
+
+
+def test_traffic_figure_missing_summary(monkeypatch, tmp_path):
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(tmp_path / "absent.md"))
+    assert bench.committed_traffic("llama405b_stage_share") is None
