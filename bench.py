@@ -137,44 +137,32 @@ def cpu_baseline(case, share, out, lse, budget_rows):
 
 
 def time_backward(share, fwd, fwd_flops, steps, warmup, rank):
-    """One backward step of the share: delta = rowsum(dout * out), then one
-    block step per key/value block (dq, and each block's dk and dv, accumulated).
-    Its algorithmic flops are five GEMMs over the visible pairs (S, dP, dQ,
-    dK, dV), 2.5 times the forward's; the dq kernel recomputes S and dP, which
-    is not counted."""
+    """The share's backward in one call (ra_backward_share): delta =
+    rowsum(dout * out), then every block's dq kernel on the launch stream and
+    its dk/dv kernels on a side stream.  Its algorithmic flops are five GEMMs
+    over the visible pairs (S, dP, dQ, dK, dV), 2.5 times the forward's; the
+    dq kernel recomputes S and dP, which is not counted."""
     g = torch.Generator(device="cuda").manual_seed(2024)
-    q, gk = share["gq"], share["gk"]
+    q = share["gq"]
     dout = torch.randn(q.shape, generator=g, device="cuda").to(torch.bfloat16)
     out, lse = fwd.out, fwd.lse
-    delta = torch.empty(lse.shape, dtype=torch.float32, device="cuda")
-    dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
-    # dk and dv accumulate (the travelling gradients of the ring); the timed
-    # steps keep adding to these buffers
-    dks = [torch.zeros(k.shape, dtype=torch.float32, device="cuda") for k in gk]
-    dvs = [torch.zeros(k.shape, dtype=torch.float32, device="cuda") for k in gk]
-    need = max(ra.backward_workspace_bytes(ra._problem_from(q, k, True, None)) for k in gk)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
-
-    def step():
-        ra.backward_prep(out, dout, delta)
-        dq.zero_()
-        for b in range(len(gk)):
-            ra.backward_step(q, share["gq_pos"], gk[b], share["gv"][b], share["gk_pos"][b], dout,
-                             lse, delta, dq, dks[b], dvs[b], workspace=ws)
-
+    f = ra.BackwardShare(q, share["gq_pos"], share["gk"], share["gv"], share["gk_pos"], side=True)
     for _ in range(warmup):
-        step()
+        f(out, lse, dout)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        step()
+        f(out, lse, dout)
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / steps
     flops = 2.5 * fwd_flops
+    n = len(share["gk"])
+    split = ra.backward_workspace_bytes(ra._problem_from(q, share["gk"][0], True, None)) > 0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "ms_per_step": dt * 1e3,
             "pct_of_bf16_peak": 100.0 * flops / dt / 1e12 / PEAK_BF16_TFLOPS,
             "flops_per_step": flops, "flops_counted": "S, dP, dQ, dK, dV over visible pairs",
-            "launches_per_step": 2 + len(gk) * (3 if need else 2), "rank": rank}
+            "entry_point": "ra_backward_share (dk/dv on a side stream)",
+            "launches_per_step": 2 + n * (5 if split else 4), "rank": rank}
 
 
 def main():

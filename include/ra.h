@@ -189,6 +189,32 @@ ra_status ra_backward_step(const ra_problem* p, const void* q, const int32_t* q_
                            const float* lse, const float* delta, float* dq, float* dk, float* dv,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Backward of the whole rank share in one call, every block resident (the
+ * all-gather form of Zero to Frontier, "distributed/context-expert", section
+ * "Splitting the sequence, and the one layer that objects": this rank's
+ * dK/dV contributions are then reduce-scattered to the blocks' owners).
+ * Block b is k_blocks[b], v_blocks[b], k_pos_blocks[b] as in ra_forward.
+ * Writes (OVERWRITES) dq[h_q][n_q][d_k] and, per block, dk_blocks[b] and
+ * dv_blocks[b][h_kv][n_k][d_k] (fp32) with this rank's gradients, from the
+ * forward's out (fp32) and lse and the output gradient dout (inputs' dtype).
+ * Workspace: ra_backward_share_workspace_bytes(p) bytes, 16-byte aligned,
+ * device memory (delta and the head-group partial sums; contents unspecified
+ * after the call); NULL is accepted when the size is 0.  With side_stream
+ * non-NULL and different from main_stream (bfloat16 with d_k = 128), the
+ * dk/dv kernels run on side_stream beside the dq kernels on main_stream;
+ * side_stream first waits for main_stream's prior work and main_stream ends
+ * waiting for side_stream, so the results are complete in main_stream order.
+ * Asynchronous; the same shapes and error codes as ra_backward_step.
+ */
+size_t ra_backward_share_workspace_bytes(const ra_problem* p);
+ra_status ra_backward_share(const ra_problem* p, int32_t n_cp, const void* q,
+                            const int32_t* q_pos, const void* const* k_blocks,
+                            const void* const* v_blocks, const int32_t* const* k_pos_blocks,
+                            const float* out, const float* lse, const void* dout, float* dq,
+                            float* const* dk_blocks, float* const* dv_blocks, void* workspace,
+                            size_t ws_bytes, void* main_stream, void* side_stream);
+
 /* Query-tile rows (bm) and key-tile columns (bn) the tile counters use. */
 ra_status ra_tile_shape(const ra_problem* p, int32_t* bm, int32_t* bn);
 

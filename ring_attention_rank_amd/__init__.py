@@ -26,7 +26,8 @@ RA_BF16, RA_F32 = 0, 1
 SYMBOLS = (
     "ra_state_init", "ra_step", "ra_finalize", "ra_forward_workspace_bytes", "ra_forward",
     "ra_forward_allgather_workspace_bytes", "ra_forward_allgather",
-    "ra_backward_prep", "ra_backward_workspace_bytes", "ra_backward_step", "ra_tile_shape", "ra_status_string", "ra_abi_version",
+    "ra_backward_prep", "ra_backward_workspace_bytes", "ra_backward_step",
+    "ra_backward_share_workspace_bytes", "ra_backward_share", "ra_tile_shape", "ra_status_string", "ra_abi_version",
 )
 
 
@@ -75,12 +76,18 @@ def lib():
     L.ra_backward_workspace_bytes.restype = ctypes.c_size_t
     L.ra_backward_step.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    ctypes.c_size_t, vp]
+    L.ra_backward_share_workspace_bytes.argtypes = [P]
+    L.ra_backward_share_workspace_bytes.restype = ctypes.c_size_t
+    L.ra_backward_share.argtypes = [P, i32, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                    ctypes.POINTER(vp), vp, vp, vp, vp, ctypes.POINTER(vp),
+                                    ctypes.POINTER(vp), vp, ctypes.c_size_t, vp, vp]
     L.ra_tile_shape.argtypes = [P, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.ra_status_string.argtypes = [i32]
     L.ra_status_string.restype = ctypes.c_char_p
     L.ra_abi_version.argtypes = []
     for name in ("ra_state_init", "ra_step", "ra_finalize", "ra_forward", "ra_tile_shape",
                  "ra_forward_allgather", "ra_backward_prep", "ra_backward_step",
+                 "ra_backward_share",
                  "ra_abi_version"):
         getattr(L, name).restype = i32
     _lib = L
@@ -334,3 +341,48 @@ def backward(q, q_pos, k_blocks, v_blocks, k_pos_blocks, out, lse, dout, causal=
         dks.append(dk)
         dvs.append(dv)
     return dq, dks, dvs
+
+
+def backward_share_workspace_bytes(p):
+    return int(lib().ra_backward_share_workspace_bytes(ctypes.byref(p)))
+
+
+class BackwardShare:
+    """A prepared whole-share backward (ra_backward_share): outputs and
+    workspace allocated once; each call overwrites dq and every block's dk,
+    dv with this rank's gradients."""
+
+    def __init__(self, q, q_pos, k_blocks, v_blocks, k_pos_blocks, causal=True, scale=None,
+                 side=True):
+        self.args = (q, q_pos, list(k_blocks), list(v_blocks), list(k_pos_blocks))
+        _need_gpu(q, q_pos, *k_blocks, *v_blocks, *k_pos_blocks)
+        self.p = _problem_from(q, k_blocks[0], causal, scale)
+        dev = q.device
+        self.dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        self.dks = [torch.empty(k.shape, dtype=torch.float32, device=dev) for k in k_blocks]
+        self.dvs = [torch.empty(k.shape, dtype=torch.float32, device=dev) for k in k_blocks]
+        need = backward_share_workspace_bytes(self.p)
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        self.side = side_stream(dev) if side else None
+        n = len(k_blocks)
+        arr = lambda ts: (ctypes.c_void_p * n)(*[_ptr(t) for t in ts])
+        self.kp, self.vp, self.pp = arr(k_blocks), arr(v_blocks), arr(k_pos_blocks)
+        self.dkp, self.dvp = arr(self.dks), arr(self.dvs)
+
+    def __call__(self, out, lse, dout, stream=None):
+        q, q_pos = self.args[0], self.args[1]
+        _need_gpu(out, lse, dout)
+        side = _stream(self.side) if self.side is not None else ctypes.c_void_p(0)
+        _check(lib().ra_backward_share(ctypes.byref(self.p), len(self.dks), _ptr(q), _ptr(q_pos),
+                                       self.kp, self.vp, self.pp, _ptr(out), _ptr(lse),
+                                       _ptr(dout), _ptr(self.dq), self.dkp, self.dvp,
+                                       _ptr(self.ws), self.ws.numel(), _stream(stream), side),
+               "ra_backward_share")
+        return self.dq, self.dks, self.dvs
+
+
+def backward_share(q, q_pos, k_blocks, v_blocks, k_pos_blocks, out, lse, dout, causal=True,
+                   scale=None, side=True):
+    """Whole-share backward in one call: returns (dq, dks, dvs), fp32."""
+    return BackwardShare(q, q_pos, k_blocks, v_blocks, k_pos_blocks, causal, scale, side)(
+        out, lse, dout)

@@ -278,21 +278,25 @@ size_t backward_ws_bytes(int n_k, int h_q, int h_kv) {
   return g > 1 ? (size_t)2 * g * h_kv * n_k * bwd::D * sizeof(float) : 0;
 }
 
+// dk/dv kernel and, with a head-group split, the reduction of its partials.
+hipError_t launch_backward_dkv(const BwdArgs& a, hipStream_t stream) {
+  if (a.n_k == 0) return hipSuccess;
+  dim3 grid((unsigned)((a.n_k + bwd::ROWS - 1) / bwd::ROWS * a.h_kv * a.n_split));
+  hipLaunchKernelGGL(bwd::dkv_kernel, grid, dim3(bwd::THREADS), 0, stream, a);
+  if (a.n_split > 1) {
+    const int64_t n4 = (int64_t)a.h_kv * a.n_k * bwd::D / 4;
+    hipLaunchKernelGGL(bwd::reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
+                       stream, a.ws, a.dk, a.dv, n4, a.n_split);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
   if (a.n_q > 0) {
     const hipError_t e = launch_backward_dq(a, stream);
     if (e != hipSuccess) return e;
   }
-  if (a.n_k > 0) {
-    dim3 grid((unsigned)((a.n_k + bwd::ROWS - 1) / bwd::ROWS * a.h_kv * a.n_split));
-    hipLaunchKernelGGL(bwd::dkv_kernel, grid, dim3(bwd::THREADS), 0, stream, a);
-    if (a.n_split > 1) {
-      const int64_t n4 = (int64_t)a.h_kv * a.n_k * bwd::D / 4;
-      hipLaunchKernelGGL(bwd::reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
-                         stream, a.ws, a.dk, a.dv, n4, a.n_split);
-    }
-  }
-  return hipGetLastError();
+  return launch_backward_dkv(a, stream);
 }
 
 }  // namespace ra

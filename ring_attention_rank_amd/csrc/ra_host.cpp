@@ -430,6 +430,142 @@ ra_status ra_backward_step(const ra_problem* p, const void* q, const int32_t* q_
   return e == hipSuccess ? RA_OK : RA_ERR_HIP;
 }
 
+namespace {
+// Workspace of ra_backward_share: delta, then the head-group partial sums the
+// dk/dv kernel writes (shared by the blocks, whose dk/dv steps are ordered).
+struct BwdShareLayout {
+  size_t delta, part, total;
+};
+BwdShareLayout bwd_share_layout(const ra_problem* p) {
+  BwdShareLayout w;
+  w.delta = 0;
+  w.part = align_up((size_t)p->h_q * p->n_q * sizeof(float));
+  const size_t part = fast_path(p) ? ra::backward_ws_bytes(p->n_k, p->h_q, p->h_kv) : 0;
+  w.total = w.part + align_up(part);
+  return w;
+}
+}  // namespace
+
+size_t ra_backward_share_workspace_bytes(const ra_problem* p) {
+  if (check_problem(p) != RA_OK) return 0;
+  return bwd_share_layout(p).total;
+}
+
+ra_status ra_backward_share(const ra_problem* p, int32_t n_cp, const void* q,
+                            const int32_t* q_pos, const void* const* k_blocks,
+                            const void* const* v_blocks, const int32_t* const* k_pos_blocks,
+                            const float* out, const float* lse, const void* dout, float* dq,
+                            float* const* dk_blocks, float* const* dv_blocks, void* workspace,
+                            size_t ws_bytes, void* main_stream, void* side_stream) {
+  ra_status st = check_problem(p);
+  if (st != RA_OK) return st;
+  if (n_cp < 1) return RA_ERR_SHAPE;
+  if (!k_blocks || !v_blocks || !k_pos_blocks || !dk_blocks || !dv_blocks) return RA_ERR_NULL;
+  if (p->n_q > 0) {
+    if (!q || !q_pos || !out || !lse || !dout || !dq) return RA_ERR_NULL;
+    if (!aligned16(q) || !aligned4(q_pos) || !aligned16(out) || !aligned4(lse) ||
+        !aligned16(dout) || !aligned16(dq))
+      return RA_ERR_ALIGN;
+  }
+  if (p->n_k > 0) {
+    for (int b = 0; b < n_cp; ++b) {
+      if (!k_blocks[b] || !v_blocks[b] || !k_pos_blocks[b] || !dk_blocks[b] || !dv_blocks[b])
+        return RA_ERR_NULL;
+      if (!aligned16(k_blocks[b]) || !aligned16(v_blocks[b]) || !aligned4(k_pos_blocks[b]) ||
+          !aligned16(dk_blocks[b]) || !aligned16(dv_blocks[b]))
+        return RA_ERR_ALIGN;
+    }
+  }
+  const BwdShareLayout w = bwd_share_layout(p);
+  if (w.total > 0) {
+    if (!workspace) return RA_ERR_NULL;
+    if (!aligned16(workspace)) return RA_ERR_ALIGN;
+    if (ws_bytes < w.total) return RA_ERR_WORKSPACE;
+  }
+
+  const bool fast = fast_path(p);
+  hipStream_t ms = (hipStream_t)main_stream;
+  hipStream_t ss = (hipStream_t)side_stream;
+  const bool use_side = fast && ss != nullptr && ss != ms;
+  hipStream_t ks = use_side ? ss : ms;  // dk/dv work
+  char* ws = (char*)workspace;
+  float* delta = (float*)(ws + w.delta);
+  const int64_t rows = (int64_t)p->h_q * p->n_q;
+  const int64_t kv_elems = (int64_t)p->h_kv * p->n_k * p->d_k;
+
+  ra::BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.q_pos = q_pos;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.n_q = p->n_q;
+  a.n_k = p->n_k;
+  a.h_q = p->h_q;
+  a.h_kv = p->h_kv;
+  a.causal = p->causal;
+  a.n_split = fast ? ra::backward_splits(p->n_k, p->h_q, p->h_kv) : 1;
+  a.ws = (float*)(ws + w.part);
+  a.scale = softmax_scale(p);
+  a.c2 = a.scale * 1.4426950408889634f;
+
+  hipEvent_t ev_ready = nullptr, ev_done = nullptr;
+  ra_status result = RA_OK;
+  auto hip = [&](hipError_t e) {
+    if (e != hipSuccess && result == RA_OK) result = RA_ERR_HIP;
+    return e == hipSuccess;
+  };
+  auto mk = [](hipEvent_t* e) {
+    return hipEventCreateWithFlags(e, hipEventDisableTiming | hipEventDisableSystemFence) ==
+           hipSuccess;
+  };
+  // dq and delta first (main stream); the dk/dv steps wait for delta
+  if (rows > 0) {
+    if (!hip(ra::launch_zero_f32(dq, rows * p->d_k, ms))) goto cleanup;
+    if (!hip(fast ? ra::launch_backward_delta(out, dout, delta, rows, ms)
+                  : ra::launch_backward_delta_generic(out, dout, delta, rows, p->dtype, p->d_k,
+                                                      ms)))
+      goto cleanup;
+  }
+  if (use_side) {
+    if (!mk(&ev_ready) || !mk(&ev_done)) {
+      result = RA_ERR_HIP;
+      goto cleanup;
+    }
+    if (!hip(hipEventRecord(ev_ready, ms)) || !hip(hipStreamWaitEvent(ss, ev_ready, 0)))
+      goto cleanup;
+  }
+  for (int b = 0; b < n_cp; ++b) {
+    a.k = k_blocks[b];
+    a.v = v_blocks[b];
+    a.k_pos = k_pos_blocks[b];
+    a.dk = dk_blocks[b];
+    a.dv = dv_blocks[b];
+    if (p->n_k > 0) {
+      if (!hip(ra::launch_zero_f32(a.dk, kv_elems, ks)) ||
+          !hip(ra::launch_zero_f32(a.dv, kv_elems, ks)))
+        goto cleanup;
+    }
+    if (fast) {
+      if (p->n_q > 0 && !hip(ra::launch_backward_dq(a, ms))) goto cleanup;
+      if (!hip(ra::launch_backward_dkv(a, ks))) goto cleanup;
+    } else if (p->n_q > 0 || p->n_k > 0) {
+      if (!hip(ra::launch_backward_generic(a, p->dtype, p->d_k, ms))) goto cleanup;
+    }
+  }
+  if (use_side) {
+    if (!hip(hipEventRecord(ev_done, ss)) || !hip(hipStreamWaitEvent(ms, ev_done, 0)))
+      goto cleanup;
+  }
+
+cleanup:
+  for (hipEvent_t e : {ev_ready, ev_done})
+    if (e) hipEventDestroy(e);
+  return result;
+}
+
 size_t ra_forward_allgather_workspace_bytes(const ra_problem* p) {
   if (check_problem(p) != RA_OK) return 0;
   return allgather_ws_bytes(p);

@@ -78,6 +78,7 @@ int backward_splits(int n_k, int h_q, int h_kv);
 size_t backward_ws_bytes(int n_k, int h_q, int h_kv);
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_backward_dq(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_backward_dkv(const BwdArgs& a, hipStream_t stream);
 // Plain per-row backward for the other supported shapes (fp32; bf16 d_k 64).
 hipError_t launch_backward_generic(const BwdArgs& a, int dtype, int d_k, hipStream_t stream);
 hipError_t launch_backward_delta_generic(const float* out, const void* dout, float* delta,
@@ -92,5 +93,6 @@ hipError_t launch_state_init(float* m, float* l, float* o, int64_t rows, int d_k
 hipError_t launch_finalize(const float* m, const float* l, const float* o, float* out,
                            float* lse, int64_t rows, int d_k, hipStream_t stream);
 hipError_t launch_zero_i64(int64_t* p, int n, hipStream_t stream);
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
 
 }  // namespace ra

@@ -678,6 +678,13 @@ __global__ void zero_i64_kernel(int64_t* p, int n) {
   if (i < n) p[i] = 0;
 }
 
+// Fills n floats with zero (a kernel, not a memset, so that a captured graph
+// holds no memset node).
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
 template <typename Tr, int D>
 static hipError_t launch_typed(const StepArgs& a, bool read, bool final_, hipStream_t stream) {
   dim3 grid((unsigned)(a.n_pairs * a.h_q)), block(256);
@@ -724,6 +731,13 @@ hipError_t launch_finalize(const float* m, const float* l, const float* o, float
 
 hipError_t launch_zero_i64(int64_t* p, int n, hipStream_t stream) {
   hipLaunchKernelGGL(zero_i64_kernel, dim3(1), dim3(64), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p,
+                     n);
   return hipGetLastError();
 }
 

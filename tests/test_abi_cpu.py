@@ -179,3 +179,26 @@ def test_backward_checks():
     assert ws(None, need) == NULL
     assert ws(v, need - 1) == WORKSPACE
     assert ws(odd, need) == ALIGN
+
+
+def test_backward_share_checks():
+    L = ra.lib()
+    v = ctypes.c_void_p(FAKE)
+    arr = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    p = good(n_k=8192, h_q=16, h_kv=1)
+    need = L.ra_backward_share_workspace_bytes(ctypes.byref(p))
+    # delta (h_q x n_q floats) plus the head-group partials of one block
+    assert need >= 16 * 256 * 4 + L.ra_backward_workspace_bytes(ctypes.byref(p))
+    call = lambda p, ncp, ka, dka, ws, wsb: L.ra_backward_share(
+        ctypes.byref(p), ncp, v, v, ka, arr, arr, v, v, v, v, dka, arr, ws, wsb, None, None)
+    assert call(p, 0, arr, arr, v, need) == SHAPE
+    assert call(p, 2, None, arr, v, need) == NULL
+    assert call(p, 2, arr, None, v, need) == NULL
+    bad = (ctypes.c_void_p * 2)(FAKE, 0)
+    assert call(p, 2, arr, bad, v, need) == NULL
+    odd = (ctypes.c_void_p * 2)(FAKE, FAKE + 4)
+    assert call(p, 2, arr, odd, v, need) == ALIGN
+    assert call(p, 2, arr, arr, None, need) == NULL
+    assert call(p, 2, arr, arr, v, need - 1) == WORKSPACE
+    assert call(p, 2, arr, arr, ctypes.c_void_p(FAKE + 4), need) == ALIGN
+    assert call(good(d_k=96), 2, arr, arr, v, need) == SHAPE

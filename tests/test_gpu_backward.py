@@ -287,3 +287,40 @@ def test_full_size_sampled(name):
     rhs = float(sum((k.double() * x.double()).sum() for k, x in zip(sh.gk, dks)))
     mag = float((sh.gq.double().abs() * dq.double().abs()).sum())
     assert abs(lhs - rhs) <= 1e-3 * mag, (lhs, rhs, mag)
+
+
+def _share_inputs(sh):
+    out32, lse32, dout = fwd_inputs(sh)
+    dt = torch.bfloat16 if sh.case.dtype == "bf16" else torch.float32
+    g = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    return g(out32), g(lse32), g(dout).to(dt)
+
+
+@pytest.mark.parametrize("side", [True, False])
+@pytest.mark.parametrize("which", ["405b", "ragged", "f32"])
+def test_whole_share_equals_block_steps(which, side):
+    """ra_backward_share (every block in one call, dk/dv on a side stream)
+    gives bit for bit what the block-by-block ra_backward_step loop gives:
+    same kernels, same order of additions into dq."""
+    if which == "405b":
+        sh = Share(synth.case_by_name("llama405b_stage_share"), 0, T=16384, n_cp=16).to_gpu()
+    elif which == "ragged":
+        sh = _custom_share(np.random.default_rng(21), "bf16", 128, 4, 2, 517, 129, 3)
+    else:
+        sh = _custom_share(np.random.default_rng(22), "f32", 64, 4, 2, 300, 200, 3)
+    print(f"[backward] whole share {which} side={side}", flush=True)
+    out, lse, dout = _share_inputs(sh)
+    a_dq, a_dks, a_dvs = ra.backward(sh.gq, sh.gq_pos, sh.gk, sh.gv, sh.gk_pos, out, lse, dout,
+                                     causal=sh.case.causal)
+    f = ra.BackwardShare(sh.gq, sh.gq_pos, sh.gk, sh.gv, sh.gk_pos, causal=sh.case.causal,
+                         side=side)
+    # garbage in the outputs first: the call overwrites them
+    f.dq.fill_(3.0)
+    for t in f.dks + f.dvs:
+        t.fill_(-5.0)
+    for rep in range(2):
+        b_dq, b_dks, b_dvs = f(out, lse, dout)
+        torch.cuda.synchronize()
+        assert torch.equal(a_dq, b_dq), rep
+        for x, y in zip(a_dks + a_dvs, b_dks + b_dvs):
+            assert torch.equal(x, y), rep
