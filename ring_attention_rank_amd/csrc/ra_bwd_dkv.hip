@@ -28,10 +28,10 @@ struct SmemKV {
 
 // dk/dv kernel: one workgroup = 128 keys of one key/value head and one split
 // of the query heads that read it; a one-dimensional grid of
-// n_kt128 * h_kv * n_split workgroups.  Walks the
-// split's heads and, per head, the query tiles that see these keys.  With one
-// split it adds to dk, dv; with several, each split writes its partial sums
-// to the workspace and a reduction adds them in a fixed order.
+// n_kt128 * h_kv * n_split workgroups.  Walks the split's heads and, per
+// head, the query tiles that see these keys.  With one split it adds to dk,
+// dv; with several, each split writes its partial sums to the workspace and
+// a reduction adds them in a fixed order.
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dkv_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) SmemKV sm;
