@@ -96,6 +96,26 @@ __device__ __forceinline__ void xcd_split(int L, int n_y, int& x, int& y) {
   }
 }
 
+// Buffer resource over `bytes` bytes at `base`: loads past the end return
+// zero without a branch, so every wave issues the same loads and the
+// compiler can count them (it waits for the oldest ones only).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Rows [r0, r0 + 64) of a [n][128] bf16 matrix behind resource r, 4 chunks of
+// 16 bytes per thread (zeros past the resource's end).
+__device__ __forceinline__ void fetch_rows(__amdgpu_buffer_rsrc_t r, int r0, u32x4 (&x)[4],
+                                           int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = tid + THREADS * i;
+    const uint32_t off = (uint32_t)(r0 + (id >> 4)) * 256u + (uint32_t)(id & 15) * 16u;
+    x[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+}
+
 // Register -> LDS, one chunk: the i-th 16-byte chunk a thread holds, into
 // one or two swizzled copies of the tile.
 __device__ __forceinline__ void put_one(const u32x4& x, uint8_t* t_row, uint8_t* t_tr, int tid,

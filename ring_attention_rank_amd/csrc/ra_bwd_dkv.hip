@@ -76,21 +76,24 @@ void dkv_kernel(const BwdArgs a) {
   u32x4 pq[4], pg[4];
   int ppos = 0;
   float plse2 = 0.f, pdelta = 0.f;
+  const auto rqp = rsrc(a.q_pos, (uint32_t)n_q * 4u);
+  int tile_row0 = 0;  // first query row of the registered tile
   auto fetch_tile = [&](int i) {
     const int head = (kvh * n_split + split) * hps + i / n_t, t0 = first + i % n_t;
-    fetch((const uint16_t*)a.q + (size_t)head * n_q * D, t0 * TILE, n_q, pq, tid);
-    fetch((const uint16_t*)a.dout + (size_t)head * n_q * D, t0 * TILE, n_q, pg, tid);
-    if (tid < TILE) {
-      const int iq = t0 * TILE + tid;
-      const bool ok = iq < n_q;
-      const size_t sr = (size_t)head * n_q + iq;
-      ppos = ok ? (a.causal ? a.q_pos[iq] : 0x7ffffffe) : (int)0x80000000;
-      // log2-domain lse; +inf for rows past n_q and rows that saw no key, so
-      // that their probabilities come out as exp2(-inf) = 0
-      const float l = ok ? a.lse[sr] : -INFINITY;
-      plse2 = l != -INFINITY ? l * kLog2e : INFINITY;
-      pdelta = ok ? a.delta[sr] : 0.f;
-    }
+    const size_t hrow = (size_t)head * n_q;
+    // queries past n_q read as zeros; every wave issues the same loads
+    fetch_rows(rsrc((const uint16_t*)a.q + hrow * D, (uint32_t)n_q * 256u), t0 * TILE, pq, tid);
+    fetch_rows(rsrc((const uint16_t*)a.dout + hrow * D, (uint32_t)n_q * 256u), t0 * TILE, pg,
+               tid);
+    const uint32_t o = (uint32_t)(t0 * TILE + (tid & (TILE - 1))) * 4u;
+    // raw per-row values; the range selects wait until they are written
+    ppos = __builtin_amdgcn_raw_buffer_load_b32(rqp, o, 0, 0);
+    plse2 = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rsrc(a.lse + hrow, (uint32_t)n_q * 4u), o, 0, 0));
+    pdelta = __builtin_bit_cast(
+        float,
+        __builtin_amdgcn_raw_buffer_load_b32(rsrc(a.delta + hrow, (uint32_t)n_q * 4u), o, 0, 0));
+    tile_row0 = t0 * TILE;
   };
   // slice w (0..16) of the registered tile into buffer b: Q and dout chunks
   // (row and transposing copies), then the per-row values and the tile flag
@@ -101,14 +104,19 @@ void dkv_kernel(const BwdArgs a) {
       uint8_t* tr = (w < 8) ? b.q_tr : b.g_tr;
       put_one(x, (w & 1) ? nullptr : row, (w & 1) ? tr : nullptr, tid, (w & 7) >> 1);
     } else {
+      const bool ok = tile_row0 + (tid & (TILE - 1)) < n_q;
+      const float l = ok ? plse2 : -INFINITY;
+      // log2-domain lse; +inf for rows past n_q and rows that saw no key, so
+      // that their probabilities come out as exp2(-inf) = 0
+      const float l2 = l != -INFINITY ? l * kLog2e : INFINITY;
       if (tid < TILE) {
-        b.pos[tid] = ppos;
-        b.lse2[tid] = plse2;
-        b.delta[tid] = pdelta;
+        b.pos[tid] = ok ? (a.causal ? ppos : 0x7ffffffe) : (int)0x80000000;
+        b.lse2[tid] = l2;
+        b.delta[tid] = ok ? pdelta : 0.f;
       }
       if (wave == 0) {  // wave 0 holds the tile's 64 rows, one per lane
-        const bool ok = __builtin_amdgcn_ballot_w64(plse2 != INFINITY) == ~0ull;
-        if (lane == 0) b.tile_ok = ok ? 1 : 0;
+        const bool all = __builtin_amdgcn_ballot_w64(l2 != INFINITY) == ~0ull;
+        if (lane == 0) b.tile_ok = all ? 1 : 0;
       }
     }
   };

@@ -54,6 +54,9 @@ struct SmemQ {
   TileQ t[2];
 };
 
+// LDS operand reads run this many MFMAs ahead of their use.
+constexpr int AHEAD = 4;
+
 // dq kernel: one workgroup = 128 query rows of one head; a one-dimensional
 // grid of n_qt128 * h_q workgroups.
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -102,39 +105,52 @@ void dq_kernel(const BwdArgs a) {
   const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)kvh * n_k) * D;
   const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)kvh * n_k) * D;
 
-  u32x4 pk[4], pv[4];
-  int ppos = 0;
-  auto fetch_tile = [&](int j) {
-    fetch(kbase, j * TILE, n_k, pk, tid);
-    fetch(vbase, j * TILE, n_k, pv, tid);
-    if (tid < TILE) {
-      const int gk = j * TILE + tid;
-      ppos = gk < n_k ? (a.causal ? a.k_pos[gk] : (int)0x80000000) : 0x7fffffff;
-    }
+  // Two register sets: the set that holds tile j + 1 is written to LDS
+  // during tile j and then receives tile j + 3, so every tile's loads have
+  // about two tiles of compute to land.  Set indices are compile-time
+  // (std::integral_constant), the loop steps two tiles at a time.
+  u32x4 pk[2][4], pv[2][4];
+  int ppos[2] = {0, 0};
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
+  const auto rk = rsrc(kbase, (uint32_t)n_k * 256u), rv_ = rsrc(vbase, (uint32_t)n_k * 256u);
+  const auto rp = rsrc(a.k_pos, (uint32_t)n_k * 4u);
+  auto fetch_tile = [&](auto set, int j) {
+    constexpr int s = decltype(set)::value;
+    fetch_rows(rk, j * TILE, pk[s], tid);  // keys past the block read as zeros
+    fetch_rows(rv_, j * TILE, pv[s], tid);
+    // raw position; the range and causal selects wait until it is written
+    ppos[s] = __builtin_amdgcn_raw_buffer_load_b32(
+        rp, (uint32_t)(j * TILE + (tid & (TILE - 1))) * 4u, 0, 0);
   };
-  // slice w (0..12) of the registered tile into buffer b: K chunks (row and
-  // transposing copies), then V chunks, then the key positions
-  auto put_slice = [&](TileQ& b, int w) {
+  // slice w (0..12) of register set s into buffer b: K chunks (row and
+  // transposing copies), then V chunks, then the key positions of tile j
+  auto put_slice = [&](auto set, TileQ& b, int w, int j) {
+    constexpr int s = decltype(set)::value;
     if (w < 8) {
-      put_one(pk[w >> 1], (w & 1) ? nullptr : b.k_row, (w & 1) ? b.k_tr : nullptr, tid, w >> 1);
+      put_one(pk[s][w >> 1], (w & 1) ? nullptr : b.k_row, (w & 1) ? b.k_tr : nullptr, tid,
+              w >> 1);
     } else if (w < 12) {
-      put_one(pv[w - 8], b.v_row, nullptr, tid, w - 8);
+      put_one(pv[s][w - 8], b.v_row, nullptr, tid, w - 8);
     } else if (tid < TILE) {
-      b.pos[tid] = ppos;
+      const int gk = j * TILE + tid;
+      b.pos[tid] = gk < n_k ? (a.causal ? ppos[s] : (int)0x80000000) : 0x7fffffff;
     }
   };
   f32x16 dq[4] = {};
   const bool wave_ok = __builtin_amdgcn_ballot_w64(!(rv && seen)) == 0;
   const int qmin = __builtin_amdgcn_readfirstlane(qp);  // lane 0 holds the wave's first row
   if (n_iter > 0) {
-    fetch_tile(0);
+    fetch_tile(Set0{}, 0);
 #pragma unroll
-    for (int w = 0; w < 13; ++w) put_slice(sm.t[0], w);
-    fetch_tile(1);  // past the last key tile every load is guarded off
+    for (int w = 0; w < 13; ++w) put_slice(Set0{}, sm.t[0], w, 0);
+    fetch_tile(Set1{}, 1);
+    fetch_tile(Set0{}, 2);
   }
   __syncthreads();
 
-  for (int j = 0; j < n_iter; ++j) {
+  // tile j; `set` holds tile j + 1
+  auto tile = [&](auto set, int j) {
     TileQ& cur = sm.t[j & 1];
     TileQ& nxt = sm.t[(j + 1) & 1];  // last read by tile j - 1, before the barrier
     // no mask when every row of the wave is valid, saw some key, and sees the
@@ -173,45 +189,46 @@ void dq_kernel(const BwdArgs a) {
         X[kb][r] = p * (P[kb][r] - delta);
       };
       auto pack_ds = [&](int kb) {
-#pragma unroll
+  #pragma unroll
         for (int t = 0; t < 2; ++t)
-#pragma unroll
+  #pragma unroll
           for (int e = 0; e < 8; ++e) ds[kb][t][e] = (__bf16)X[kb][8 * t + e];
       };
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rdA(0, i);
+  #pragma unroll
+      for (int i = 0; i < AHEAD; ++i) rdA(0, i);
       read_half(cur.pos, 0, L.h, pz[0]);
       read_half(cur.pos, 1, L.h, pz[1]);
       RA_FENCE();
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {  // S, dP of half 0; tile j + 1 into the other buffer
+  #pragma unroll
+      for (int i = 0; i < 16; ++i) {  // S, dP of half 0
         mA(0, i);
-        if (i + 4 < 16) rdA(0, i + 4); else rdA(1, i - 12);
-        if (i < 13) put_slice(nxt, i);
-        if (i == 13) fetch_tile(j + 2);
+        if (i + AHEAD < 16) rdA(0, i + AHEAD); else rdA(1, i + AHEAD - 16);
         RA_FENCE();
       }
-#pragma unroll
+  #pragma unroll
       for (int i = 0; i < 16; ++i) {  // S, dP of half 1; dS of half 0
         mA(1, i);
-        if (i + 4 < 16) rdA(1, i + 4); else rdT(0, i - 12);
+        if (i + AHEAD < 16) rdA(1, i + AHEAD); else rdT(0, i + AHEAD - 16);
         valu(0, i);
         RA_FENCE();
       }
       pack_ds(0);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {  // dQ from half 0; dS of half 1
+  #pragma unroll
+      for (int i = 0; i < 8; ++i) {  // dQ from half 0; dS of half 1; tile j + 1 to LDS
         mT(0, i);
-        if (i + 4 < 8) rdT(0, i + 4); else rdT(1, i - 4);
+        if (i + AHEAD < 8) rdT(0, i + AHEAD); else rdT(1, i + AHEAD - 8);
         valu(1, 2 * i);
         valu(1, 2 * i + 1);
+        put_slice(set, nxt, i, j + 1);
         RA_FENCE();
       }
       pack_ds(1);
-#pragma unroll
+  #pragma unroll
       for (int i = 0; i < 8; ++i) {  // dQ from half 1
         mT(1, i);
-        if (i + 4 < 8) rdT(1, i + 4);
+        if (i + AHEAD < 8) rdT(1, i + AHEAD);
+        if (i < 5) put_slice(set, nxt, 8 + i, j + 1);
+        if (i == 5) fetch_tile(set, j + 3);  // loads land two tiles later
         RA_FENCE();
       }
     };
@@ -220,6 +237,10 @@ void dq_kernel(const BwdArgs a) {
     else
       body(std::true_type{});
     __syncthreads();  // tile j + 1 is in place; tile j's buffer is free
+  };
+  for (int j = 0; j < n_iter; j += 2) {
+    tile(Set1{}, j);
+    if (j + 1 < n_iter) tile(Set0{}, j + 1);
   }
   if (rv) store_rows<true>(a.dq + srow * D, dq, L.h, a.scale);
 }
