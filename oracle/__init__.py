@@ -41,6 +41,7 @@ from .ring import (  # noqa: F401
     ring_forward_ref,
     brute_attention,
     default_scale,
+    doc_ids,
 )
 from .backward import (  # noqa: F401
     backward_prep_ref,

@@ -77,7 +77,7 @@ def visible_pairs(q_pos, k_pos, causal=True):
     return int(np.searchsorted(ks, q_pos, side="right").sum())
 
 
-def tile_work(q_pos, k_pos, BM, BN, causal=True):
+def tile_work(q_pos, k_pos, BM, BN, causal=True, q_doc=None, k_doc=None):
     """Classify every (query tile, key tile) pair of one block and count them.
 
     Tiles are consecutive runs of BM query rows and BN key rows (the last of
@@ -87,7 +87,8 @@ def tile_work(q_pos, k_pos, BM, BN, causal=True):
 
     Computed by counting the visible pairs of every tile (query rows in
     slices so the visibility matrix stays small) and comparing the count with
-    the tile's size.
+    the tile's size.  With document ids (``q_doc``, ``k_doc``) a visible pair
+    must also share its document.
     """
     q_pos = np.asarray(q_pos, dtype=np.int64)
     k_pos = np.asarray(k_pos, dtype=np.int64)
@@ -95,7 +96,11 @@ def tile_work(q_pos, k_pos, BM, BN, causal=True):
     if n_q == 0 or n_k == 0:
         return 0, 0, 0
     n_qt, n_kt = -(-n_q // BM), -(-n_k // BN)
-    if not causal:
+    docs = q_doc is not None
+    if docs:
+        q_doc = np.asarray(q_doc, dtype=np.int64)
+        k_doc = np.asarray(k_doc, dtype=np.int64)
+    if not causal and not docs:
         return n_qt * n_kt, 0, 0
     col_starts = np.arange(0, n_k, BN)
     col_sizes = np.minimum(col_starts + BN, n_k) - col_starts
@@ -103,7 +108,12 @@ def tile_work(q_pos, k_pos, BM, BN, causal=True):
     rows_per_slice = max(BM, (1 << 22) // max(1, n_k) // BM * BM)
     for r0 in range(0, n_q, rows_per_slice):
         qp = q_pos[r0:r0 + rows_per_slice]
-        vis = (k_pos[None, :] <= qp[:, None]).astype(np.int32)
+        vis = np.ones((qp.size, n_k), dtype=bool)
+        if causal:
+            vis &= k_pos[None, :] <= qp[:, None]
+        if docs:
+            vis &= k_doc[None, :] == q_doc[r0:r0 + rows_per_slice, None]
+        vis = vis.astype(np.int32)
         per_col_tile = np.add.reduceat(vis, col_starts, axis=1)  # [rows][n_kt]
         row_starts = np.arange(0, qp.size, BM)
         counts = np.add.reduceat(per_col_tile, row_starts, axis=0)  # [tiles][n_kt]

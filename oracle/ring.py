@@ -16,6 +16,11 @@ Conventions shared by every function below:
 * Query head h reads key/value head ``h // (h_q // h_kv)`` (consecutive query
   heads share a key/value head).  The pages give only the ratio of query to
   key/value heads, not the assignment.
+* Document masks (packed sequences, Zero to Frontier "Splitting the
+  sequence ...": gathering the keys and values makes such masks easy to
+  support): when ``q_doc`` and ``k_doc`` give each query and key the id of the
+  document it belongs to, a visible key must also be in the query's document.
+  Without them every key is in one document.
 * Scores are ``scale * q.k`` with ``scale = 1/sqrt(d_k)`` unless given.
 * State (m, l, O) is the running maximum, running exp-sum and running
   unnormalised weighted value sum of the online softmax, in natural-log units
@@ -119,7 +124,40 @@ def _row_chunks(n_q, n_k):
         yield slice(i0, min(n_q, i0 + step))
 
 
-def block_partial(q, q_pos, k, v, k_pos, scale=None, causal=True):
+def doc_ids(pos, doc_starts):
+    """Document id of each global position: the index of the last document
+    start at or before it.  ``doc_starts`` are the increasing first positions
+    of the packed documents (the first one 0)."""
+    starts = np.asarray(doc_starts, dtype=np.int64)
+    pos = np.asarray(pos, dtype=np.int64)
+    return np.searchsorted(starts, pos, side="right") - 1
+
+
+def _visible(q_pos_rows, k_pos, causal, q_doc_rows, k_doc):
+    """[rows][n_k] visibility: causal order, and the same document when
+    documents are given; None when every key is visible."""
+    vis = None
+    if causal:
+        vis = k_pos[None, :] <= q_pos_rows[:, None]
+    if q_doc_rows is not None:
+        same = np.asarray(k_doc)[None, :] == np.asarray(q_doc_rows)[:, None]
+        vis = same if vis is None else (vis & same)
+    return vis
+
+
+def _docs(q_doc, k_doc, n_q, n_k):
+    if (q_doc is None) != (k_doc is None):
+        raise ValueError("give both q_doc and k_doc, or neither")
+    if q_doc is None:
+        return None, None
+    q_doc = np.asarray(q_doc, dtype=np.int64)
+    k_doc = np.asarray(k_doc, dtype=np.int64)
+    if q_doc.shape != (n_q,) or k_doc.shape != (n_k,):
+        raise ValueError("document ids must match the row counts")
+    return q_doc, k_doc
+
+
+def block_partial(q, q_pos, k, v, k_pos, scale=None, causal=True, q_doc=None, k_doc=None):
     """Softmax partial of every query against one key/value block.
 
     For each query head h and query i, over the visible keys j of the block:
@@ -132,6 +170,7 @@ def block_partial(q, q_pos, k, v, k_pos, scale=None, causal=True):
     q, k, v, q_pos, k_pos = _check(q, k, v, q_pos, k_pos)
     h_q, n_q, d = q.shape
     h_kv, n_k, _ = k.shape
+    q_doc, k_doc = _docs(q_doc, k_doc, n_q, n_k)
     g = h_q // h_kv
     if scale is None:
         scale = default_scale(d)
@@ -144,8 +183,9 @@ def block_partial(q, q_pos, k, v, k_pos, scale=None, causal=True):
         kv = h // g
         for rows in _row_chunks(n_q, n_k):
             s = scale * (q[h, rows] @ k[kv].T)
-            if causal:
-                visible = k_pos[None, :] <= q_pos[rows, None]
+            visible = _visible(q_pos[rows], k_pos, causal,
+                               None if q_doc is None else q_doc[rows], k_doc)
+            if visible is not None:
                 s = np.where(visible, s, -np.inf)
             mb = s.max(axis=1)
             shift = np.where(np.isfinite(mb), mb, 0.0)
@@ -173,9 +213,10 @@ def fold(state, partial):
     return mn, alpha * l + beta * lb, alpha[..., None] * O + beta[..., None] * Ob
 
 
-def ring_step_ref(q, q_pos, k, v, k_pos, state, scale=None, causal=True):
+def ring_step_ref(q, q_pos, k, v, k_pos, state, scale=None, causal=True, q_doc=None,
+                  k_doc=None):
     """One ring step: fold this block's partial into ``state``."""
-    return fold(state, block_partial(q, q_pos, k, v, k_pos, scale, causal))
+    return fold(state, block_partial(q, q_pos, k, v, k_pos, scale, causal, q_doc, k_doc))
 
 
 def finalize(m, l, O):
@@ -196,21 +237,25 @@ def finalize(m, l, O):
 
 
 def ring_forward_ref(q, q_pos, k_blocks, v_blocks, k_pos_blocks, scale=None,
-                     causal=True, return_state=False):
+                     causal=True, return_state=False, q_doc=None, k_doc_blocks=None):
     """One rank's forward share: fold every block in the given (ring) order,
-    then normalise.  Returns (out, lse) and optionally the final state."""
+    then normalise.  Returns (out, lse) and optionally the final state.  With
+    ``q_doc`` and ``k_doc_blocks`` (document ids of the queries and of each
+    block's keys) the document mask applies as well."""
     q = np.asarray(q, dtype=np.float64)
     h_q, n_q, d = q.shape
     state = init_state(h_q, n_q, d)
-    for k, v, kp in zip(k_blocks, v_blocks, k_pos_blocks):
-        state = ring_step_ref(q, q_pos, k, v, kp, state, scale, causal)
+    if k_doc_blocks is None:
+        k_doc_blocks = [None] * len(k_blocks)
+    for k, v, kp, kd in zip(k_blocks, v_blocks, k_pos_blocks, k_doc_blocks):
+        state = ring_step_ref(q, q_pos, k, v, kp, state, scale, causal, q_doc, kd)
     out, lse = finalize(*state)
     if return_state:
         return out, lse, state
     return out, lse
 
 
-def brute_attention(q, q_pos, k, v, k_pos, scale=None, causal=True):
+def brute_attention(q, q_pos, k, v, k_pos, scale=None, causal=True, q_doc=None, k_doc=None):
     """Ordinary (non-blockwise) masked softmax attention over all keys at once.
 
     For each query: lse = log sum_j exp(s_ij) over visible j (computed with the
@@ -220,6 +265,7 @@ def brute_attention(q, q_pos, k, v, k_pos, scale=None, causal=True):
     q, k, v, q_pos, k_pos = _check(q, k, v, q_pos, k_pos)
     h_q, n_q, d = q.shape
     h_kv, n_k, _ = k.shape
+    q_doc, k_doc = _docs(q_doc, k_doc, n_q, n_k)
     g = h_q // h_kv
     if scale is None:
         scale = default_scale(d)
@@ -231,8 +277,10 @@ def brute_attention(q, q_pos, k, v, k_pos, scale=None, causal=True):
         kv = h // g
         for rows in _row_chunks(n_q, n_k):
             s = scale * (q[h, rows] @ k[kv].T)
-            if causal:
-                s = np.where(k_pos[None, :] <= q_pos[rows, None], s, -np.inf)
+            visible = _visible(q_pos[rows], k_pos, causal,
+                               None if q_doc is None else q_doc[rows], k_doc)
+            if visible is not None:
+                s = np.where(visible, s, -np.inf)
             mx = s.max(axis=1)
             has = np.isfinite(mx)
             shift = np.where(has, mx, 0.0)

@@ -41,3 +41,20 @@ def rank_positions(T, n_cp, r, layout):
 def ring_block_owner(n_cp, r, step):
     """Rank whose block rank r holds at ring step ``step``."""
     return (r - step) % n_cp
+
+
+def document_start_of(pos, doc_starts):
+    """int32 first global position of the document holding each position.
+
+    Packed sequences (Zero to Frontier, "Splitting the sequence, and the one
+    layer that objects": gathered keys and values make document masks easy):
+    ``doc_starts`` are the increasing first positions of the documents, the
+    first one 0.  A key is visible to a query under the document mask exactly
+    when its position lies between the query's document start and the query
+    itself, which is the lower bound the all-gather entry point takes.
+    """
+    starts = np.asarray(doc_starts, dtype=np.int64)
+    pos = np.asarray(pos, dtype=np.int64)
+    if starts.size == 0 or starts[0] != 0 or np.any(np.diff(starts) <= 0):
+        raise ValueError("doc_starts must increase from 0")
+    return starts[np.searchsorted(starts, pos, side="right") - 1].astype(np.int32)

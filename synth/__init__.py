@@ -104,3 +104,29 @@ def case_dout(case, q_pos):
     ``[h_q][len(q_pos)][d_k]`` float32 holding values of the workload's dtype."""
     return global_rows(case.seed, TENSOR_DOUT, case.h_q, case.d_k, q_pos, 1.0,
                        case.dtype == "bf16")
+
+
+TENSOR_DOCS = 4
+
+
+def document_starts(T, seed, min_len=512, max_len=32768):
+    """First global positions of the documents packed into a T-token sequence.
+
+    Packed-sequence recipe: document lengths are drawn log-uniformly between
+    ``min_len`` and ``max_len`` tokens from
+    ``numpy.random.Generator(PCG64(SeedSequence([seed, 4])))`` and laid end to
+    end from position 0; the last document is cut at T.  Returns an
+    increasing int64 array whose first entry is 0.
+    """
+    if T <= 0:
+        return np.zeros(0, dtype=np.int64)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, TENSOR_DOCS])))
+    starts = [0]
+    lo, hi = np.log(min_len), np.log(max_len)
+    while True:
+        n = int(round(float(np.exp(rng.uniform(lo, hi)))))
+        nxt = starts[-1] + max(1, n)
+        if nxt >= T:
+            break
+        starts.append(nxt)
+    return np.asarray(starts, dtype=np.int64)
