@@ -15,8 +15,9 @@ import test_oracle_counts as tc
 import test_oracle_layouts as tl
 
 
-def _bp(q, q_pos, k, v, k_pos, scale=None, causal=True, mistake=None):
-    """The block partial with one planted mistake."""
+def _bp(q, q_pos, k, v, k_pos, scale=None, causal=True, q_doc=None, k_doc=None, mistake=None):
+    """The block partial with one planted mistake (these pins use no documents)."""
+    assert q_doc is None and k_doc is None
     q = np.asarray(q, np.float64); k = np.asarray(k, np.float64); v = np.asarray(v, np.float64)
     q_pos = np.asarray(q_pos); k_pos = np.asarray(k_pos)
     h_q, n_q, d = q.shape
