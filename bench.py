@@ -81,6 +81,14 @@ def visible_pairs(q_pos, k_pos):
     return int(np.searchsorted(ks, np.asarray(q_pos, dtype=np.int64), side="right").sum())
 
 
+def visible_pairs_docs(q_pos, q_lo, k_pos):
+    """Pairs with q_lo[i] <= k_pos[j] <= q_pos[i] (the document mask)."""
+    ks = np.sort(np.asarray(k_pos, dtype=np.int64))
+    hi = np.searchsorted(ks, np.asarray(q_pos, dtype=np.int64), side="right")
+    lo = np.searchsorted(ks, np.asarray(q_lo, dtype=np.int64), side="left")
+    return int(np.maximum(hi - lo, 0).sum())
+
+
 def build_share(case, rank, device):
     L = ra.layouts
     q_pos = L.rank_positions(case.T, case.n_cp, rank, case.layout)
@@ -178,6 +186,8 @@ def main():
     ap.add_argument("--no-side-stream", action="store_true")
     ap.add_argument("--no-allgather", action="store_true",
                     help="skip timing the all-gather form (every block resident, one launch)")
+    ap.add_argument("--no-docs", action="store_true",
+                    help="skip the document-masked all-gather side line")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the backward of the share (bf16, d_k = 128)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -291,6 +301,31 @@ def main():
             "pct_of_bf16_peak": 100.0 * flops / ag_s / 1e12 / PEAK_BF16_TFLOPS,
             "launches_per_step": 1 if case.dtype == "bf16" and case.d_k == 128 else case.n_cp,
             "rank": ranks[-1],
+        }
+    if not args.no_allgather and not args.no_docs and case.causal:
+        # The same share under a document mask: the sequence packed from
+        # seeded documents of 512 to 32768 tokens (synth.document_starts),
+        # each query seeing only the earlier tokens of its own document.
+        # FLOPs are those of the pairs visible under that mask.
+        starts = synth.document_starts(case.T, case.seed)
+        lo = ra.layouts.document_start_of(share["q_pos"], starts)
+        doc_pairs = sum(visible_pairs_docs(share["q_pos"], lo, kp) for kp in share["k_pos"])
+        doc_flops = 4 * case.d_k * case.h_q * doc_pairs
+        agd = ra.AllGather(share["gq"], share["gq_pos"], share["gk"], share["gv"], share["gk_pos"],
+                           q_doc_start=torch.from_numpy(lo).to(dev))
+        for _ in range(args.warmup):
+            agd()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            agd()
+        torch.cuda.synchronize()
+        agd_s = (time.perf_counter() - t0) / args.steps
+        result["allgather_docs"] = {
+            "value": doc_flops / agd_s / 1e12, "unit": "TFLOP/s", "ms_per_step": agd_s * 1e3,
+            "pct_of_bf16_peak": 100.0 * doc_flops / agd_s / 1e12 / PEAK_BF16_TFLOPS,
+            "documents": int(len(starts)), "visible_flops": doc_flops,
+            "entry_point": "ra_forward_allgather_docs", "rank": ranks[-1],
         }
     if not args.no_backward and case.dtype == "bf16" and case.d_k == 128:
         result["backward"] = time_backward(share, fwd, flops, args.steps, args.warmup, ranks[-1])

@@ -61,7 +61,8 @@ enum {
   RA_ERR_ALIGN = -4,     /* a pointer breaks the alignment rules above */
   RA_ERR_WORKSPACE = -5, /* workspace smaller than ra_forward_workspace_bytes() */
   RA_ERR_HIP = -6,       /* a HIP runtime call or launch failed */
-  RA_ERR_ARG = -7        /* scale not finite and > 0 (or 0 for the default) */
+  RA_ERR_ARG = -7        /* scale not finite and > 0 (or 0 for the default); causal not 1
+                            with a document mask */
 };
 
 enum { RA_BF16 = 0, RA_F32 = 1 };
@@ -149,6 +150,30 @@ ra_status ra_forward_allgather(const ra_problem* p, int32_t n_cp, const void* q,
                                const void* const* v_blocks, const int32_t* const* k_pos_blocks,
                                void* workspace, size_t ws_bytes, float* out, float* lse,
                                int64_t* work, void* stream);
+
+/*
+ * The all-gather form under a document mask (packed sequences: Zero to
+ * Frontier, "distributed/context-expert", section "Splitting the sequence,
+ * and the one layer that objects", gives easy support of arbitrary masks such
+ * as document masks as one reason to gather the keys and values first).  As
+ * ra_forward_allgather, plus q_doc_start: a DEVICE int32[n_q] holding, for
+ * each query, the first global position of the document it belongs to.  Key
+ * j is visible to query i iff q_doc_start[i] <= k_pos[j] <= q_pos[i], which
+ * for documents packed one after another is "the same document and not
+ * later".  Requirements: p->causal == 1 (RA_ERR_ARG otherwise);
+ * q_doc_start[i] <= q_pos[i] and non-decreasing in i (true for packed
+ * documents, since q_pos increases); 4-byte aligned (RA_ERR_ALIGN); not
+ * NULL when n_q > 0 (RA_ERR_NULL).  Values breaking the ordering give
+ * unspecified results but no out-of-bounds access.  A query whose document
+ * has no key among the blocks gets out = 0 and lse = -inf.  No tile counters
+ * (the causal work counts of ra_forward describe the causal mask alone).
+ * Asynchronous on stream; the caller owns every buffer.
+ */
+ra_status ra_forward_allgather_docs(const ra_problem* p, int32_t n_cp, const void* q,
+                                    const int32_t* q_pos, const int32_t* q_doc_start,
+                                    const void* const* k_blocks, const void* const* v_blocks,
+                                    const int32_t* const* k_pos_blocks, void* workspace,
+                                    size_t ws_bytes, float* out, float* lse, void* stream);
 
 /*
  * Backward of the rank share (Zero to Frontier, "distributed/context-expert",

@@ -25,7 +25,7 @@ RA_BF16, RA_F32 = 0, 1
 
 SYMBOLS = (
     "ra_state_init", "ra_step", "ra_finalize", "ra_forward_workspace_bytes", "ra_forward",
-    "ra_forward_allgather_workspace_bytes", "ra_forward_allgather",
+    "ra_forward_allgather_workspace_bytes", "ra_forward_allgather", "ra_forward_allgather_docs",
     "ra_backward_prep", "ra_backward_workspace_bytes", "ra_backward_step",
     "ra_backward_share_workspace_bytes", "ra_backward_share", "ra_tile_shape", "ra_status_string", "ra_abi_version",
 )
@@ -71,6 +71,9 @@ def lib():
     L.ra_forward_allgather_workspace_bytes.restype = ctypes.c_size_t
     L.ra_forward_allgather.argtypes = [P, i32, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                        ctypes.POINTER(vp), vp, ctypes.c_size_t, vp, vp, vp, vp]
+    L.ra_forward_allgather_docs.argtypes = [P, i32, vp, vp, vp, ctypes.POINTER(vp),
+                                            ctypes.POINTER(vp), ctypes.POINTER(vp), vp,
+                                            ctypes.c_size_t, vp, vp, vp]
     L.ra_backward_prep.argtypes = [P, vp, vp, vp, vp]
     L.ra_backward_workspace_bytes.argtypes = [P]
     L.ra_backward_workspace_bytes.restype = ctypes.c_size_t
@@ -86,7 +89,8 @@ def lib():
     L.ra_status_string.restype = ctypes.c_char_p
     L.ra_abi_version.argtypes = []
     for name in ("ra_state_init", "ra_step", "ra_finalize", "ra_forward", "ra_tile_shape",
-                 "ra_forward_allgather", "ra_backward_prep", "ra_backward_step",
+                 "ra_forward_allgather", "ra_forward_allgather_docs", "ra_backward_prep",
+                 "ra_backward_step",
                  "ra_backward_share",
                  "ra_abi_version"):
         getattr(L, name).restype = i32
@@ -238,11 +242,18 @@ def allgather_workspace_bytes(p):
 
 
 class AllGather:
-    """A prepared ra_forward_allgather call (every key/value block resident)."""
+    """A prepared ra_forward_allgather call (every key/value block resident).
+    With ``q_doc_start`` (int32 per query: the first global position of its
+    document) it is ra_forward_allgather_docs, the document-masked form,
+    which reports no tile counters."""
 
     def __init__(self, q, q_pos, k_blocks, v_blocks, k_pos_blocks, causal=True, scale=None,
-                 count_work=True):
-        _need_gpu(q, q_pos, *k_blocks, *v_blocks, *k_pos_blocks)
+                 count_work=True, q_doc_start=None):
+        _need_gpu(q, q_pos, *k_blocks, *v_blocks, *k_pos_blocks,
+                  *([] if q_doc_start is None else [q_doc_start]))
+        self.q_doc_start = q_doc_start
+        if q_doc_start is not None:
+            count_work = False
         n_cp = len(k_blocks)
         if not (n_cp == len(v_blocks) == len(k_pos_blocks)) or n_cp < 1:
             raise ValueError("need n_cp >= 1 blocks of k, v and k_pos")
@@ -262,17 +273,26 @@ class AllGather:
 
     def __call__(self, stream=None):
         q, q_pos = self.keep[0], self.keep[1]
-        _check(lib().ra_forward_allgather(
-            ctypes.byref(self.p), self.n_cp, _ptr(q), _ptr(q_pos), self.kp, self.vp, self.pp,
-            _ptr(self.ws), ctypes.c_size_t(self.ws.numel() if self.ws is not None else 0),
-            _ptr(self.out), _ptr(self.lse), _ptr(self.work), _stream(stream)),
-            "ra_forward_allgather")
+        ws_n = ctypes.c_size_t(self.ws.numel() if self.ws is not None else 0)
+        if self.q_doc_start is None:
+            _check(lib().ra_forward_allgather(
+                ctypes.byref(self.p), self.n_cp, _ptr(q), _ptr(q_pos), self.kp, self.vp, self.pp,
+                _ptr(self.ws), ws_n, _ptr(self.out), _ptr(self.lse), _ptr(self.work),
+                _stream(stream)), "ra_forward_allgather")
+        else:
+            _check(lib().ra_forward_allgather_docs(
+                ctypes.byref(self.p), self.n_cp, _ptr(q), _ptr(q_pos), _ptr(self.q_doc_start),
+                self.kp, self.vp, self.pp, _ptr(self.ws), ws_n, _ptr(self.out), _ptr(self.lse),
+                _stream(stream)), "ra_forward_allgather_docs")
         return self.out, self.lse
 
 
-def forward_allgather(q, q_pos, k_blocks, v_blocks, k_pos_blocks, causal=True, scale=None):
-    """The rank share with every block resident: returns (out, lse, work[3] tensor)."""
-    f = AllGather(q, q_pos, k_blocks, v_blocks, k_pos_blocks, causal, scale)
+def forward_allgather(q, q_pos, k_blocks, v_blocks, k_pos_blocks, causal=True, scale=None,
+                      q_doc_start=None):
+    """The rank share with every block resident: returns (out, lse, work[3] tensor,
+    or None under a document mask given by ``q_doc_start``)."""
+    f = AllGather(q, q_pos, k_blocks, v_blocks, k_pos_blocks, causal, scale,
+                  q_doc_start=q_doc_start)
     out, lse = f()
     return out, lse, f.work
 

@@ -59,6 +59,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kPosRowNone = (int)0x80000000;
 constexpr int kPosRowAll = 0x7ffffffe;
+constexpr int kPosLoNone = (int)0x80000000;  // no lower bound on a row's visible keys
 // Word 3 of a raw (untyped, stride-0) buffer resource on gfx9: 32-bit data
 // format; offsets at or past num_records read as zero.
 constexpr int kBufferFlags = 0x00020000;
@@ -137,7 +138,7 @@ __device__ __forceinline__ void dma_words_to_lds(const i32x4& rsrc, uint32_t lds
 __device__ __forceinline__ int k_chunk_off(int r, int c) { return r * 256 + 16 * (c ^ (r & 15)); }
 __device__ __forceinline__ int v_chunk_off(int r, int c) { return r * 256 + 16 * (c ^ (4 * (r & 3))); }
 
-template <bool READ, bool FINAL>
+template <bool READ, bool FINAL, bool DOCS = false>
 struct Step {
   const StepArgs& a;
   Smem& sm;
@@ -149,6 +150,15 @@ struct Step {
   int n_iter = 0, n_own = 0;
   bool wave_valid = false;
   int qmin_w = 0, qmax_w = 0, qp = 0;
+  // Lower bounds of the visible key positions (document starts): this
+  // lane's row, the wave's smallest and largest, the workgroup's smallest.
+  int qlo = kPosLoNone, qlo_min_w = kPosLoNone, qlo_max_w = kPosLoNone, qlo_min_wg = kPosLoNone;
+  // First key tile the workgroup visits in the current block (even, so each
+  // group keeps its tile parity); 0 without lower bounds.
+  int j0 = 0;
+  int lo_vis_w = 0, lo_full_w = 0;  // this wave's first visible / fully visible tile
+  // Without document masks all of this folds away to the plain causal case.
+  __device__ __forceinline__ int tile0() const { return DOCS ? j0 : 0; }
   float c2 = 0.f;
 
   // Buffer resources of this head's K, V and key positions: loads past the
@@ -238,14 +248,14 @@ struct Step {
 
   // The first two K tiles and position tiles of a block (own tiles 0 and 1),
   // into K stages 0, 1 and position stages 0, 1.
-  __device__ __forceinline__ void load_block_head(int n_own_b) {
+  __device__ __forceinline__ void load_block_head(int n_own_b, int j0_b) {
     if (n_own_b > 0) {
-      load_k_tile(grp, 0);
-      load_pos(grp, 0);
+      load_k_tile(j0_b + grp, 0);
+      load_pos(j0_b + grp, 0);
     }
     if (n_own_b > 1) {
-      load_k_tile(2 + grp, 1);
-      load_pos(2 + grp, 1);
+      load_k_tile(j0_b + 2 + grp, 1);
+      load_pos(j0_b + 2 + grp, 1);
     }
   }
 
@@ -291,7 +301,8 @@ struct Step {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int lim = nvalid - 32 * kb - (16 * (r >> 3) + (r & 7));
-      const bool vis = kp4[r >> 2][r & 3] <= qpe && h8 < lim;
+      const int kp = kp4[r >> 2][r & 3];
+      const bool vis = kp <= qpe && (!DOCS || kp >= qlo) && h8 < lim;
       s[r] = vis ? s[r] : -INFINITY;
     }
   }
@@ -345,13 +356,13 @@ struct Step {
     // The batch's DMA instructions are spread over the phase: a wave that
     // issues them back to back stalls on the CU's load path (64 B/clk).
     const bool has_k = s + 2 < n_own, has_v = s + 1 < n_own;
-    if (has_k) load_k_tile(2 * (s + 2) + grp, s & 1);
+    if (has_k) load_k_tile(tile0() + 2 * (s + 2) + grp, s & 1);
     __builtin_amdgcn_sched_barrier(0);
 
-    const int j = 2 * s + grp;
+    const int j = tile0() + 2 * s + grp;
     const int nvalid = min(BN, n_k - j * BN);
-    const bool skip = j >= n_vis_w;
-    const bool full = j < n_full_w;
+    const bool skip = j >= n_vis_w || (DOCS && j < lo_vis_w);
+    const bool full = j < n_full_w && (!DOCS || j >= lo_full_w);
     if (!skip) {
       if (full) ++cnt_full; else ++cnt_masked;
     }
@@ -380,11 +391,11 @@ struct Step {
     }
     const float muse = (m2 == -INFINITY) ? 0.f : m2;
     __builtin_amdgcn_sched_barrier(0);
-    if (has_v) load_v_tile(2 * (s + 1) + grp, (s + 1) & 1);
+    if (has_v) load_v_tile(tile0() + 2 * (s + 1) + grp, (s + 1) & 1);
     __builtin_amdgcn_sched_barrier(0);
     exp_pack(sc[0], muse, pp[0]);
     __builtin_amdgcn_sched_barrier(0);
-    if (has_k) load_pos(2 * (s + 2) + grp, (s + 2) % 3);
+    if (has_k) load_pos(tile0() + 2 * (s + 2) + grp, (s + 2) % 3);
     __builtin_amdgcn_sched_barrier(0);
     exp_pack(sc[1], muse, pp[1]);
     pin_softmax();
@@ -438,6 +449,16 @@ struct Step {
     }
     qmax_wg = causal ? a.q_pos[min(row0_wg + ROWS, n_q) - 1] : kPosRowAll;
     qp = row < n_q ? (causal ? a.q_pos[row] : kPosRowAll) : kPosRowNone;
+    if (DOCS) {
+      // Lower bounds never decrease along the rows (documents follow the
+      // positions), so first and last rows give the extremes.
+      qlo_min_wg = a.q_lo[row0_wg];
+      if (wave_valid) {
+        qlo_min_w = __builtin_amdgcn_readfirstlane(a.q_lo[row0]);
+        qlo_max_w = __builtin_amdgcn_readfirstlane(a.q_lo[min(row0 + WAVE_ROWS, n_q) - 1]);
+      }
+      qlo = row < n_q ? a.q_lo[row] : kPosLoNone;
+    }
     count = a.work != nullptr && head == 0 && wave_valid;
     srow = (size_t)head * n_q + row;
   }
@@ -446,24 +467,39 @@ struct Step {
   // Positions increase, so the key tiles the workgroup sees form a prefix of
   // the block (n_iter tiles), and so do the tiles this wave sees completely
   // (n_full_w) and at all (n_vis_w).
+  // With lower bounds (document starts) the tiles seen also start late:
+  // those whose last key lies before a bound form a prefix too, so each set
+  // is a range [lo, end) of tiles.  The workgroup visits [j0, n_iter_end),
+  // j0 its first visible tile rounded down to even; n_iter counts from j0.
   struct Classes {
-    int n_iter, n_full_w, n_vis_w;
+    int n_iter, n_full_w, n_vis_w, j0, lo_full_w, lo_vis_w;
   };
   __device__ __forceinline__ Classes classes_of(const int32_t* k_pos) const {
     const int nkt = (n_k + BN - 1) / BN;
-    Classes c{nkt, 0, 0};
+    Classes c{nkt, 0, 0, 0, 0, 0};
     if (causal) {
-      int ci = 0, cf = 0, cv = 0;
+      int ci = 0, cf = 0, cv = 0, li = 0, lf = 0, lv = 0;
       for (int j = lane; j < nkt; j += 64) {
         const int kf = k_pos[j * BN];
         const int kl = k_pos[min(j * BN + BN, n_k) - 1];
         ci += kf <= qmax_wg ? 1 : 0;
         cf += kl <= qmin_w ? 1 : 0;
         cv += kf <= qmax_w ? 1 : 0;
+        if (DOCS) {
+          li += kl < qlo_min_wg ? 1 : 0;
+          lf += kf < qlo_max_w ? 1 : 0;
+          lv += kl < qlo_min_w ? 1 : 0;
+        }
       }
-      c.n_iter = __builtin_amdgcn_readfirstlane(wave_sum_i(ci));
+      const int n_end = __builtin_amdgcn_readfirstlane(wave_sum_i(ci));
       c.n_full_w = wave_valid ? __builtin_amdgcn_readfirstlane(wave_sum_i(cf)) : 0;
       c.n_vis_w = wave_valid ? __builtin_amdgcn_readfirstlane(wave_sum_i(cv)) : 0;
+      if (DOCS) {
+        c.j0 = __builtin_amdgcn_readfirstlane(wave_sum_i(li)) & ~1;
+        c.lo_full_w = __builtin_amdgcn_readfirstlane(wave_sum_i(lf));
+        c.lo_vis_w = __builtin_amdgcn_readfirstlane(wave_sum_i(lv));
+      }
+      c.n_iter = DOCS ? max(0, n_end - c.j0) : n_end;
     } else {
       c.n_full_w = c.n_vis_w = wave_valid ? nkt : 0;
     }
@@ -476,6 +512,9 @@ struct Step {
     n_iter = c.n_iter;
     n_full_w = c.n_full_w;
     n_vis_w = c.n_vis_w;
+    j0 = c.j0;
+    lo_full_w = c.lo_full_w;
+    lo_vis_w = c.lo_vis_w;
     // tiles of this group among all key tiles, and among the visited ones
     n_kt_g = (n_kt - grp + 1) / 2;
     n_own = own_tiles(n_iter);
@@ -486,7 +525,7 @@ struct Step {
   // whether this group already issued the loads of its first tiles.
   const void* nxt_k = nullptr;
   const int32_t* nxt_pos = nullptr;
-  int nxt_own = 0, nxt_kvh = 0;
+  int nxt_own = 0, nxt_kvh = 0, nxt_j0 = 0;
   bool head_issued = false;
 
   // Issued by the last GEMM phase of a block (PV only: the K stages are idle
@@ -496,7 +535,7 @@ struct Step {
     if (nxt_k == nullptr || nxt_own == 0) return;
     krs = buffer_rsrc((const uint16_t*)nxt_k + ((size_t)nxt_kvh * n_k) * D, n_k * D * 2);
     prs = buffer_rsrc(nxt_pos, n_k * 4);
-    load_block_head(nxt_own);
+    load_block_head(nxt_own, DOCS ? nxt_j0 : 0);
     head_issued = true;
   }
 
@@ -554,12 +593,12 @@ struct Step {
       krs = buffer_rsrc(kbase, n_k * D * 2);
       vrs = buffer_rsrc(vbase, n_k * D * 2);
       prs = buffer_rsrc(k_pos, n_k * 4);
-      if (!head_issued) load_block_head(n_own);
+      if (!head_issued) load_block_head(n_own, tile0());
       head_issued = false;
       // V of own tile 0 is first read two phases on; the softmax phase of
       // own tile 0 waits for it.  Everything older must land now.
       if (n_own > 0) {
-        load_v_tile(grp, 0);
+        load_v_tile(tile0() + grp, 0);
         wait_loads(4);
       } else {
         wait_loads(0);
@@ -689,6 +728,7 @@ struct Step {
         nxt_k = ma.k[b + 1];
         nxt_pos = ma.k_pos[b + 1];
         nxt_own = own_tiles(cur.n_iter);
+        nxt_j0 = cur.j0;
       } else {
         nxt_k = nullptr;
         nxt_pos = nullptr;
@@ -718,7 +758,9 @@ void step_kernel_fast(const StepArgs a) {
   }
 }
 
-// All-gather form: every key/value block resident, one launch.
+// All-gather form: every key/value block resident, one launch.  DOCS: each
+// query's keys are also bounded below by its document start (a.q_lo).
+template <bool DOCS>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void allgather_kernel_fast(const MultiArgs ma) {
   __shared__ Smem sm;
@@ -727,7 +769,7 @@ void allgather_kernel_fast(const MultiArgs ma) {
   const int head = ma.s.head_of[u % ma.s.h_q];
   const int p = u / ma.s.h_q;
   const int t_hi = ma.s.n_qt - 1 - p, t_lo = p;
-  Step<false, true> s(ma.s, sm, tid);
+  Step<false, true, DOCS> s(ma.s, sm, tid);
   s.run_all(ma, t_hi, head);
   if (t_lo < t_hi) {
     __syncthreads();
@@ -739,7 +781,10 @@ void allgather_kernel_fast(const MultiArgs ma) {
 
 hipError_t launch_allgather_fast(const MultiArgs& ma, hipStream_t stream) {
   dim3 grid((unsigned)(ma.s.n_pairs * ma.s.h_q)), block(fast::THREADS);
-  hipLaunchKernelGGL(fast::allgather_kernel_fast, grid, block, 0, stream, ma);
+  if (ma.s.q_lo != nullptr)
+    hipLaunchKernelGGL(fast::allgather_kernel_fast<true>, grid, block, 0, stream, ma);
+  else
+    hipLaunchKernelGGL(fast::allgather_kernel_fast<false>, grid, block, 0, stream, ma);
   return hipGetLastError();
 }
 

@@ -155,7 +155,7 @@ const char* ra_status_string(ra_status s) {
     case RA_ERR_ALIGN: return "misaligned pointer (16 B for q,k,v,o,out,workspace; 4 B positions,m,l,lse; 8 B work)";
     case RA_ERR_WORKSPACE: return "workspace too small";
     case RA_ERR_HIP: return "HIP runtime call or kernel launch failed";
-    case RA_ERR_ARG: return "invalid argument (scale must be finite and > 0, causal 0 or 1)";
+    case RA_ERR_ARG: return "invalid argument (scale must be finite and > 0, causal 0 or 1; causal 1 with a document mask)";
     default: return "unknown status";
   }
 }
@@ -571,11 +571,17 @@ size_t ra_forward_allgather_workspace_bytes(const ra_problem* p) {
   return allgather_ws_bytes(p);
 }
 
-ra_status ra_forward_allgather(const ra_problem* p, int32_t n_cp, const void* q,
-                               const int32_t* q_pos, const void* const* k_blocks,
-                               const void* const* v_blocks, const int32_t* const* k_pos_blocks,
-                               void* workspace, size_t ws_bytes, float* out, float* lse,
-                               int64_t* work, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The all-gather form, with an optional per-query lower bound on the visible
+// key positions (q_lo, the document start under a document mask).
+ra_status allgather_impl(const ra_problem* p, int32_t n_cp, const void* q, const int32_t* q_pos,
+                         const int32_t* q_lo, const void* const* k_blocks,
+                         const void* const* v_blocks, const int32_t* const* k_pos_blocks,
+                         void* workspace, size_t ws_bytes, float* out, float* lse, int64_t* work,
+                         void* stream) {
   ra_status st = check_problem(p);
   if (st != RA_OK) return st;
   if (n_cp < 1 || n_cp > ra::kMaxBlocks) return RA_ERR_SHAPE;
@@ -610,6 +616,7 @@ ra_status ra_forward_allgather(const ra_problem* p, int32_t n_cp, const void* q,
   fill_args(p, &a);
   a.q = q;
   a.q_pos = q_pos;
+  a.q_lo = q_lo;
   a.out = out;
   a.lse = lse;
   a.work = reinterpret_cast<unsigned long long*>(work);
@@ -642,6 +649,35 @@ ra_status ra_forward_allgather(const ra_problem* p, int32_t n_cp, const void* q,
     if (st != RA_OK) return st;
   }
   return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ra_status ra_forward_allgather(const ra_problem* p, int32_t n_cp, const void* q,
+                               const int32_t* q_pos, const void* const* k_blocks,
+                               const void* const* v_blocks, const int32_t* const* k_pos_blocks,
+                               void* workspace, size_t ws_bytes, float* out, float* lse,
+                               int64_t* work, void* stream) {
+  return allgather_impl(p, n_cp, q, q_pos, nullptr, k_blocks, v_blocks, k_pos_blocks, workspace,
+                        ws_bytes, out, lse, work, stream);
+}
+
+ra_status ra_forward_allgather_docs(const ra_problem* p, int32_t n_cp, const void* q,
+                                    const int32_t* q_pos, const int32_t* q_doc_start,
+                                    const void* const* k_blocks, const void* const* v_blocks,
+                                    const int32_t* const* k_pos_blocks, void* workspace,
+                                    size_t ws_bytes, float* out, float* lse, void* stream) {
+  ra_status st = check_problem(p);
+  if (st != RA_OK) return st;
+  if (p->causal != 1) return RA_ERR_ARG;
+  if (p->n_q > 0) {
+    if (!q_doc_start) return RA_ERR_NULL;
+    if (!aligned4(q_doc_start)) return RA_ERR_ALIGN;
+  }
+  return allgather_impl(p, n_cp, q, q_pos, q_doc_start, k_blocks, v_blocks, k_pos_blocks,
+                        workspace, ws_bytes, out, lse, nullptr, stream);
 }
 
 }  // extern "C"

@@ -33,6 +33,9 @@ struct StepArgs {
   float* out;
   float* lse;
   unsigned long long* work;  // int64[3] {full, masked, skipped} or null
+  // Per-query lower bound of the visible key positions (the first position
+  // of the query's document under a document mask), or null for none.
+  const int32_t* q_lo;
   int32_t n_q, n_k, h_q, h_kv, causal;
   int32_t n_qt;              // query tiles of kRowsPerGroup rows
   int32_t n_pairs;           // workgroups per head: tile t is paired with tile n_qt-1-t

@@ -68,6 +68,7 @@ constexpr int kPosHidden = 0x7fffffff;        // key slot past the block's end
 constexpr int kPosAlways = (int)0x80000000;   // key visible to every row (non-causal)
 constexpr int kPosRowNone = (int)0x80000000;  // query row past the end: sees no causal key
 constexpr int kPosRowAll = 0x7ffffffe;        // non-causal query row
+constexpr int kPosLoNone = (int)0x80000000;   // no lower bound on a row's visible keys
 
 // Accumulator row i of a 32-key block holds key sigma(i): bits 2 and 3 swapped.
 __device__ __forceinline__ int sigma(int i) {
@@ -331,15 +332,20 @@ struct Smem {
   int32_t pos[3][kKeysPerTile];
 };
 
-// Masks hidden keys of one 32-key half to -inf.  Accumulator register r of
-// half kb holds tile key 32kb + 8h + 16(r/8) + r%8.
-__device__ __forceinline__ void apply_mask(f32x16& s, const int32_t* pos, int kb, int h, int qp) {
+// Masks hidden keys of one 32-key half to -inf: those after the query (qp)
+// and those before its lower bound (qlo, the document start).  Accumulator
+// register r of half kb holds tile key 32kb + 8h + 16(r/8) + r%8.
+__device__ __forceinline__ void apply_mask(f32x16& s, const int32_t* pos, int kb, int h, int qp,
+                                           int qlo) {
   i32x4 kp4[4];
 #pragma unroll
   for (int x = 0; x < 4; ++x)
     kp4[x] = *(const i32x4*)&pos[32 * kb + 8 * h + 16 * (x >> 1) + 4 * (x & 1)];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) s[r] = (kp4[r >> 2][r & 3] <= qp) ? s[r] : -INFINITY;
+  for (int r = 0; r < 16; ++r) {
+    const int kp = kp4[r >> 2][r & 3];
+    s[r] = (kp <= qp && kp >= qlo) ? s[r] : -INFINITY;
+  }
 }
 
 // Position of key gk of the block as the tile masks see it (branch-free:
@@ -375,6 +381,9 @@ struct QTile {
   int n_iter = 0;
   bool wave_valid = false;
   int qmin_w = 0, qmax_w = 0, qp = 0;
+  // Lower bounds of the visible key positions: this lane's row, and the
+  // smallest and largest over the wave's rows (kPosLoNone without a bound).
+  int qlo = kPosLoNone, qlo_min_w = kPosLoNone, qlo_max_w = kPosLoNone;
   float c2 = 0.f;
 
   typename Tr::Q q;
@@ -440,16 +449,16 @@ struct QTile {
     const int last_valid = min(j0 + kKeysPerTile, n_k) - 1 - j0;
     const int kmin = pos[0], kmax = pos[last_valid];
     const bool ragged = j0 + kKeysPerTile > n_k;
-    const bool skip = !wave_valid || kmin > qmax_w;
-    const bool full = kmax <= qmin_w;
+    const bool skip = !wave_valid || kmin > qmax_w || kmax < qlo_min_w;
+    const bool full = kmax <= qmin_w && kmin >= qlo_max_w;
     if (!skip) {
       if (full) ++cnt_full; else ++cnt_masked;
     }
     if (skip || !full || ragged) {
       // A skipped tile is masked completely: P = 0, nothing changes.
       const int qpe = skip ? kPosRowNone : qp;
-      apply_mask(s_cur[0], pos, 0, h, qpe);
-      apply_mask(s_cur[1], pos, 1, h, qpe);
+      apply_mask(s_cur[0], pos, 0, h, qpe, qlo);
+      apply_mask(s_cur[1], pos, 1, h, qpe, qlo);
     }
 
     // ---- one branch-free block: MFMA stream and softmax interleave ----
@@ -521,6 +530,13 @@ struct QTile {
     }
     const int row = row0 + col;
     qp = row < n_q ? (causal ? a.q_pos[row] : kPosRowAll) : kPosRowNone;
+    if (a.q_lo != nullptr && wave_valid) {
+      // Lower bounds never decrease along the rows (documents follow the
+      // positions), so the wave's first and last rows give its extremes.
+      qlo_min_w = a.q_lo[row0];
+      qlo_max_w = a.q_lo[min(row0 + kRowsPerWave, n_q) - 1];
+      qlo = row < n_q ? a.q_lo[row] : kPosLoNone;
+    }
 
     kbase = (const E*)a.k + ((size_t)kvh * n_k) * D;
     vbase = (const E*)a.v + ((size_t)kvh * n_k) * D;

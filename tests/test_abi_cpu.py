@@ -139,6 +139,26 @@ def test_allgather_checks():
     assert L.ra_forward_allgather(*args(pf, 2, ctypes.c_void_p(FAKE + 4), need)) == ALIGN
 
 
+def test_allgather_docs_checks():
+    """The document-masked all-gather entry point refuses, before any device
+    work, a non-causal problem, a missing or misaligned document-start array,
+    and whatever ra_forward_allgather refuses."""
+    L = ra.lib()
+    v = ctypes.c_void_p(FAKE)
+    arr = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    p = good()
+    call = lambda p, ncp, docs: L.ra_forward_allgather_docs(
+        ctypes.byref(p), ncp, v, v, docs, arr, arr, arr, None, 0, v, v, None)
+    assert call(good(causal=0), 2, v) == ARG
+    assert call(p, 2, None) == NULL
+    assert call(p, 2, ctypes.c_void_p(FAKE + 2)) == ALIGN
+    assert call(p, 0, v) == SHAPE
+    assert call(p, 65, v) == SHAPE
+    bad = (ctypes.c_void_p * 2)(FAKE, 0)
+    assert L.ra_forward_allgather_docs(ctypes.byref(p), 2, v, v, v, arr, bad, arr, None, 0, v, v,
+                                       None) == NULL
+
+
 def test_backward_checks():
     L = ra.lib()
     v = ctypes.c_void_p(FAKE)

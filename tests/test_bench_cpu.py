@@ -35,3 +35,18 @@ def test_traffic_figure_dropped_when_the_kernel_changes(monkeypatch):
 def test_traffic_figure_missing_summary(monkeypatch, tmp_path):
     monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(tmp_path / "absent.md"))
     assert bench.committed_traffic("llama405b_stage_share") is None
+
+
+def test_document_mask_pair_count_matches_brute_force():
+    import numpy as np
+    import oracle
+    import ring_attention_rank_amd as ra
+    starts = np.array([0, 17, 40, 41, 100, 200])
+    for layout in ("contiguous", "zigzag", "striped"):
+        qp = oracle.positions(256, 4, 1, layout)
+        for s in range(4):
+            kp = oracle.positions(256, 4, s, layout)
+            lo = ra.layouts.document_start_of(qp, starts)
+            same = oracle.doc_ids(kp, starts)[None, :] == oracle.doc_ids(qp, starts)[:, None]
+            brute = int(((kp[None, :] <= qp[:, None]) & same).sum())
+            assert bench.visible_pairs_docs(qp, lo, kp) == brute

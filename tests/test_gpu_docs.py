@@ -1,0 +1,129 @@
+"""Parity of the document-masked all-gather form (ra_forward_allgather_docs:
+packed sequences, a key visible only within the query's document) with the
+float64 oracle, which applies the mask as document ids.  Element by element
+at reduced sizes on every workload, single-token and tile-aligned documents,
+ragged shares on both kernels, block order, the full 405B share on sampled
+rows, and one document reproducing the unmasked result bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ring_attention_rank_amd as ra
+import ring_attention_rank_amd.layouts as L
+import synth
+from gpu_util import TOL, Share, max_err, sample_rows
+from test_gpu_parity import _custom_share, compare
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def doc_inputs(sh, starts, rows=None):
+    qp = sh.q_pos if rows is None else sh.q_pos[rows]
+    q_doc = oracle.doc_ids(qp, starts)
+    k_doc = [oracle.doc_ids(p, starts) for p in sh.k_pos]
+    lo = torch.from_numpy(L.document_start_of(sh.q_pos, starts)).cuda()
+    return q_doc, k_doc, lo
+
+
+def run_docs(sh, lo, order=None):
+    idx = list(range(len(sh.gk))) if order is None else list(order)
+    out, lse, work = ra.forward_allgather(sh.gq, sh.gq_pos, [sh.gk[i] for i in idx],
+                                          [sh.gv[i] for i in idx], [sh.gk_pos[i] for i in idx],
+                                          q_doc_start=lo)
+    torch.cuda.synchronize()
+    assert work is None
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def check_docs(sh, starts, label):
+    print(f"[docs] {label}: {len(starts)} documents", flush=True)
+    q_doc, k_doc, lo = doc_inputs(sh, starts)
+    out, lse = run_docs(sh, lo)
+    ro, rl = oracle.ring_forward_ref(sh.q, sh.q_pos, sh.k, sh.v, sh.k_pos,
+                                     q_doc=q_doc, k_doc_blocks=k_doc)
+    return compare(out, lse, ro, rl, TOL[sh.case.dtype], label)
+
+
+@pytest.mark.parametrize("name,T,n_cp,rank,lens", [
+    ("tiny_f32_contiguous", 1024, 4, 2, (16, 400)),
+    ("llama8b_gqa_zigzag", 4096, 4, 1, (64, 2048)),
+    ("llama70b_stage_share", 8192, 16, 15, (64, 4096)),
+    ("llama405b_stage_share", 8192, 16, 0, (64, 4096)),
+    ("million_striped_mha", 16384, 64, 5, (128, 4096)),
+])
+def test_reduced_configs(name, T, n_cp, rank, lens):
+    case = synth.case_by_name(name)
+    sh = Share(case, rank, T=T, n_cp=n_cp).to_gpu()
+    starts = synth.document_starts(T, case.seed, *lens)
+    check_docs(sh, starts, f"{name}@T{T}/r{rank}")
+
+
+@pytest.mark.parametrize("name", ["llama405b_stage_share", "tiny_f32_contiguous"])
+def test_single_token_and_aligned_documents(name):
+    """Documents of one token, documents that start on wave (32), tile (64)
+    and workgroup (128) boundaries, and one that starts a token past one."""
+    case = synth.case_by_name(name)
+    T, n_cp = (8192, 16) if case.dtype == "bf16" else (1024, 4)
+    sh = Share(case, n_cp - 1, T=T, n_cp=n_cp).to_gpu()
+    starts = np.array(sorted({0, 5, 6, 7, 32, 64, 65, 128, 129, 300, 301, 302, 512, T // 2,
+                              T // 2 + 1, T - 64, T - 3, T - 2, T - 1}))
+    check_docs(sh, starts, f"{name} single-token and aligned documents")
+
+
+@pytest.mark.parametrize("name", ["llama405b_stage_share", "tiny_f32_contiguous"])
+def test_one_document_is_the_unmasked_result(name):
+    case = synth.case_by_name(name)
+    T, n_cp = (8192, 16) if case.dtype == "bf16" else (1024, 4)
+    sh = Share(case, 0, T=T, n_cp=n_cp).to_gpu()
+    _, _, lo = doc_inputs(sh, np.array([0]))
+    out, lse = run_docs(sh, lo)
+    ref_out, ref_lse, _ = ra.forward_allgather(sh.gq, sh.gq_pos, sh.gk, sh.gv, sh.gk_pos)
+    torch.cuda.synchronize()
+    assert np.array_equal(out, ref_out.cpu().numpy()) and np.array_equal(lse, ref_lse.cpu().numpy())
+
+
+@pytest.mark.parametrize("dtype,d_k", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_ragged_random_documents(dtype, d_k):
+    rng = np.random.default_rng(21 + d_k)
+    sh = _custom_share(rng, dtype, d_k, 4, 2, 517, 129, 3)
+    span = int(max(sh.q_pos.max(), max(p.max() for p in sh.k_pos))) + 1
+    starts = np.concatenate([[0], np.sort(rng.choice(np.arange(1, span), 40, replace=False))])
+    check_docs(sh, starts, f"ragged {dtype} d{d_k}")
+
+
+def test_block_order_does_not_matter():
+    case = synth.case_by_name("llama8b_gqa_zigzag")
+    sh = Share(case, 2, T=4096, n_cp=4).to_gpu()
+    _, _, lo = doc_inputs(sh, synth.document_starts(4096, case.seed, 64, 2048))
+    a_out, a_lse = run_docs(sh, lo)
+    b_out, b_lse = run_docs(sh, lo, order=[3, 1, 0, 2])
+    tol = TOL["bf16"]
+    assert max_err(a_out, b_out) <= tol["out"] and max_err(a_lse, b_lse) <= tol["lse"]
+
+
+def test_full_size_sampled():
+    """The 405B stage share (T = 131072, 16 zigzag blocks) with its sequence
+    packed from documents of 512 to 32768 tokens."""
+    case = synth.case_by_name("llama405b_stage_share")
+    sh = Share(case, 0).to_gpu()
+    starts = synth.document_starts(case.T, case.seed)
+    print(f"[docs] 405B share full size, {len(starts)} documents", flush=True)
+    _, _, lo = doc_inputs(sh, starts)
+    out, lse, _ = ra.forward_allgather(sh.gq, sh.gq_pos, sh.gk, sh.gv, sh.gk_pos, q_doc_start=lo)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+    rows = sample_rows(sh.q_pos, seed=9)
+    # also the first rows of documents inside the share, where windows are short
+    firsts = np.searchsorted(sh.q_pos, starts)
+    rows = np.unique(np.concatenate([rows, firsts[firsts < sh.q_pos.size]]))
+    q_doc, k_doc, _ = doc_inputs(sh, starts, rows)
+    ro, rl = oracle.ring_forward_ref(sh.q[:, rows], sh.q_pos[rows], sh.k, sh.v, sh.k_pos,
+                                     q_doc=q_doc, k_doc_blocks=k_doc)
+    idx = torch.from_numpy(rows).cuda()
+    eo = max_err(out[:, idx].cpu().numpy(), ro)
+    el = max_err(lse[:, idx].cpu().numpy(), rl)
+    print(f"[docs] 405B share: out err {eo:.3e} lse err {el:.3e}", flush=True)
+    assert eo <= TOL["bf16"]["out"] and el <= TOL["bf16"]["lse"]
