@@ -718,15 +718,52 @@ struct Step {
     const int kvh = head / (a.h_q / a.h_kv);
     head_issued = false;
     nxt_kvh = kvh;
-    Classes cur = ma.n_blocks > 0 ? classes_of(ma.k_pos[0]) : Classes{0, 0, 0};
-    for (int b = 0; b < ma.n_blocks; ++b) {
+    if constexpr (DOCS) {
+      run_blocks_screened(ma, kvh);
+    } else {
+      Classes cur = ma.n_blocks > 0 ? classes_of(ma.k_pos[0]) : Classes{0, 0, 0, 0, 0, 0};
+      for (int b = 0; b < ma.n_blocks; ++b) {
+        use_classes(cur);
+        // the next block's classes (their loads overlap this block) and what
+        // its first tiles need
+        if (b + 1 < ma.n_blocks) {
+          cur = classes_of(ma.k_pos[b + 1]);
+          nxt_k = ma.k[b + 1];
+          nxt_pos = ma.k_pos[b + 1];
+          nxt_own = own_tiles(cur.n_iter);
+        } else {
+          nxt_k = nullptr;
+          nxt_pos = nullptr;
+          nxt_own = 0;
+        }
+        fold_block(ma.k[b], ma.v[b], ma.k_pos[b], kvh);
+      }
+    }
+    nxt_k = nullptr;
+    finish();
+  }
+
+  // Under a document mask most blocks hold no key a workgroup sees.  Lane b
+  // checks block b's first key against the workgroup's last query and its
+  // last key against the smallest document start; one ballot, the same in
+  // every wave, then replaces a classification pass per hidden block.
+  __device__ __forceinline__ void run_blocks_screened(const MultiArgs& ma, int kvh) {
+    bool maybe = false;
+    if (lane < ma.n_blocks && n_k > 0) {
+      const int32_t* kp = ma.k_pos[lane];
+      maybe = kp[0] <= qmax_wg && kp[n_k - 1] >= qlo_min_wg;
+    }
+    uint64_t todo = __ballot(maybe);
+    int b = todo ? __builtin_ctzll(todo) : -1;
+    Classes cur = b >= 0 ? classes_of(ma.k_pos[b]) : Classes{0, 0, 0, 0, 0, 0};
+    while (b >= 0) {
       use_classes(cur);
-      // the next block's classes (their loads overlap this block) and what
-      // its first tiles need
-      if (b + 1 < ma.n_blocks) {
-        cur = classes_of(ma.k_pos[b + 1]);
-        nxt_k = ma.k[b + 1];
-        nxt_pos = ma.k_pos[b + 1];
+      todo &= todo - 1;
+      const int nb = todo ? __builtin_ctzll(todo) : -1;
+      if (nb >= 0) {
+        cur = classes_of(ma.k_pos[nb]);
+        nxt_k = ma.k[nb];
+        nxt_pos = ma.k_pos[nb];
         nxt_own = own_tiles(cur.n_iter);
         nxt_j0 = cur.j0;
       } else {
@@ -735,9 +772,8 @@ struct Step {
         nxt_own = 0;
       }
       fold_block(ma.k[b], ma.v[b], ma.k_pos[b], kvh);
+      b = nb;
     }
-    nxt_k = nullptr;
-    finish();
   }
 };
 
