@@ -69,7 +69,9 @@ enum { RA_BF16 = 0, RA_F32 = 1 };
 
 typedef struct ra_problem {
   int32_t n_q;    /* queries on this rank, >= 0 */
-  int32_t n_k;    /* keys per key/value block, >= 0 (all blocks equal) */
+  int32_t n_k;    /* keys per key/value block, >= 0 (all blocks equal); one head's
+                     rows of q (n_q) and of a block (n_k) each under 2 GiB, i.e.
+                     n * d_k * element size <= 2^31 - 1 (RA_ERR_SHAPE otherwise) */
   int32_t h_q;    /* query heads, 1..256 */
   int32_t h_kv;   /* key/value heads, h_q % h_kv == 0 */
   int32_t d_k;    /* head width: 64 or 128 */

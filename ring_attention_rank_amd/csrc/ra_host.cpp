@@ -42,6 +42,11 @@ ra_status check_problem(const ra_problem* p) {
   // row index within int32
   if ((int64_t)p->h_q * p->n_q > INT32_MAX || (int64_t)p->h_kv * p->n_k > INT32_MAX)
     return RA_ERR_SHAPE;
+  // the kernels address one head's rows of q, k, v (and the gradients) with
+  // 32-bit byte offsets and buffer sizes: each head's rows stay under 2 GiB
+  const int64_t row_bytes = (int64_t)p->d_k * elem_bytes(p->dtype);
+  if ((int64_t)p->n_q * row_bytes > INT32_MAX || (int64_t)p->n_k * row_bytes > INT32_MAX)
+    return RA_ERR_SHAPE;
   return RA_OK;
 }
 

@@ -53,6 +53,8 @@ def good(**kw):
     (dict(n_q=-1), SHAPE),
     (dict(h_q=0), SHAPE),
     (dict(h_q=512, h_kv=1), SHAPE),
+    (dict(n_k=(1 << 23)), SHAPE),                     # one head's block at 2 GiB (bf16, d 128)
+    (dict(n_q=(1 << 22), dtype=torch.float32), SHAPE),  # one head's queries at 2 GiB (fp32)
     (dict(dtype=7), DTYPE),
     (dict(scale=-1.0), ARG),
     (dict(scale=float("inf")), ARG),

@@ -324,3 +324,12 @@ def test_whole_share_equals_block_steps(which, side):
         assert torch.equal(a_dq, b_dq), rep
         for x, y in zip(a_dks + a_dvs, b_dks + b_dvs):
             assert torch.equal(x, y), rep
+
+
+@pytest.mark.parametrize("h_q,h_kv", [(256, 1), (256, 256)])
+def test_max_heads(h_q, h_kv):
+    """256 query heads: the head-group split of the dk/dv grid with one
+    key/value head, and no split with one query head per key/value head."""
+    rng = np.random.default_rng(300 + h_kv)
+    sh = _custom_share(rng, "bf16", 128, h_q, h_kv, 130, 96, 2)
+    check_share(sh, f"max heads {h_q}/{h_kv}")

@@ -241,3 +241,12 @@ def test_work_counts_give_pages_half_blocks():
             assert got == [2 * i + 1 for i in range(n_cp)]
         else:
             assert got == [4 * n_cp] * n_cp
+
+
+@pytest.mark.parametrize("h_q,h_kv", [(256, 1), (256, 256), (256, 16)])
+def test_max_heads(h_q, h_kv):
+    """The largest head count the boundary takes (256 query heads), with one,
+    every and an intermediate number of key/value heads."""
+    rng = np.random.default_rng(h_kv)
+    sh = _custom_share(rng, "bf16", 128, h_q, h_kv, 160, 96, 2)
+    check_share(sh, f"max heads {h_q}/{h_kv}")
