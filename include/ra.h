@@ -27,8 +27,10 @@
  *  - q_pos[n_q] and k_pos[n_k] are int32 global positions in [0, 2^31-2],
  *    strictly increasing within each array (true of the contiguous, zigzag
  *    and striped layouts).  Key j is visible to query i iff
- *    k_pos[j] <= q_pos[i] when causal, always otherwise.  Positions that do
- *    not increase give unspecified values but never an out-of-bounds access.
+ *    k_pos[j] <= q_pos[i] when causal, always otherwise (and, through
+ *    ra_forward_allgather_docs only, not before the query's document start).
+ *    Positions that do not increase give unspecified values but never an
+ *    out-of-bounds access.
  *  - Query head h reads key/value head h / (h_q / h_kv).
  *  - State (m, l, O): m is the running maximum of the scores s = scale * q.k
  *    (natural-log units) over the visible keys seen so far, l = sum exp(s - m)

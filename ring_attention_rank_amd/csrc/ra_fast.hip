@@ -31,6 +31,10 @@
 //  * Loads are DMA issued three phases before their use and waited for with
 //    explicit vmcnt counts; K and V tiles have two stages per group,
 //    positions three.
+//  * The all-gather form runs the same machinery over every resident block
+//    in one launch, the state staying in registers.  Its document-mask
+//    variant (DOCS) also bounds each query's keys below by its document
+//    start; without it that code compiles away.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
