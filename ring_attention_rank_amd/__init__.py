@@ -133,6 +133,32 @@ def _need_gpu(*tensors):
             raise ValueError("all tensors must be contiguous")
 
 
+def _check_rows(q, q_pos, k_blocks, v_blocks, k_pos_blocks, q_doc_start=None):
+    """What the C ABI cannot see: each position array is an int32 vector
+    with one entry per row, and every key/value block has the first block's
+    shape and q's element type.  Kernels read positions by row index, so a
+    short array would be read past its end."""
+    if q.dim() != 3:
+        raise ValueError("q must be [h_q][n_q][d_k]")
+    n_q, d_k = q.shape[1], q.shape[2]
+
+    def vec(t, n, name):
+        if t.dtype != torch.int32 or t.dim() != 1 or t.numel() != n:
+            raise ValueError(f"{name} must be an int32 vector of {n} positions")
+
+    vec(q_pos, n_q, "q_pos")
+    if q_doc_start is not None:
+        vec(q_doc_start, n_q, "q_doc_start")
+    shape = tuple(k_blocks[0].shape)
+    if len(shape) != 3 or shape[2] != d_k:
+        raise ValueError("key/value blocks must be [h_kv][n_k][d_k] with q's d_k")
+    for k, v, kp in zip(k_blocks, v_blocks, k_pos_blocks):
+        if tuple(k.shape) != shape or tuple(v.shape) != shape or k.dtype != q.dtype \
+                or v.dtype != q.dtype:
+            raise ValueError("every key/value block needs the first block's shape and q's dtype")
+        vec(kp, shape[1], "k_pos")
+
+
 def _problem_from(q, k, causal, scale):
     h_q, n_q, d_k = q.shape
     h_kv, n_k, _ = k.shape
@@ -165,6 +191,7 @@ def state_init(p, m, l, o, stream=None):
 def step(q, q_pos, k, v, k_pos, m, l, o, work=None, causal=True, scale=None, stream=None):
     """Fold one key/value block into the state (m, l, o) in place."""
     _need_gpu(q, q_pos, k, v, k_pos, m, l, o, work)
+    _check_rows(q, q_pos, [k], [v], [k_pos])
     p = _problem_from(q, k, causal, scale)
     _check(lib().ra_step(ctypes.byref(p), _ptr(q), _ptr(q_pos), _ptr(k), _ptr(v), _ptr(k_pos),
                          _ptr(m), _ptr(l), _ptr(o), _ptr(work), _stream(stream)), "ra_step")
@@ -206,6 +233,7 @@ class Forward:
         n_cp = len(k_blocks)
         if not (n_cp == len(v_blocks) == len(k_pos_blocks)) or n_cp < 1:
             raise ValueError("need n_cp >= 1 blocks of k, v and k_pos")
+        _check_rows(q, q_pos, k_blocks, v_blocks, k_pos_blocks)
         self.p = _problem_from(q, k_blocks[0], causal, scale)
         self.n_cp = n_cp
         dev = q.device
@@ -257,6 +285,7 @@ class AllGather:
         n_cp = len(k_blocks)
         if not (n_cp == len(v_blocks) == len(k_pos_blocks)) or n_cp < 1:
             raise ValueError("need n_cp >= 1 blocks of k, v and k_pos")
+        _check_rows(q, q_pos, k_blocks, v_blocks, k_pos_blocks, q_doc_start)
         self.p = _problem_from(q, k_blocks[0], causal, scale)
         self.n_cp = n_cp
         dev = q.device
@@ -333,6 +362,7 @@ def backward_step(q, q_pos, k, v, k_pos, dout, lse, delta, dq, dk=None, dv=None,
     if dv is None:
         dv = torch.zeros(v.shape, dtype=torch.float32, device=v.device)
     _need_gpu(q, q_pos, k, v, k_pos, dout, lse, delta, dq, dk, dv, workspace)
+    _check_rows(q, q_pos, [k], [v], [k_pos])
     p = _problem_from(q, k, causal, scale)
     if workspace is None:
         need = backward_workspace_bytes(p)
@@ -376,6 +406,7 @@ class BackwardShare:
                  side=True):
         self.args = (q, q_pos, list(k_blocks), list(v_blocks), list(k_pos_blocks))
         _need_gpu(q, q_pos, *k_blocks, *v_blocks, *k_pos_blocks)
+        _check_rows(q, q_pos, k_blocks, v_blocks, k_pos_blocks)
         self.p = _problem_from(q, k_blocks[0], causal, scale)
         dev = q.device
         self.dq = torch.empty(q.shape, dtype=torch.float32, device=dev)

@@ -224,3 +224,23 @@ def test_backward_share_checks():
     assert call(p, 2, arr, arr, v, need - 1) == WORKSPACE
     assert call(p, 2, arr, arr, ctypes.c_void_p(FAKE + 4), need) == ALIGN
     assert call(good(d_k=96), 2, arr, arr, v, need) == SHAPE
+
+
+def test_binding_checks_row_arrays():
+    """The binding refuses what the C ABI cannot see (before it touches a
+    GPU): short or mistyped position arrays and mismatched key/value blocks."""
+    q = torch.zeros(2, 8, 64)
+    k = torch.zeros(1, 5, 64)
+    ok = dict(q=q, q_pos=torch.zeros(8, dtype=torch.int32), k_blocks=[k], v_blocks=[k],
+              k_pos_blocks=[torch.zeros(5, dtype=torch.int32)])
+    ra._check_rows(**ok)
+    bad = [dict(q_pos=torch.zeros(7, dtype=torch.int32)),
+           dict(q_pos=torch.zeros(8, dtype=torch.int64)),
+           dict(k_pos_blocks=[torch.zeros(4, dtype=torch.int32)]),
+           dict(v_blocks=[torch.zeros(1, 6, 64)]),
+           dict(k_blocks=[torch.zeros(1, 5, 64, dtype=torch.bfloat16)],
+                v_blocks=[torch.zeros(1, 5, 64, dtype=torch.bfloat16)]),
+           dict(q_doc_start=torch.zeros(3, dtype=torch.int32))]
+    for b in bad:
+        with pytest.raises(ValueError):
+            ra._check_rows(**{**ok, **b})
