@@ -127,3 +127,13 @@ def test_full_size_sampled():
     el = max_err(lse[:, idx].cpu().numpy(), rl)
     print(f"[docs] 405B share: out err {eo:.3e} lse err {el:.3e}", flush=True)
     assert eo <= TOL["bf16"]["out"] and el <= TOL["bf16"]["lse"]
+
+
+@pytest.mark.parametrize("name,T", [("llama8b_gqa_zigzag", 8192), ("tiny_f32_contiguous", 1024)])
+def test_single_block_packed_sequence(name, T):
+    """One rank holding the whole sequence (n_cp = 1, as in the Ulysses share):
+    plain causal attention over a packed sequence, one resident block."""
+    case = synth.case_by_name(name)
+    sh = Share(case, 0, T=T, n_cp=1).to_gpu()
+    starts = synth.document_starts(T, case.seed + 7, 16, T // 4)
+    check_docs(sh, starts, f"{name}@T{T} single block")
