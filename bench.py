@@ -186,6 +186,8 @@ def main():
     ap.add_argument("--no-side-stream", action="store_true")
     ap.add_argument("--no-allgather", action="store_true",
                     help="skip timing the all-gather form (every block resident, one launch)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay side line")
     ap.add_argument("--no-docs", action="store_true",
                     help="skip the document-masked all-gather side line")
     ap.add_argument("--no-backward", action="store_true",
@@ -283,6 +285,26 @@ def main():
         },
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
+    if not args.no_graph:
+        # The same ring forward captured once in a HIP graph and replayed
+        # (ra.ForwardGraph): the same copies, events and launches, submitted
+        # as one graph launch.  Context only; the headline is the eager call.
+        fg = ra.ForwardGraph(share["gq"], share["gq_pos"], share["gk"], share["gv"],
+                             share["gk_pos"])
+        for _ in range(args.warmup):
+            fg()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fg()
+        torch.cuda.synchronize()
+        fg_s = (time.perf_counter() - t0) / args.steps
+        result["ring_graph"] = {
+            "value": flops / fg_s / 1e12, "unit": "TFLOP/s", "ms_per_step": fg_s * 1e3,
+            "pct_of_bf16_peak": 100.0 * flops / fg_s / 1e12 / PEAK_BF16_TFLOPS,
+            "entry_point": "ra_forward replayed from a HIP graph", "rank": ranks[-1],
+        }
+        del fg
     if not args.no_allgather:
         # The all-gather form of the same share: every block resident, one
         # launch (bf16 d_k=128), the state in registers.  Context only; the

@@ -265,6 +265,33 @@ class Forward:
         return self.out, self.lse
 
 
+class ForwardGraph:
+    """ra_forward captured once in a HIP graph and replayed.
+
+    The share's staging copies, the events between the launch and side
+    streams, and the n_cp step launches go to the GPU as one graph launch.
+    The graph reads the same device buffers on every replay: refresh q, k, v
+    and the positions in place, and read the results from ``out`` and
+    ``lse`` (overwritten by each replay).  A replay runs on the current stream.
+    """
+
+    def __init__(self, q, q_pos, k_blocks, v_blocks, k_pos_blocks, causal=True, scale=None):
+        self.fwd = Forward(q, q_pos, k_blocks, v_blocks, k_pos_blocks, causal, scale, side=True,
+                           count_work=False)
+        self.stream = torch.cuda.Stream(device=q.device)
+        self.stream.wait_stream(torch.cuda.current_stream(q.device))
+        self.fwd(stream=self.stream)  # one eager call first, outside the capture
+        self.stream.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph, stream=self.stream):
+            self.fwd(stream=self.stream)
+        self.out, self.lse = self.fwd.out, self.fwd.lse
+
+    def __call__(self):
+        self.graph.replay()  # on the current stream, in order with the caller's work
+        return self.out, self.lse
+
+
 def allgather_workspace_bytes(p):
     return int(lib().ra_forward_allgather_workspace_bytes(ctypes.byref(p)))
 
