@@ -145,6 +145,82 @@ WsLayout ws_layout(const ra_problem* p) {
   return w;
 }
 
+// The all-gather form, with an optional per-query lower bound on the visible
+// key positions (q_lo, the document start under a document mask).
+ra_status allgather_impl(const ra_problem* p, int32_t n_cp, const void* q, const int32_t* q_pos,
+                         const int32_t* q_lo, const void* const* k_blocks,
+                         const void* const* v_blocks, const int32_t* const* k_pos_blocks,
+                         void* workspace, size_t ws_bytes, float* out, float* lse, int64_t* work,
+                         void* stream) {
+  ra_status st = check_problem(p);
+  if (st != RA_OK) return st;
+  if (n_cp < 1 || n_cp > ra::kMaxBlocks) return RA_ERR_SHAPE;
+  if (!k_blocks || !v_blocks || !k_pos_blocks) return RA_ERR_NULL;
+  if (p->n_q > 0) {
+    if (!q || !q_pos || !out || !lse) return RA_ERR_NULL;
+    if (!aligned16(q) || !aligned4(q_pos) || !aligned16(out) || !aligned4(lse))
+      return RA_ERR_ALIGN;
+  }
+  if (work && !aligned8(work)) return RA_ERR_ALIGN;
+  if (p->n_k > 0) {
+    for (int b = 0; b < n_cp; ++b) {
+      if (!k_blocks[b] || !v_blocks[b] || !k_pos_blocks[b]) return RA_ERR_NULL;
+      if (!aligned16(k_blocks[b]) || !aligned16(v_blocks[b]) || !aligned4(k_pos_blocks[b]))
+        return RA_ERR_ALIGN;
+    }
+  }
+  const size_t need = allgather_ws_bytes(p);
+  if (need > 0) {
+    if (!workspace) return RA_ERR_NULL;
+    if (!aligned16(workspace)) return RA_ERR_ALIGN;
+    if (ws_bytes < need) return RA_ERR_WORKSPACE;
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  if (work) {
+    if (ra::launch_zero_i64(work, 3, s) != hipSuccess) return RA_ERR_HIP;
+  }
+  if (p->n_q == 0) return RA_OK;
+
+  ra::StepArgs a;
+  fill_args(p, &a);
+  a.q = q;
+  a.q_pos = q_pos;
+  a.q_lo = q_lo;
+  a.out = out;
+  a.lse = lse;
+  a.work = reinterpret_cast<unsigned long long*>(work);
+  if (fast_path(p)) {
+    ra::MultiArgs ma;
+    std::memset(&ma, 0, sizeof(ma));
+    ma.s = a;
+    ma.n_blocks = p->n_k > 0 ? n_cp : 0;
+    for (int b = 0; b < ma.n_blocks; ++b) {
+      ma.k[b] = k_blocks[b];
+      ma.v[b] = v_blocks[b];
+      ma.k_pos[b] = k_pos_blocks[b];
+    }
+    return ra::launch_allgather_fast(ma, s) == hipSuccess ? RA_OK : RA_ERR_HIP;
+  }
+  // Other shapes: one step launch per block against a state in the workspace.
+  const size_t rows = (size_t)p->h_q * p->n_q;
+  char* ws = (char*)workspace;
+  float* m = (float*)ws;
+  float* l = (float*)(ws + align_up(rows * 4));
+  float* o = (float*)(ws + 2 * align_up(rows * 4));
+  a.m_in = a.m_out = m;
+  a.l_in = a.l_out = l;
+  a.o_in = a.o_out = o;
+  for (int b = 0; b < n_cp; ++b) {
+    a.k = k_blocks[b];
+    a.v = v_blocks[b];
+    a.k_pos = k_pos_blocks[b];
+    st = launch(p, a, /*read=*/b > 0, /*final=*/b == n_cp - 1, s);
+    if (st != RA_OK) return st;
+  }
+  return RA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -575,90 +651,6 @@ size_t ra_forward_allgather_workspace_bytes(const ra_problem* p) {
   if (check_problem(p) != RA_OK) return 0;
   return allgather_ws_bytes(p);
 }
-
-}  // extern "C"
-
-namespace {
-
-// The all-gather form, with an optional per-query lower bound on the visible
-// key positions (q_lo, the document start under a document mask).
-ra_status allgather_impl(const ra_problem* p, int32_t n_cp, const void* q, const int32_t* q_pos,
-                         const int32_t* q_lo, const void* const* k_blocks,
-                         const void* const* v_blocks, const int32_t* const* k_pos_blocks,
-                         void* workspace, size_t ws_bytes, float* out, float* lse, int64_t* work,
-                         void* stream) {
-  ra_status st = check_problem(p);
-  if (st != RA_OK) return st;
-  if (n_cp < 1 || n_cp > ra::kMaxBlocks) return RA_ERR_SHAPE;
-  if (!k_blocks || !v_blocks || !k_pos_blocks) return RA_ERR_NULL;
-  if (p->n_q > 0) {
-    if (!q || !q_pos || !out || !lse) return RA_ERR_NULL;
-    if (!aligned16(q) || !aligned4(q_pos) || !aligned16(out) || !aligned4(lse))
-      return RA_ERR_ALIGN;
-  }
-  if (work && !aligned8(work)) return RA_ERR_ALIGN;
-  if (p->n_k > 0) {
-    for (int b = 0; b < n_cp; ++b) {
-      if (!k_blocks[b] || !v_blocks[b] || !k_pos_blocks[b]) return RA_ERR_NULL;
-      if (!aligned16(k_blocks[b]) || !aligned16(v_blocks[b]) || !aligned4(k_pos_blocks[b]))
-        return RA_ERR_ALIGN;
-    }
-  }
-  const size_t need = allgather_ws_bytes(p);
-  if (need > 0) {
-    if (!workspace) return RA_ERR_NULL;
-    if (!aligned16(workspace)) return RA_ERR_ALIGN;
-    if (ws_bytes < need) return RA_ERR_WORKSPACE;
-  }
-
-  hipStream_t s = (hipStream_t)stream;
-  if (work) {
-    if (ra::launch_zero_i64(work, 3, s) != hipSuccess) return RA_ERR_HIP;
-  }
-  if (p->n_q == 0) return RA_OK;
-
-  ra::StepArgs a;
-  fill_args(p, &a);
-  a.q = q;
-  a.q_pos = q_pos;
-  a.q_lo = q_lo;
-  a.out = out;
-  a.lse = lse;
-  a.work = reinterpret_cast<unsigned long long*>(work);
-  if (fast_path(p)) {
-    ra::MultiArgs ma;
-    std::memset(&ma, 0, sizeof(ma));
-    ma.s = a;
-    ma.n_blocks = p->n_k > 0 ? n_cp : 0;
-    for (int b = 0; b < ma.n_blocks; ++b) {
-      ma.k[b] = k_blocks[b];
-      ma.v[b] = v_blocks[b];
-      ma.k_pos[b] = k_pos_blocks[b];
-    }
-    return ra::launch_allgather_fast(ma, s) == hipSuccess ? RA_OK : RA_ERR_HIP;
-  }
-  // Other shapes: one step launch per block against a state in the workspace.
-  const size_t rows = (size_t)p->h_q * p->n_q;
-  char* ws = (char*)workspace;
-  float* m = (float*)ws;
-  float* l = (float*)(ws + align_up(rows * 4));
-  float* o = (float*)(ws + 2 * align_up(rows * 4));
-  a.m_in = a.m_out = m;
-  a.l_in = a.l_out = l;
-  a.o_in = a.o_out = o;
-  for (int b = 0; b < n_cp; ++b) {
-    a.k = k_blocks[b];
-    a.v = v_blocks[b];
-    a.k_pos = k_pos_blocks[b];
-    st = launch(p, a, /*read=*/b > 0, /*final=*/b == n_cp - 1, s);
-    if (st != RA_OK) return st;
-  }
-  return RA_OK;
-}
-
-}  // namespace
-
-extern "C" {
 
 ra_status ra_forward_allgather(const ra_problem* p, int32_t n_cp, const void* q,
                                const int32_t* q_pos, const void* const* k_blocks,
