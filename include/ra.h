@@ -155,6 +155,13 @@ ra_status ra_forward_allgather(const ra_problem* p, int32_t n_cp, const void* q,
                                void* workspace, size_t ws_bytes, float* out, float* lse,
                                int64_t* work, void* stream);
 
+/* Bytes of device workspace ra_forward_allgather_docs needs for n_cp blocks
+ * (0 for an invalid problem or n_cp).  bfloat16 with d_k = 128 splits the
+ * key blocks over several workgroups per query tile when the launch would
+ * otherwise be small, and keeps their partial states (m, l, o) here; other
+ * shapes need ra_forward_allgather_workspace_bytes(p). */
+size_t ra_forward_allgather_docs_workspace_bytes(const ra_problem* p, int32_t n_cp);
+
 /*
  * The all-gather form under a document mask (packed sequences: Zero to
  * Frontier, "distributed/context-expert", section "Splitting the sequence,
@@ -171,7 +178,13 @@ ra_status ra_forward_allgather(const ra_problem* p, int32_t n_cp, const void* q,
  * unspecified results but no out-of-bounds access.  A query whose document
  * has no key among the blocks gets out = 0 and lse = -inf.  No tile counters
  * (the causal work counts of ra_forward describe the causal mask alone).
- * Asynchronous on stream; the caller owns every buffer.
+ * workspace: ra_forward_allgather_docs_workspace_bytes(p, n_cp) bytes of
+ * device memory, 16-byte aligned (RA_ERR_WORKSPACE if ws_bytes is smaller,
+ * RA_ERR_NULL if it is needed and NULL); its contents after the call are
+ * unspecified.  With split key blocks the partial states are combined in a
+ * second launch, so results agree with ra_forward_allgather on a single
+ * document to rounding, not bit for bit.  Asynchronous on stream; calls
+ * sharing a workspace must be ordered; the caller owns every buffer.
  */
 ra_status ra_forward_allgather_docs(const ra_problem* p, int32_t n_cp, const void* q,
                                     const int32_t* q_pos, const int32_t* q_doc_start,

@@ -25,7 +25,8 @@ RA_BF16, RA_F32 = 0, 1
 
 SYMBOLS = (
     "ra_state_init", "ra_step", "ra_finalize", "ra_forward_workspace_bytes", "ra_forward",
-    "ra_forward_allgather_workspace_bytes", "ra_forward_allgather", "ra_forward_allgather_docs",
+    "ra_forward_allgather_workspace_bytes", "ra_forward_allgather",
+    "ra_forward_allgather_docs_workspace_bytes", "ra_forward_allgather_docs",
     "ra_backward_prep", "ra_backward_workspace_bytes", "ra_backward_step",
     "ra_backward_share_workspace_bytes", "ra_backward_share", "ra_tile_shape", "ra_status_string", "ra_abi_version",
 )
@@ -69,6 +70,8 @@ def lib():
                              ctypes.POINTER(ctypes.c_int64), vp, vp]
     L.ra_forward_allgather_workspace_bytes.argtypes = [P]
     L.ra_forward_allgather_workspace_bytes.restype = ctypes.c_size_t
+    L.ra_forward_allgather_docs_workspace_bytes.argtypes = [P, i32]
+    L.ra_forward_allgather_docs_workspace_bytes.restype = ctypes.c_size_t
     L.ra_forward_allgather.argtypes = [P, i32, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                        ctypes.POINTER(vp), vp, ctypes.c_size_t, vp, vp, vp, vp]
     L.ra_forward_allgather_docs.argtypes = [P, i32, vp, vp, vp, ctypes.POINTER(vp),
@@ -296,6 +299,10 @@ def allgather_workspace_bytes(p):
     return int(lib().ra_forward_allgather_workspace_bytes(ctypes.byref(p)))
 
 
+def allgather_docs_workspace_bytes(p, n_cp):
+    return int(lib().ra_forward_allgather_docs_workspace_bytes(ctypes.byref(p), n_cp))
+
+
 class AllGather:
     """A prepared ra_forward_allgather call (every key/value block resident).
     With ``q_doc_start`` (int32 per query: the first global position of its
@@ -321,7 +328,8 @@ class AllGather:
         self.kp = arr(*[t.data_ptr() for t in k_blocks])
         self.vp = arr(*[t.data_ptr() for t in v_blocks])
         self.pp = arr(*[t.data_ptr() for t in k_pos_blocks])
-        nbytes = allgather_workspace_bytes(self.p)
+        nbytes = (allgather_workspace_bytes(self.p) if q_doc_start is None
+                  else allgather_docs_workspace_bytes(self.p, n_cp))
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
         self.out = torch.empty(q.shape, dtype=torch.float32, device=dev)
         self.lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)

@@ -433,6 +433,12 @@ struct Step {
   // ---- one run: a query tile (128 rows of one head) against blocks --------
   int row = 0, n_kt = 0, n_kt_g = 0, qmax_wg = 0;
   size_t srow = 0;
+  // First state row of this workgroup's slot when the key blocks are split
+  // over several workgroups (each split writes its own partial state).
+  size_t slot_rows = 0;
+  // Write out/lse rather than the state even though FINAL is false (a tile
+  // of the split launch that is folded whole).
+  bool final_rt = false;
   float m_nat0 = -INFINITY, m2_0 = -INFINITY;
   bool count = false;
 
@@ -464,7 +470,7 @@ struct Step {
       qlo = row < n_q ? a.q_lo[row] : kPosLoNone;
     }
     count = a.work != nullptr && head == 0 && wave_valid;
-    srow = (size_t)head * n_q + row;
+    srow = slot_rows + (size_t)head * n_q + row;
   }
 
   // Tile classes of one key block from one pass over its positions.
@@ -668,7 +674,7 @@ struct Step {
     const float ltot = half_swap_sum(lsum);
     if (row >= n_q) return;
     const float m_nat = (m2 == m2_0) ? m_nat0 : m2 * kLn2;
-    if (FINAL) {
+    if (FINAL || final_rt) {
       const bool ok = ltot > 0.f;
       const float inv = ok ? 1.f / ltot : 0.f;
       float* orow = a.out + srow * D;
@@ -715,15 +721,21 @@ struct Step {
   }
 
   // All blocks resident: the query tile against every block in turn, the
-  // running state staying in registers between them.
-  __device__ void run_all(const MultiArgs& ma, int qt, int head) {
+  // running state staying in registers between them.  Under a document mask
+  // only the blocks b with b mod n_split = split are folded.
+  __device__ void run_all(const MultiArgs& ma, int qt, int head, int split = 0, int n_split = 1) {
     positions(qt, head);
     load_state(head);
     const int kvh = head / (a.h_q / a.h_kv);
     head_issued = false;
     nxt_kvh = kvh;
     if constexpr (DOCS) {
-      run_blocks_screened(ma, kvh);
+      if (!run_blocks_screened(ma, kvh, split, n_split) && !FINAL && !final_rt) {
+        // No block of this split can hold a visible key: the partial state
+        // is empty, which its max alone records (the merge reads nothing else).
+        if (grp == 0 && h == 0 && row < n_q) a.m_out[srow] = -INFINITY;
+        return;
+      }
     } else {
       Classes cur = ma.n_blocks > 0 ? classes_of(ma.k_pos[0]) : Classes{0, 0, 0, 0, 0, 0};
       for (int b = 0; b < ma.n_blocks; ++b) {
@@ -751,13 +763,15 @@ struct Step {
   // checks block b's first key against the workgroup's last query and its
   // last key against the smallest document start; one ballot, the same in
   // every wave, then replaces a classification pass per hidden block.
-  __device__ __forceinline__ void run_blocks_screened(const MultiArgs& ma, int kvh) {
+  __device__ __forceinline__ bool run_blocks_screened(const MultiArgs& ma, int kvh, int split,
+                                                      int n_split) {
     bool maybe = false;
-    if (lane < ma.n_blocks && n_k > 0) {
+    if (lane < ma.n_blocks && n_k > 0 && lane % n_split == split) {
       const int32_t* kp = ma.k_pos[lane];
       maybe = kp[0] <= qmax_wg && kp[n_k - 1] >= qlo_min_wg;
     }
     uint64_t todo = __ballot(maybe);
+    const bool any = todo != 0;
     int b = todo ? __builtin_ctzll(todo) : -1;
     Classes cur = b >= 0 ? classes_of(ma.k_pos[b]) : Classes{0, 0, 0, 0, 0, 0};
     while (b >= 0) {
@@ -778,6 +792,7 @@ struct Step {
       fold_block(ma.k[b], ma.v[b], ma.k_pos[b], kvh);
       b = nb;
     }
+    return any;
   }
 };
 
@@ -817,7 +832,102 @@ void allgather_kernel_fast(const MultiArgs ma) {
   }
 }
 
+// The same under a document mask with the key blocks split over n_split
+// workgroups per query tile pair.  A tile whose rows see a long span of
+// positions (late rows of a long document) is split: split s folds the blocks
+// b with b mod n_split = s into a partial state (m, l, O) in slot s of the
+// state arrays, and merge_splits_kernel combines them.  That walk then no
+// longer sets the length of the whole launch, and consecutive chunks of one
+// document (held by different blocks) go to different splits.  Other tiles
+// are folded whole by split 0, which writes out and lse itself.
+//
+// Every global position lies in exactly one block, so a tile's walk over all
+// blocks is about (last row's position - first row's document start) / 64
+// key tiles; a tile is split when that span exceeds kSplitSpan positions.
+constexpr int kSplitSpan = 8192;
+__device__ __forceinline__ bool split_tile(const int32_t* q_pos, const int32_t* q_lo, int n_q,
+                                           int t) {
+  const int last = min((t + 1) * ROWS, n_q) - 1;
+  return q_pos[last] - q_lo[t * ROWS] > kSplitSpan;
+}
+
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void allgather_split_kernel_fast(const MultiArgs ma, int n_split) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x;
+  const int u = blockIdx.x;
+  const int sp = blockIdx.y;
+  const int head = ma.s.head_of[u % ma.s.h_q];
+  const int p = u / ma.s.h_q;
+  const int t_hi = ma.s.n_qt - 1 - p, t_lo = p;
+  Step<false, false, true> s(ma.s, sm, tid);
+  for (int k = 0; k < 2; ++k) {
+    const int t = k == 0 ? t_hi : t_lo;
+    if (k == 1) {
+      if (t_lo >= t_hi) break;
+      __syncthreads();
+    }
+    const bool split = split_tile(ma.s.q_pos, ma.s.q_lo, ma.s.n_q, t);
+    if (!split && sp != 0) continue;
+    s.final_rt = !split;
+    s.slot_rows = split ? (size_t)sp * ma.s.h_q * ma.s.n_q : 0;
+    s.run_all(ma, t, head, split ? sp : 0, split ? n_split : 1);
+  }
+}
+
+// Combines the n_split partial states of each row of a split tile (slot s at
+// m + s rows, l + s rows, o + s rows * D) with the online-softmax rescale and
+// writes the normalised out and lse: M = max_s m_s, L = sum_s l_s e^(m_s - M),
+// out = sum_s O_s e^(m_s - M) / L, lse = M + ln L.  A slot whose max is -inf
+// saw no key and is not read further.  Rows of tiles that were not split
+// already hold their result.  One wave per row, two columns a lane.
+constexpr int MERGE_ROWS = 4;
+__global__ __launch_bounds__(64 * MERGE_ROWS)
+void merge_splits_kernel(const float* __restrict__ m, const float* __restrict__ l,
+                         const float* __restrict__ o, const int32_t* __restrict__ q_pos,
+                         const int32_t* __restrict__ q_lo, int n_q, int n_split, long long rows,
+                         float* __restrict__ out, float* __restrict__ lse) {
+  const long long r = (long long)blockIdx.x * MERGE_ROWS + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  if (!split_tile(q_pos, q_lo, n_q, (int)(r % n_q) / ROWS)) return;
+  const float ms = lane < n_split ? m[lane * rows + r] : -INFINITY;
+  float mx = ms;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  uint64_t seen = __ballot(ms != -INFINITY);
+  float lt = 0.f, o0 = 0.f, o1 = 0.f;
+  while (seen) {
+    const int s = __builtin_ctzll(seen);
+    seen &= seen - 1;
+    const float w = expf(__shfl(ms, s) - mx);
+    const long long sr = s * rows + r;
+    lt += w * l[sr];
+    const float2 x = *(const float2*)(o + sr * D + 2 * lane);
+    o0 += w * x.x;
+    o1 += w * x.y;
+  }
+  const bool ok = lt > 0.f;
+  const float inv = ok ? 1.f / lt : 0.f;
+  *(float2*)(out + r * D + 2 * lane) = float2{o0 * inv, o1 * inv};
+  if (lane == 0) lse[r] = ok ? mx + logf(lt) : -INFINITY;
+}
+
 }  // namespace fast
+
+hipError_t launch_allgather_split_fast(const MultiArgs& ma, int n_split, hipStream_t stream) {
+  dim3 grid((unsigned)(ma.s.n_pairs * ma.s.h_q), (unsigned)n_split), block(fast::THREADS);
+  hipLaunchKernelGGL(fast::allgather_split_kernel_fast, grid, block, 0, stream, ma, n_split);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long rows = (long long)ma.s.h_q * ma.s.n_q;
+  dim3 mgrid((unsigned)((rows + fast::MERGE_ROWS - 1) / fast::MERGE_ROWS)),
+      mblock(64 * fast::MERGE_ROWS);
+  hipLaunchKernelGGL(fast::merge_splits_kernel, mgrid, mblock, 0, stream, ma.s.m_out, ma.s.l_out,
+                     ma.s.o_out, ma.s.q_pos, ma.s.q_lo, ma.s.n_q, n_split, rows, ma.s.out,
+                     ma.s.lse);
+  return hipGetLastError();
+}
 
 hipError_t launch_allgather_fast(const MultiArgs& ma, hipStream_t stream) {
   dim3 grid((unsigned)(ma.s.n_pairs * ma.s.h_q)), block(fast::THREADS);

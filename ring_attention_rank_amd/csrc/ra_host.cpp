@@ -10,6 +10,7 @@
 // from being overwritten before its step has read it.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -98,6 +99,42 @@ size_t allgather_ws_bytes(const ra_problem* p) {
   return 2 * align_up(rows * 4) + align_up(rows * p->d_k * 4);
 }
 
+// Key-block splits of the document-masked all-gather.  A launch of fewer than
+// kSplitBelow workgroups (4 per compute unit) is split into enough of them to
+// reach about kSplitTarget (8 per compute unit), at most one split per block,
+// so that rows late in long documents, which see many blocks, share their
+// walk among several workgroups (the kernel splits only such tiles).  A
+// larger launch already spreads those walks among enough other work, and the
+// partial states would only add traffic.  1 = no split (one launch, the state
+// in registers).
+constexpr int kSplitBelow = 1024;
+constexpr int kSplitTarget = 2048;
+int docs_splits(const ra_problem* p, int32_t n_cp) {
+  if (!fast_path(p) || p->n_q == 0 || p->n_k == 0 || n_cp < 2) return 1;
+  const int n_qt = (p->n_q + ra::kRowsPerGroup - 1) / ra::kRowsPerGroup;
+  const int base = (n_qt + 1) / 2 * p->h_q;
+  if (base >= kSplitBelow) return 1;
+  return std::max(1, std::min<int>(n_cp, (kSplitTarget + base - 1) / base));
+}
+
+// Partial states (m, l, o) of the splits, slot after slot within each array.
+struct SplitLayout {
+  size_t l, o, total;
+};
+SplitLayout split_layout(const ra_problem* p, int n_split) {
+  const size_t rows = (size_t)n_split * p->h_q * p->n_q;
+  SplitLayout w;
+  w.l = align_up(rows * 4);
+  w.o = 2 * align_up(rows * 4);
+  w.total = w.o + align_up(rows * 128 * 4);
+  return w;
+}
+
+size_t docs_ws_bytes(const ra_problem* p, int32_t n_cp) {
+  const int n_split = docs_splits(p, n_cp);
+  return n_split > 1 ? split_layout(p, n_split).total : allgather_ws_bytes(p);
+}
+
 ra_status fill_args(const ra_problem* p, ra::StepArgs* a) {
   std::memset(a, 0, sizeof(*a));
   a->n_q = p->n_q;
@@ -169,7 +206,8 @@ ra_status allgather_impl(const ra_problem* p, int32_t n_cp, const void* q, const
         return RA_ERR_ALIGN;
     }
   }
-  const size_t need = allgather_ws_bytes(p);
+  const int n_split = q_lo ? docs_splits(p, n_cp) : 1;
+  const size_t need = q_lo ? docs_ws_bytes(p, n_cp) : allgather_ws_bytes(p);
   if (need > 0) {
     if (!workspace) return RA_ERR_NULL;
     if (!aligned16(workspace)) return RA_ERR_ALIGN;
@@ -199,6 +237,14 @@ ra_status allgather_impl(const ra_problem* p, int32_t n_cp, const void* q, const
       ma.k[b] = k_blocks[b];
       ma.v[b] = v_blocks[b];
       ma.k_pos[b] = k_pos_blocks[b];
+    }
+    if (n_split > 1) {
+      const SplitLayout w = split_layout(p, n_split);
+      char* ws = (char*)workspace;
+      ma.s.m_out = (float*)ws;
+      ma.s.l_out = (float*)(ws + w.l);
+      ma.s.o_out = (float*)(ws + w.o);
+      return ra::launch_allgather_split_fast(ma, n_split, s) == hipSuccess ? RA_OK : RA_ERR_HIP;
     }
     return ra::launch_allgather_fast(ma, s) == hipSuccess ? RA_OK : RA_ERR_HIP;
   }
@@ -659,6 +705,11 @@ ra_status ra_forward_allgather(const ra_problem* p, int32_t n_cp, const void* q,
                                int64_t* work, void* stream) {
   return allgather_impl(p, n_cp, q, q_pos, nullptr, k_blocks, v_blocks, k_pos_blocks, workspace,
                         ws_bytes, out, lse, work, stream);
+}
+
+size_t ra_forward_allgather_docs_workspace_bytes(const ra_problem* p, int32_t n_cp) {
+  if (check_problem(p) != RA_OK || n_cp < 1 || n_cp > ra::kMaxBlocks) return 0;
+  return docs_ws_bytes(p, n_cp);
 }
 
 ra_status ra_forward_allgather_docs(const ra_problem* p, int32_t n_cp, const void* q,

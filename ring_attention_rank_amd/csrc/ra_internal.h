@@ -91,6 +91,11 @@ hipError_t launch_backward_delta(const float* out, const void* dout, float* delt
 
 // bfloat16, d_k = 128 only.
 hipError_t launch_allgather_fast(const MultiArgs& ma, hipStream_t stream);
+// The document-masked all-gather with the key blocks split over n_split
+// workgroups per query tile (2 <= n_split <= n_blocks): partial states go to
+// slots s = 0 .. n_split-1 of ma.s.m_out / l_out ([n_split][h_q * n_q]) and
+// ma.s.o_out ([n_split][h_q * n_q][128]), then a merge writes out and lse.
+hipError_t launch_allgather_split_fast(const MultiArgs& ma, int n_split, hipStream_t stream);
 hipError_t launch_state_init(float* m, float* l, float* o, int64_t rows, int d_k,
                              hipStream_t stream);
 hipError_t launch_finalize(const float* m, const float* l, const float* o, float* out,

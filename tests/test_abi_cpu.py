@@ -161,6 +161,34 @@ def test_allgather_docs_checks():
                                        None) == NULL
 
 
+def test_allgather_docs_workspace():
+    """The document-masked form splits the key blocks of a small launch
+    (fewer than 1024 workgroups) over up to one workgroup per block and keeps
+    the partial states (m, l, o: 130 floats a row and split) in the workspace;
+    a large launch, a single block or the fp32 path does not split."""
+    L = ra.lib()
+    v = ctypes.c_void_p(FAKE)
+    arr = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    p = good()  # 2 query tiles x 4 heads: one workgroup pair per head
+    rows = 4 * 256
+    need2 = ra.allgather_docs_workspace_bytes(p, 2)
+    assert need2 >= 2 * rows * 130 * 4
+    assert ra.allgather_docs_workspace_bytes(p, 4) >= 4 * rows * 130 * 4 > need2
+    assert ra.allgather_docs_workspace_bytes(p, 1) == 0
+    assert ra.allgather_docs_workspace_bytes(p, 0) == 0
+    assert ra.allgather_docs_workspace_bytes(p, 65) == 0
+    assert ra.allgather_docs_workspace_bytes(good(d_k=96), 2) == 0
+    # 128 query tiles x 16 heads = 1024 workgroups: no split
+    assert ra.allgather_docs_workspace_bytes(good(n_q=16384, h_q=16, h_kv=1), 16) == 0
+    pf = good(dtype=ra.RA_F32, d_k=64)
+    assert ra.allgather_docs_workspace_bytes(pf, 2) == ra.allgather_workspace_bytes(pf) > 0
+    call = lambda ws, wsb: L.ra_forward_allgather_docs(ctypes.byref(p), 2, v, v, v, arr, arr, arr,
+                                                       ws, wsb, v, v, None)
+    assert call(None, need2) == NULL
+    assert call(v, need2 - 1) == WORKSPACE
+    assert call(ctypes.c_void_p(FAKE + 4), need2) == ALIGN
+
+
 def test_backward_checks():
     L = ra.lib()
     v = ctypes.c_void_p(FAKE)
