@@ -93,6 +93,19 @@ def test_split_tiles(name, T, n_cp, rank, lens):
     check_docs(sh, starts, f"{name}@T{T}/r{rank} split")
 
 
+@pytest.mark.parametrize("seed", [31, 32])
+def test_split_tiles_ragged(seed):
+    """Ragged sizes with split tiles: 517 queries (a last tile of 5 rows,
+    split with seed 31, whole with seed 32), 1100 keys a block over 6 blocks
+    (a ragged last key tile), random sparse positions and four documents."""
+    rng = np.random.default_rng(seed)
+    sh = _custom_share(rng, "bf16", 128, 4, 1, 517, 1100, 6)
+    span = int(max(sh.q_pos.max(), max(p.max() for p in sh.k_pos))) + 1
+    starts = np.concatenate([[0], np.sort(rng.choice(np.arange(1, span), 3, replace=False))])
+    assert 0 < split_tiles(sh, starts) < 5
+    check_docs(sh, starts, f"ragged split seed {seed}")
+
+
 @pytest.mark.parametrize("name", ["llama405b_stage_share", "tiny_f32_contiguous"])
 def test_single_token_and_aligned_documents(name):
     """Documents of one token, documents that start on wave (32), tile (64)
