@@ -196,3 +196,39 @@ def test_single_block_packed_sequence(name, T):
     sh = Share(case, 0, T=T, n_cp=1).to_gpu()
     starts = synth.document_starts(T, case.seed + 7, 16, T // 4)
     check_docs(sh, starts, f"{name}@T{T} single block")
+
+
+def test_empty_queries_and_blocks():
+    """No queries: nothing to do.  Blocks without keys: every query's document
+    has no key, so out = 0 and lse = -inf (the entry point's stated result)."""
+    d = 128
+    q = torch.empty((2, 0, d), dtype=torch.bfloat16, device="cuda")
+    qp = torch.empty((0,), dtype=torch.int32, device="cuda")
+    k = torch.randn((1, 64, d), device="cuda").to(torch.bfloat16)
+    kp = torch.arange(64, dtype=torch.int32, device="cuda")
+    out, lse, _ = ra.forward_allgather(q, qp, [k, k], [k, k], [kp, kp + 64], q_doc_start=qp)
+    assert out.shape == (2, 0, d) and lse.shape == (2, 0)
+    q = torch.randn((2, 200, d), device="cuda").to(torch.bfloat16)
+    qp = torch.arange(200, dtype=torch.int32, device="cuda")
+    k0 = torch.empty((1, 0, d), dtype=torch.bfloat16, device="cuda")
+    kp0 = torch.empty((0,), dtype=torch.int32, device="cuda")
+    out, lse, _ = ra.forward_allgather(q, qp, [k0, k0], [k0, k0], [kp0, kp0],
+                                       q_doc_start=torch.zeros_like(qp))
+    torch.cuda.synchronize()
+    assert bool((out == 0).all()) and bool(torch.isneginf(lse).all())
+
+
+@pytest.mark.parametrize("h_kv", [1, 256])
+def test_max_heads_split(h_kv):
+    """The largest head count the boundary takes (256 query heads) with split
+    tiles: positions spread 64 apart so that a 128-row tile spans well over
+    8192 positions, two documents."""
+    rng = np.random.default_rng(40 + h_kv)
+    sh = _custom_share(rng, "bf16", 128, 256, h_kv, 160, 96, 2)
+    sh.q_pos = sh.q_pos * 64
+    sh.k_pos = [p * 64 for p in sh.k_pos]
+    sh.to_gpu()
+    span = int(max(sh.q_pos.max(), max(p.max() for p in sh.k_pos))) + 1
+    starts = np.array([0, span // 3])
+    assert split_tiles(sh, starts) > 0
+    check_docs(sh, starts, f"max heads 256/{h_kv} split")
