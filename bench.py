@@ -81,6 +81,13 @@ def visible_pairs(q_pos, k_pos):
     return int(np.searchsorted(ks, np.asarray(q_pos, dtype=np.int64), side="right").sum())
 
 
+def long_tiles(q_pos, q_lo, rows=128, span=8192):
+    """Query tiles whose last row lies more than ``span`` positions past the
+    first row's document start (those the document-masked launch splits)."""
+    n = len(q_pos)
+    return sum(int(q_pos[min(t + rows, n) - 1] - q_lo[t] > span) for t in range(0, n, rows))
+
+
 def visible_pairs_docs(q_pos, q_lo, k_pos):
     """Pairs with q_lo[i] <= k_pos[j] <= q_pos[i] (the document mask)."""
     ks = np.sort(np.asarray(k_pos, dtype=np.int64))
@@ -348,6 +355,11 @@ def main():
             "pct_of_bf16_peak": 100.0 * doc_flops / agd_s / 1e12 / PEAK_BF16_TFLOPS,
             "documents": int(len(starts)), "visible_flops": doc_flops,
             "entry_point": "ra_forward_allgather_docs", "rank": ranks[-1],
+            # nonzero: the launch splits key walks over workgroups (partial
+            # states kept here); only tiles of 128 query rows spanning more
+            # than 8192 positions from the first row's document start are split
+            "workspace_bytes": int(agd.ws.numel()) if agd.ws is not None else 0,
+            "long_tiles": long_tiles(share["q_pos"], lo),
         }
     if not args.no_backward and case.dtype == "bf16" and case.d_k == 128:
         result["backward"] = time_backward(share, fwd, flops, args.steps, args.warmup, ranks[-1])
