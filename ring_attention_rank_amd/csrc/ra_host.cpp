@@ -483,7 +483,7 @@ ra_status ra_forward(const ra_problem* p, int32_t n_cp, const void* q, const int
 
 cleanup:
   for (hipEvent_t e : {ev_start, ev_staged[0], ev_staged[1], ev_used[0], ev_used[1]})
-    if (e) hipEventDestroy(e);
+    if (e) (void)hipEventDestroy(e);  // the call's status is already decided
   return result;
 }
 
@@ -689,7 +689,7 @@ ra_status ra_backward_share(const ra_problem* p, int32_t n_cp, const void* q,
 
 cleanup:
   for (hipEvent_t e : {ev_ready, ev_done})
-    if (e) hipEventDestroy(e);
+    if (e) (void)hipEventDestroy(e);  // the call's status is already decided
   return result;
 }
 
