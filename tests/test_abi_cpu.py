@@ -189,6 +189,24 @@ def test_allgather_docs_workspace():
     assert call(ctypes.c_void_p(FAKE + 4), need2) == ALIGN
 
 
+@pytest.mark.parametrize("n_q,h_q,h_kv,n_cp,splits", [
+    (8192, 8, 1, 16, 8),     # 70B stage share: 256 workgroups -> 8 splits
+    (8192, 16, 1, 16, 4),    # 405B stage share: 512 -> 4
+    (8192, 8, 8, 64, 8),     # striped share: 256 -> 8 (of 64 blocks)
+    (8192, 32, 8, 4, 0),     # 8B share: 1024 workgroups, no split
+    (256, 4, 2, 3, 3),       # tiny: at most one split per block
+])
+def test_docs_split_counts(n_q, h_q, h_kv, n_cp, splits):
+    """The split count behind the document-masked workspace: about 2048
+    workgroups for launches under 1024, at most one split per block; the
+    workspace holds 130 floats per row and split (plus alignment)."""
+    p = good(n_q=n_q, n_k=n_q, h_q=h_q, h_kv=h_kv)
+    ws = ra.allgather_docs_workspace_bytes(p, n_cp)
+    per_split = h_q * n_q * 130 * 4
+    assert ws // per_split == splits
+    assert ws - splits * per_split < 3 * 256
+
+
 def test_backward_checks():
     L = ra.lib()
     v = ctypes.c_void_p(FAKE)
