@@ -21,13 +21,23 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr and r.stdout == ""
 
 
-def test_traffic_figure_matches_its_workload_only():
-    value = bench.committed_traffic("llama405b_stage_share")
-    assert value is not None and 1e8 < value < 1e9
+def _summary(tmp_path, workload, sha, value="1.6e8"):
+    f = tmp_path / "traffic.md"
+    f.write_text(f"# traffic\n\n- workload: {workload}\n- kernel_source_sha256: {sha}\n"
+                 f"- hbm_bytes_per_launch: {value}\n")
+    return str(f)
+
+
+def test_traffic_figure_matches_its_workload_only(monkeypatch, tmp_path):
+    sha = bench.kernel_source_sha256()
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", _summary(tmp_path, "llama405b_stage_share", sha))
+    assert bench.committed_traffic("llama405b_stage_share") == 1.6e8
     assert bench.committed_traffic("llama70b_stage_share") is None
 
 
-def test_traffic_figure_dropped_when_the_kernel_changes(monkeypatch):
+def test_traffic_figure_dropped_when_the_kernel_changes(monkeypatch, tmp_path):
+    monkeypatch.setattr(bench, "TRAFFIC_SUMMARY",
+                        _summary(tmp_path, "llama405b_stage_share", bench.kernel_source_sha256()))
     monkeypatch.setattr(bench, "kernel_source_sha256", lambda: "0" * 64)
     assert bench.committed_traffic("llama405b_stage_share") is None
 
