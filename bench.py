@@ -36,7 +36,13 @@ METRIC = "causal attention TFLOP/s per rank-share and % of bf16 MFMA peak (1 GPU
 
 
 KERNEL_SOURCE = os.path.join(ROOT, "ring_attention_rank_amd", "csrc", "ra_fast.hip")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "traffic_step_kernel_fast_llama405b_stage_share.md")
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_SUMMARY = os.path.join(PROFILES, "traffic_step_kernel_fast_llama405b_stage_share.md")
+# The dominant kernel of the ring forward: a middle step (reads and writes the
+# running state), n_cp - 2 of the n_cp launches.
+DOMINANT = "step_kernel_fast<true, false>"
+# The other workloads of the size table timed beside the headline (bf16, d_k=128).
+SIDE_WORKLOADS = ("llama8b_gqa_zigzag", "llama70b_stage_share", "million_striped_mha")
 
 
 def kernel_source_sha256():
@@ -44,21 +50,46 @@ def kernel_source_sha256():
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def committed_traffic(workload):
-    """HBM bytes per step launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
-    (calibrated on a plain copy), or None when there is no summary for this
-    workload or the kernel source changed since it was taken."""
+def summary_fields(path, workload):
+    """The ``- key: value`` lines of a committed profile summary, or None when
+    it is missing, covers another workload or predates the kernel source."""
     try:
-        text = open(TRAFFIC_SUMMARY).read()
+        text = open(path).read()
     except OSError:
         return None
     fields = dict(re.findall(r"^- ([a-z_0-9]+): (\S+)$", text, re.M))
     if fields.get("workload") != workload or fields.get("kernel_source_sha256") != kernel_source_sha256():
         return None
+    return fields
+
+
+def summary_float(path, workload, key):
+    fields = summary_fields(path, workload)
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return float(fields[key]) if fields else None
     except (KeyError, ValueError):
         return None
+
+
+def committed_traffic(workload):
+    """HBM bytes per step launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (calibrated on a plain copy), or None when there is no summary for this
+    workload or the kernel source changed since it was taken."""
+    return summary_float(TRAFFIC_SUMMARY, workload, "hbm_bytes_per_launch")
+
+
+def committed_trace_us(workload):
+    """Average duration (us) of the dominant kernel in the committed
+    rocprofv3 --kernel-trace --stats summary of this workload."""
+    return summary_float(os.path.join(PROFILES, f"step_kernel_fast_{workload}.md"), workload,
+                         "dominant_avg_us")
+
+
+def committed_sclk_mhz(workload):
+    """Shader clock held during the dominant kernel: GRBM_GUI_ACTIVE per XCD
+    over the dispatch's duration, from the committed counter pass."""
+    return summary_float(os.path.join(PROFILES, f"mfma_utilisation_{workload}.md"), workload,
+                         "sclk_mhz")
 
 
 def copy_calibration(mib, reps):
@@ -81,7 +112,7 @@ def visible_pairs(q_pos, k_pos):
     return int(np.searchsorted(ks, np.asarray(q_pos, dtype=np.int64), side="right").sum())
 
 
-def long_tiles(q_pos, q_lo, rows=128, span=8192):
+def long_tiles(q_pos, q_lo, span, rows=128):
     """Query tiles whose last row lies more than ``span`` positions past the
     first row's document start (those the document-masked launch splits)."""
     n = len(q_pos)
@@ -180,6 +211,116 @@ def time_backward(share, fwd, fwd_flops, steps, warmup, rank):
             "launches_per_step": 2 + n * (5 if split else 4), "rank": rank}
 
 
+def launch_timing(fwd, pairs_per_step, case, reps):
+    """Per-launch kernel times of the ring forward, measured live: ``reps``
+    calls of ra_forward_timed, HIP events recorded on the launch stream right
+    before and after every step launch.  Returns the mean time of each step
+    launch, the mean gap before it, the exposed staging wait before it and the
+    achieved rate of the middle launches (the dominant kernel)."""
+    runs = [fwd.timed() for _ in range(reps)]
+    n = len(pairs_per_step)
+    mean = lambda key: [float(np.mean([r[key][b] for r in runs])) for b in range(n)]
+    kern, gap, wait = mean("kernel_ms"), mean("gap_ms"), mean("staging_wait_ms")
+    flops = [4 * case.d_k * case.h_q * p for p in pairs_per_step]
+    mid = list(range(1, n - 1)) if n > 2 else list(range(n))
+    mid_ms = float(np.sum([kern[b] for b in mid]))
+    mid_flops = float(np.sum([flops[b] for b in mid]))
+    return {
+        "reps": reps, "kernel_ms": kern, "gap_ms": gap, "staging_wait_ms": wait,
+        "staging_wait_ms_total": float(np.sum(wait)), "gap_ms_total": float(np.sum(gap)),
+        "kernel_ms_total": float(np.sum(kern)),
+        "forward_ms": float(np.mean([r["total_ms"] for r in runs])),
+        "middle_launches": len(mid), "middle_mean_ms": mid_ms / len(mid),
+        "middle_flops_per_launch": mid_flops / len(mid),
+        "middle_tflops": mid_flops / (mid_ms * 1e-3) / 1e12,
+    }
+
+
+def time_ring(case, ranks, dev, steps, warmup, side=True):
+    """The headline measure: ``steps`` ra_forward calls per rank share after
+    ``warmup`` untimed ones, wall clock with the device synchronised on both
+    sides; per-step HIP events on the launch stream alongside."""
+    total_flops, total_time, step_ms, per_rank, last = 0, 0.0, [], [], None
+    for r in ranks:
+        share = build_share(case, r, dev)
+        fwd = ra.Forward(share["gq"], share["gq_pos"], share["gk"], share["gv"], share["gk_pos"],
+                         side=side)
+        flops = 4 * case.d_k * case.h_q * sum(share["pairs_per_step"])
+        for _ in range(warmup):
+            fwd()
+        torch.cuda.synchronize()
+        main_stream = torch.cuda.current_stream()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e0, e1 in evs:
+            e0.record(main_stream)
+            fwd()
+            e1.record(main_stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+        step_ms += ms
+        total_flops += flops * steps
+        total_time += wall
+        per_rank.append({"rank": r, "median_ms": float(np.median(ms)),
+                         "tflops_median": flops / (np.median(ms) * 1e-3) / 1e12,
+                         "visible_flops": flops, "staged_bytes": fwd.staged.value,
+                         "work": fwd.work.tolist()})
+        last = (share, fwd, flops)
+    return {"value": total_flops / total_time / 1e12, "ms_per_step": total_time / (steps * len(ranks)) * 1e3,
+            "step_ms": step_ms, "per_rank": per_rank, "last": last}
+
+
+def time_call(f, steps, warmup):
+    """Seconds per call of f (wall clock, device synchronised on both sides)."""
+    for _ in range(warmup):
+        f()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        f()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def side_workload(name, dev, steps, warmup, timing_reps):
+    """One more workload of the size table, timed like the headline: the ring
+    forward (every rank share the case lists), its per-launch kernel times
+    and staging waits (last rank), and the all-gather form of the last share."""
+    case = synth.case_by_name(name)
+    ring = time_ring(case, case.ranks, dev, steps, warmup)
+    share, fwd, flops = ring.pop("last")
+    t = launch_timing(fwd, share["pairs_per_step"], case, timing_reps)
+    ag = ra.AllGather(share["gq"], share["gq_pos"], share["gk"], share["gv"], share["gk_pos"])
+    ag_s = time_call(ag, steps, warmup)
+    out = {
+        "value": ring["value"], "unit": "TFLOP/s", "ms_per_step": ring["ms_per_step"],
+        "pct_of_bf16_peak": 100.0 * ring["value"] / PEAK_BF16_TFLOPS,
+        "config": {"workload": name, "T": case.T, "n_cp": case.n_cp, "layout": case.layout,
+                   "ranks": list(case.ranks), "h_q": case.h_q, "h_kv": case.h_kv,
+                   "d_k": case.d_k, "n_q": len(share["q_pos"]),
+                   "n_k_per_block": len(share["k_pos"][0])},
+        "per_rank": ring["per_rank"],
+        "dominant_kernel": {
+            "kernel": DOMINANT, "event_mean_ms": t["middle_mean_ms"],
+            "achieved": t["middle_tflops"], "frac": t["middle_tflops"] / PEAK_BF16_TFLOPS,
+            "traced_avg_us": committed_trace_us(name)},
+        "staging_wait_ms_total": t["staging_wait_ms_total"], "gap_ms_total": t["gap_ms_total"],
+        "allgather": {"value": flops / ag_s / 1e12, "ms_per_step": ag_s * 1e3,
+                      "pct_of_bf16_peak": 100.0 * flops / ag_s / 1e12 / PEAK_BF16_TFLOPS,
+                      "rank": case.ranks[-1]},
+    }
+    tr = out["dominant_kernel"]["traced_avg_us"]
+    if tr:
+        out["dominant_kernel"]["traced_frac"] = \
+            t["middle_flops_per_launch"] / (tr * 1e-6) / 1e12 / PEAK_BF16_TFLOPS
+    del fwd, ag, share
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,6 +332,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-side-stream", action="store_true")
+    ap.add_argument("--timing-reps", type=int, default=5,
+                    help="ra_forward_timed calls for the per-launch kernel times")
     ap.add_argument("--no-allgather", action="store_true",
                     help="skip timing the all-gather form (every block resident, one launch)")
     ap.add_argument("--no-graph", action="store_true",
@@ -199,6 +342,8 @@ def main():
                     help="skip the document-masked all-gather side line")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the backward of the share (bf16, d_k = 128)")
+    ap.add_argument("--no-side-workloads", action="store_true",
+                    help="skip timing the other bf16 workloads of the size table")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -220,47 +365,31 @@ def main():
     dev = torch.device("cuda", 0)
     props = torch.cuda.get_device_properties(dev)
 
-    total_flops = 0
-    total_time = 0.0
-    step_ms = []
-    per_rank = []
-    last = None
-    for r in ranks:
-        share = build_share(case, r, dev)
-        fwd = ra.Forward(share["gq"], share["gq_pos"], share["gk"], share["gv"], share["gk_pos"],
-                         side=not args.no_side_stream)
-        flops = 4 * case.d_k * case.h_q * sum(share["pairs_per_step"])
-        for _ in range(args.warmup):
-            fwd()
-        torch.cuda.synchronize()
-        main_stream = torch.cuda.current_stream()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for e0, e1 in evs:
-            e0.record(main_stream)
-            fwd()
-            e1.record(main_stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        ms = [e0.elapsed_time(e1) for e0, e1 in evs]
-        step_ms += ms
-        total_flops += flops * args.steps
-        total_time += wall
-        per_rank.append({"rank": r, "median_ms": float(np.median(ms)),
-                         "tflops_median": flops / (np.median(ms) * 1e-3) / 1e12,
-                         "visible_flops": flops, "staged_bytes": fwd.staged.value,
-                         "work": fwd.work.tolist()})
-        last = (share, fwd, flops)
-
-    ms_per_step = total_time / (args.steps * len(ranks)) * 1e3
-    value = total_flops / total_time / 1e12
+    print(f"[bench] ring forward {case.name} ranks {list(ranks)}", file=sys.stderr, flush=True)
+    ring = time_ring(case, ranks, dev, args.steps, args.warmup, side=not args.no_side_stream)
+    share, fwd, flops = ring["last"]
+    value, ms_per_step = ring["value"], ring["ms_per_step"]
     peak = PEAK_BF16_TFLOPS if case.dtype == "bf16" else PEAK_F32_TFLOPS
-    share, fwd, flops = last
     n_launch = case.n_cp
-    avg_launch_ms = float(np.mean(step_ms)) / n_launch
-    achieved = flops / n_launch / (avg_launch_ms * 1e-3) / 1e12
+    t = launch_timing(fwd, share["pairs_per_step"], case, args.timing_reps)
+    fast = case.dtype == "bf16" and case.d_k == 128
+    traced_us = committed_trace_us(case.name) if fast else None
+    roofline = {
+        # achieved: visible FLOPs of a middle ring step over that launch's
+        # kernel time, HIP events around each launch on its stream
+        "bound": "mfma", "achieved": t["middle_tflops"], "peak": peak, "unit": "TFLOP/s",
+        "frac": t["middle_tflops"] / peak, "traffic": committed_traffic(case.name),
+        "kernel": (DOMINANT + " (bf16 MFMA 32x32x16)") if fast else "step_kernel<true, false> (generic)",
+        "flops_per_launch": t["middle_flops_per_launch"], "avg_launch_ms": t["middle_mean_ms"],
+        "launches_per_step": n_launch, "middle_launches_per_step": t["middle_launches"],
+        # the committed kernel trace of the same command (rocprofv3 --stats)
+        "traced_avg_us": traced_us,
+        "traced_frac": (t["middle_flops_per_launch"] / (traced_us * 1e-6) / 1e12 / peak
+                        if traced_us else None),
+        # the whole forward per launch, gaps between launches included
+        "event_forward_per_launch_ms": float(np.mean(ring["step_ms"])) / n_launch,
+        "event_median_ms_per_step": float(np.median(ring["step_ms"])),
+    }
     result = {
         "metric": METRIC,
         "value": value,
@@ -281,16 +410,19 @@ def main():
             "n_q": len(share["q_pos"]), "n_k_per_block": len(share["k_pos"][0]),
             "visible_flops_per_step": flops, "side_stream_staging": not args.no_side_stream,
         },
-        "per_rank": per_rank,
-        "roofline": {
-            "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-            "frac": achieved / peak, "traffic": committed_traffic(case.name),
-            "kernel": ("step_kernel_fast (bf16 MFMA 32x32x16)" if case.dtype == "bf16" and case.d_k == 128
-                       else "step_kernel (generic)"),
-            "avg_launch_ms": avg_launch_ms, "launches_per_step": n_launch,
-            "event_median_ms_per_step": float(np.median(step_ms)),
+        "per_rank": ring["per_rank"],
+        "roofline": roofline,
+        # Zero to Frontier, "When the ring hides its communication": each
+        # step's exchange should finish under the previous step's compute.
+        "ring_steps": {
+            "kernel_ms": t["kernel_ms"], "gap_ms": t["gap_ms"],
+            "staging_wait_ms": t["staging_wait_ms"],
+            "staging_wait_ms_total": t["staging_wait_ms_total"],
+            "gap_ms_total": t["gap_ms_total"], "kernel_ms_total": t["kernel_ms_total"],
+            "forward_ms": t["forward_ms"], "reps": t["reps"],
         },
-        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "sclk_mhz": committed_sclk_mhz(case.name) if fast else None},
     }
     if not args.no_graph:
         # The same ring forward captured once in a HIP graph and replayed
@@ -298,14 +430,7 @@ def main():
         # as one graph launch.  Context only; the headline is the eager call.
         fg = ra.ForwardGraph(share["gq"], share["gq_pos"], share["gk"], share["gv"],
                              share["gk_pos"])
-        for _ in range(args.warmup):
-            fg()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            fg()
-        torch.cuda.synchronize()
-        fg_s = (time.perf_counter() - t0) / args.steps
+        fg_s = time_call(fg, args.steps, args.warmup)
         result["ring_graph"] = {
             "value": flops / fg_s / 1e12, "unit": "TFLOP/s", "ms_per_step": fg_s * 1e3,
             "pct_of_bf16_peak": 100.0 * flops / fg_s / 1e12 / PEAK_BF16_TFLOPS,
@@ -317,20 +442,13 @@ def main():
         # launch (bf16 d_k=128), the state in registers.  Context only; the
         # headline value is the ring with side-stream staging above.
         ag = ra.AllGather(share["gq"], share["gq_pos"], share["gk"], share["gv"], share["gk_pos"])
-        for _ in range(args.warmup):
-            ag()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            ag()
-        torch.cuda.synchronize()
-        ag_s = (time.perf_counter() - t0) / args.steps
+        ag_s = time_call(ag, args.steps, args.warmup)
         result["allgather"] = {
             "value": flops / ag_s / 1e12, "unit": "TFLOP/s", "ms_per_step": ag_s * 1e3,
             "pct_of_bf16_peak": 100.0 * flops / ag_s / 1e12 / PEAK_BF16_TFLOPS,
-            "launches_per_step": 1 if case.dtype == "bf16" and case.d_k == 128 else case.n_cp,
-            "rank": ranks[-1],
+            "launches_per_step": 1 if fast else case.n_cp, "rank": ranks[-1],
         }
+        del ag
     if not args.no_allgather and not args.no_docs and case.causal:
         # The same share under a document mask: the sequence packed from
         # seeded documents of 512 to 32768 tokens (synth.document_starts),
@@ -342,14 +460,7 @@ def main():
         doc_flops = 4 * case.d_k * case.h_q * doc_pairs
         agd = ra.AllGather(share["gq"], share["gq_pos"], share["gk"], share["gv"], share["gk_pos"],
                            q_doc_start=torch.from_numpy(lo).to(dev))
-        for _ in range(args.warmup):
-            agd()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            agd()
-        torch.cuda.synchronize()
-        agd_s = (time.perf_counter() - t0) / args.steps
+        agd_s = time_call(agd, args.steps, args.warmup)
         result["allgather_docs"] = {
             "value": doc_flops / agd_s / 1e12, "unit": "TFLOP/s", "ms_per_step": agd_s * 1e3,
             "pct_of_bf16_peak": 100.0 * doc_flops / agd_s / 1e12 / PEAK_BF16_TFLOPS,
@@ -357,15 +468,29 @@ def main():
             "entry_point": "ra_forward_allgather_docs", "rank": ranks[-1],
             # nonzero: the launch splits key walks over workgroups (partial
             # states kept here); only tiles of 128 query rows spanning more
-            # than 8192 positions from the first row's document start are split
+            # than ra_docs_split_span() positions from the first row's
+            # document start are split
             "workspace_bytes": int(agd.ws.numel()) if agd.ws is not None else 0,
-            "long_tiles": long_tiles(share["q_pos"], lo),
+            "long_tiles": long_tiles(share["q_pos"], lo, span=ra.docs_split_span()),
         }
-    if not args.no_backward and case.dtype == "bf16" and case.d_k == 128:
+        del agd
+    if not args.no_backward and fast:
+        print("[bench] backward", file=sys.stderr, flush=True)
         result["backward"] = time_backward(share, fwd, flops, args.steps, args.warmup, ranks[-1])
     if not args.no_cpu_baseline and len(ranks) >= 1:
         out, lse = fwd.out, fwd.lse
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(case, share, out, lse, args.cpu_rows)
+    if not args.no_side_workloads and fast and args.config == "llama405b_stage_share" \
+            and args.rank is None:
+        del fwd, share
+        ring.pop("last")
+        torch.cuda.empty_cache()
+        result["side_workloads"] = {}
+        for name in SIDE_WORKLOADS:
+            print(f"[bench] side workload {name}", file=sys.stderr, flush=True)
+            result["side_workloads"][name] = side_workload(name, dev, args.steps, args.warmup,
+                                                           args.timing_reps)
     print(json.dumps(result), flush=True)
 
 

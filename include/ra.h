@@ -87,8 +87,11 @@ ra_status ra_state_init(const ra_problem* p, float* m, float* l, float* o, void*
 
 /*
  * One ring step: fold the attention of q against one key/value block into the
- * state (m, l, o) in place.  Exactly the online-softmax rescale of the pages
- * (new max, old totals times exp(old max - new max), plus this block's terms).
+ * state (m, l, o) in place.  Exactly the online-softmax rescale of Zero to
+ * Frontier, "distributed/context-expert", section "Splitting the sequence,
+ * and the one layer that objects" (and the "Context Parallelism (CP)" concept
+ * page, "Key math / How it works"): the new running max, the old totals times
+ * exp(old max - new max), plus this block's terms against the new max.
  * Rows that see no key of the block are left untouched.
  * work: optional device int64[3] that gets += {full, masked, skipped} tile
  * counts of this block (query tiles x key tiles of ra_tile_shape(), counted
@@ -98,8 +101,10 @@ ra_status ra_step(const ra_problem* p, const void* q, const int32_t* q_pos,
                   const void* k, const void* v, const int32_t* k_pos,
                   float* m, float* l, float* o, int64_t* work, void* stream);
 
-/* Normalise: out = o / l, lse = m + ln l; a row with l == 0 gives out = 0,
- * lse = -inf. */
+/* Normalise after the last block (same section of Zero to Frontier: the
+ * output is the weighted sum divided by the exp-sum; the log-sum-exp is the
+ * running max plus the log of the exp-sum): out = o / l, lse = m + ln l; a row
+ * with l == 0 gives out = 0, lse = -inf. */
 ra_status ra_finalize(const ra_problem* p, const float* m, const float* l, const float* o,
                       float* out, float* lse, void* stream);
 
@@ -130,6 +135,31 @@ ra_status ra_forward(const ra_problem* p, int32_t n_cp, const void* q, const int
                      const int32_t* const* k_pos_blocks, void* workspace, size_t ws_bytes,
                      float* out, float* lse, int64_t* work, int64_t* staged_bytes,
                      void* main_stream, void* side_stream);
+
+/*
+ * ra_forward with timing marks, for measuring the ring on one GPU: the
+ * per-step kernel time and how much of the next block's staging shows
+ * between steps (Zero to Frontier, "distributed/context-expert", section
+ * "When the ring hides its communication": the exchange for the next step
+ * runs while this step computes and costs nothing when it finishes first).
+ * Arguments and behaviour are those of ra_forward, plus:
+ *  launch_events: NULL, or a HOST array of 2 * n_cp hipEvent_t handles (as
+ *    void*) created by the caller with timing enabled.  Entries 2b and 2b+1
+ *    take the start and end times of step b's kernel itself (the launch
+ *    goes through hipExtLaunchKernel with them), so their difference is that
+ *    kernel's duration and the time from 2b-1 to 2b the gap between steps.
+ *  staged_events: NULL, or a HOST array of n_cp such handles.  Entry 0 is
+ *    recorded on main_stream before any work of the call; entry b >= 1 on the
+ *    stream that copies block b, right after its copies.
+ * The events stay owned by the caller; read them after synchronising.  With
+ * both arrays NULL the call is ra_forward.
+ */
+ra_status ra_forward_timed(const ra_problem* p, int32_t n_cp, const void* q, const int32_t* q_pos,
+                           const void* const* k_blocks, const void* const* v_blocks,
+                           const int32_t* const* k_pos_blocks, void* workspace, size_t ws_bytes,
+                           float* out, float* lse, int64_t* work, int64_t* staged_bytes,
+                           void* main_stream, void* side_stream, void* const* launch_events,
+                           void* const* staged_events);
 
 /* Bytes of device workspace ra_forward_allgather needs: 0 for bfloat16 with
  * d_k = 128 (the state stays in registers), else the running state (m, l, o). */
@@ -257,7 +287,11 @@ ra_status ra_backward_share(const ra_problem* p, int32_t n_cp, const void* q,
                             float* const* dk_blocks, float* const* dv_blocks, void* workspace,
                             size_t ws_bytes, void* main_stream, void* side_stream);
 
-/* Query-tile rows (bm) and key-tile columns (bn) the tile counters use. */
+/* Query-tile rows (bm) and key-tile columns (bn) the tile counters use.  The
+ * classes follow the causal picture of Zero to Frontier, "distributed/
+ * context-expert", section "The causal mask unbalances the sequence": a tile
+ * whose keys all precede its queries is full, one that straddles the diagonal
+ * is masked, one wholly after it is skipped. */
 ra_status ra_tile_shape(const ra_problem* p, int32_t* bm, int32_t* bn);
 
 /* Static description of a status code. */
@@ -265,6 +299,16 @@ const char* ra_status_string(ra_status s);
 
 /* ABI version of this header (bumped on any incompatible change). */
 int32_t ra_abi_version(void);
+
+/* The document-masked all-gather (ra_forward_allgather_docs) splits a long
+ * key walk over several workgroups when its launch alone would leave compute
+ * units idle: ra_docs_splits() gives the number of splits for this problem
+ * and n_cp (1 = one workgroup per query tile pair; 0 for a bad problem or
+ * n_cp outside 1..64), and a tile of 128 query rows is split only when its
+ * last row's position lies more than ra_docs_split_span() positions past its
+ * first row's document start.  Host-only; no device work. */
+int32_t ra_docs_split_span(void);
+int32_t ra_docs_splits(const ra_problem* p, int32_t n_cp);
 
 #ifdef __cplusplus
 }

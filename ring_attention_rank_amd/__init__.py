@@ -25,10 +25,12 @@ RA_BF16, RA_F32 = 0, 1
 
 SYMBOLS = (
     "ra_state_init", "ra_step", "ra_finalize", "ra_forward_workspace_bytes", "ra_forward",
+    "ra_forward_timed",
     "ra_forward_allgather_workspace_bytes", "ra_forward_allgather",
     "ra_forward_allgather_docs_workspace_bytes", "ra_forward_allgather_docs",
     "ra_backward_prep", "ra_backward_workspace_bytes", "ra_backward_step",
     "ra_backward_share_workspace_bytes", "ra_backward_share", "ra_tile_shape", "ra_status_string", "ra_abi_version",
+    "ra_docs_split_span", "ra_docs_splits",
 )
 
 
@@ -68,6 +70,7 @@ def lib():
     L.ra_forward.argtypes = [P, i32, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
                              ctypes.POINTER(vp), vp, ctypes.c_size_t, vp, vp, vp,
                              ctypes.POINTER(ctypes.c_int64), vp, vp]
+    L.ra_forward_timed.argtypes = L.ra_forward.argtypes + [ctypes.POINTER(vp), ctypes.POINTER(vp)]
     L.ra_forward_allgather_workspace_bytes.argtypes = [P]
     L.ra_forward_allgather_workspace_bytes.restype = ctypes.c_size_t
     L.ra_forward_allgather_docs_workspace_bytes.argtypes = [P, i32]
@@ -91,7 +94,12 @@ def lib():
     L.ra_status_string.argtypes = [i32]
     L.ra_status_string.restype = ctypes.c_char_p
     L.ra_abi_version.argtypes = []
-    for name in ("ra_state_init", "ra_step", "ra_finalize", "ra_forward", "ra_tile_shape",
+    L.ra_docs_split_span.argtypes = []
+    L.ra_docs_split_span.restype = i32
+    L.ra_docs_splits.argtypes = [P, i32]
+    L.ra_docs_splits.restype = i32
+    for name in ("ra_state_init", "ra_step", "ra_finalize", "ra_forward", "ra_forward_timed",
+                 "ra_tile_shape",
                  "ra_forward_allgather", "ra_forward_allgather_docs", "ra_backward_prep",
                  "ra_backward_step",
                  "ra_backward_share",
@@ -160,6 +168,22 @@ def _check_rows(q, q_pos, k_blocks, v_blocks, k_pos_blocks, q_doc_start=None):
                 or v.dtype != q.dtype:
             raise ValueError("every key/value block needs the first block's shape and q's dtype")
         vec(kp, shape[1], "k_pos")
+    _check_increasing(q_pos, k_pos_blocks, q_doc_start)
+
+
+def _check_increasing(q_pos, k_pos_blocks, q_doc_start=None):
+    """With RA_DEBUG=1 in the environment: positions must increase strictly
+    within each array, and document starts must not decrease (the kernels'
+    tile classes rely on both; otherwise the values are unspecified).  The
+    check synchronises with the device, so it is off by default."""
+    if os.environ.get("RA_DEBUG", "0") in ("", "0"):
+        return
+    for name, t in [("q_pos", q_pos)] + [(f"k_pos[{b}]", kp) for b, kp in enumerate(k_pos_blocks)]:
+        if t.numel() > 1 and not bool((t[1:] > t[:-1]).all()):
+            raise ValueError(f"{name}: positions must increase strictly")
+    if q_doc_start is not None and q_doc_start.numel() > 1 \
+            and not bool((q_doc_start[1:] >= q_doc_start[:-1]).all()):
+        raise ValueError("q_doc_start must not decrease")
 
 
 def _problem_from(q, k, causal, scale):
@@ -226,6 +250,21 @@ def side_stream(device=None):
     return s
 
 
+def _record_streams(obj, streams, tensors):
+    """The buffers of a prepared call were allocated on the stream current at
+    its construction; work enqueued on another stream (the caller's, or the
+    side stream that fills staging slots) must keep them alive until it has
+    run, so the caching allocator is told of each such stream once."""
+    for st in streams:
+        if st is None or st.cuda_stream == obj.alloc_stream.cuda_stream \
+                or st.cuda_stream in obj.recorded:
+            continue
+        for t in tensors:
+            if t is not None:
+                t.record_stream(st)
+        obj.recorded.add(st.cuda_stream)
+
+
 class Forward:
     """A prepared ra_forward call: the pointer arrays, workspace and outputs
     are built once, so repeated calls only cross the C ABI."""
@@ -254,18 +293,55 @@ class Forward:
         self.work = torch.zeros(3, dtype=torch.int64, device=dev) if count_work else None
         self.side = side_stream(dev) if side else None
         self.staged = ctypes.c_int64(0)
+        self.alloc_stream = torch.cuda.current_stream(dev)
+        self.recorded = set()
+
+    def _mark_streams(self, main):
+        _record_streams(self, (main, self.side), (self.ws, self.out, self.lse, self.work))
 
     def __call__(self, stream=None):
+        return self._run(stream, None, None)
+
+    def _run(self, stream, launch_events, staged_events):
         main = torch.cuda.current_stream() if stream is None else stream
         side = self.side if self.side is not None else None
+        self._mark_streams(main)
         q, q_pos = self.keep[0], self.keep[1]
-        _check(lib().ra_forward(
-            ctypes.byref(self.p), self.n_cp, _ptr(q), _ptr(q_pos), self.kp, self.vp, self.pp,
-            _ptr(self.ws), ctypes.c_size_t(self.ws.numel()), _ptr(self.out), _ptr(self.lse),
-            _ptr(self.work), ctypes.byref(self.staged), _stream(main),
-            ctypes.c_void_p(side.cuda_stream) if side is not None else ctypes.c_void_p(0)),
-            "ra_forward")
+        args = (ctypes.byref(self.p), self.n_cp, _ptr(q), _ptr(q_pos), self.kp, self.vp, self.pp,
+                _ptr(self.ws), ctypes.c_size_t(self.ws.numel()), _ptr(self.out), _ptr(self.lse),
+                _ptr(self.work), ctypes.byref(self.staged), _stream(main),
+                ctypes.c_void_p(side.cuda_stream) if side is not None else ctypes.c_void_p(0))
+        if launch_events is None and staged_events is None:
+            _check(lib().ra_forward(*args), "ra_forward")
+        else:
+            _check(lib().ra_forward_timed(*args, launch_events, staged_events), "ra_forward_timed")
         return self.out, self.lse
+
+    def timed(self, stream=None):
+        """One call of ra_forward_timed, synchronised: per step b the kernel
+        time (ms between the marks around its launch), the gap since step
+        b-1 ended, and the exposed staging wait, i.e. how long after step b-1
+        ended block b's copies finished (0 when the copy was already done)."""
+        main = torch.cuda.current_stream() if stream is None else stream
+        n = self.n_cp
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(3 * n)]
+        for e in evs:  # torch creates the HIP event on its first record
+            e.record(main)
+        main.synchronize()
+        arr = ctypes.c_void_p * n
+        launch = (ctypes.c_void_p * (2 * n))(*[e.cuda_event for e in evs[:2 * n]])
+        staged = arr(*[e.cuda_event for e in evs[2 * n:]])
+        self._run(main, launch, staged)
+        main.synchronize()
+        if self.side is not None:
+            self.side.synchronize()
+        st, en, cp = evs[0:2 * n:2], evs[1:2 * n:2], evs[2 * n:]
+        kernel_ms = [st[b].elapsed_time(en[b]) for b in range(n)]
+        gap_ms = [0.0] + [en[b - 1].elapsed_time(st[b]) for b in range(1, n)]
+        wait_ms = [0.0] + [max(0.0, en[b - 1].elapsed_time(cp[b])) for b in range(1, n)]
+        total_ms = cp[0].elapsed_time(en[n - 1])
+        return {"kernel_ms": kernel_ms, "gap_ms": gap_ms, "staging_wait_ms": wait_ms,
+                "total_ms": total_ms}
 
 
 class ForwardGraph:
@@ -293,6 +369,17 @@ class ForwardGraph:
     def __call__(self):
         self.graph.replay()  # on the current stream, in order with the caller's work
         return self.out, self.lse
+
+
+def docs_split_span():
+    """Positions a 128-row query tile may span (first row's document start to
+    last row's position) before the document-masked launch splits its walk."""
+    return int(lib().ra_docs_split_span())
+
+
+def docs_splits(p, n_cp):
+    """Key-block splits of the document-masked launch for this problem (1 = none)."""
+    return int(lib().ra_docs_splits(ctypes.byref(p), int(n_cp)))
 
 
 def allgather_workspace_bytes(p):
@@ -334,8 +421,12 @@ class AllGather:
         self.out = torch.empty(q.shape, dtype=torch.float32, device=dev)
         self.lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev)
         self.work = torch.zeros(3, dtype=torch.int64, device=dev) if count_work else None
+        self.alloc_stream = torch.cuda.current_stream(dev)
+        self.recorded = set()
 
     def __call__(self, stream=None):
+        if stream is not None:
+            _record_streams(self, (stream,), (self.ws, self.out, self.lse, self.work))
         q, q_pos = self.keep[0], self.keep[1]
         ws_n = ctypes.c_size_t(self.ws.numel() if self.ws is not None else 0)
         if self.q_doc_start is None:
@@ -454,10 +545,13 @@ class BackwardShare:
         arr = lambda ts: (ctypes.c_void_p * n)(*[_ptr(t) for t in ts])
         self.kp, self.vp, self.pp = arr(k_blocks), arr(v_blocks), arr(k_pos_blocks)
         self.dkp, self.dvp = arr(self.dks), arr(self.dvs)
+        self.alloc_stream = torch.cuda.current_stream(dev)
+        self.recorded = set()
 
     def __call__(self, out, lse, dout, stream=None):
         q, q_pos = self.args[0], self.args[1]
         _need_gpu(out, lse, dout)
+        _record_streams(self, (stream, self.side), (self.dq, self.ws, *self.dks, *self.dvs))
         side = _stream(self.side) if self.side is not None else ctypes.c_void_p(0)
         _check(lib().ra_backward_share(ctypes.byref(self.p), len(self.dks), _ptr(q), _ptr(q_pos),
                                        self.kp, self.vp, self.pp, _ptr(out), _ptr(lse),

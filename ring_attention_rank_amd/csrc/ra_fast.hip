@@ -35,6 +35,7 @@
 //    in one launch, the state staying in registers.  Its document-mask
 //    variant (DOCS) also bounds each query's keys below by its document
 //    start; without it that code compiles away.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -264,18 +265,36 @@ struct Step {
   }
 
   // ---- MFMA pieces --------------------------------------------------------
+  // Each operand is read from LDS three MFMAs ahead of its use: with four
+  // waves of the CU reading at once, an LDS read takes longer than one
+  // 32-cycle MFMA, so a read issued just one MFMA ahead stalls the matrix
+  // pipe.  The scheduling groups (0x100: LDS reads, 0x008: MFMAs) fix that
+  // order; the compiler would otherwise interleave one read per MFMA.
+  template <int MASK, int N>
+  __device__ __forceinline__ static void sched() {
+    __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
+  }
   __device__ __forceinline__ f32x16 qk(int stage, int kb) const {
     const uint8_t* base = sm.k[grp][stage] + kb * 32 * 256;
     f32x16 s = {};
+    bf16x8 av[8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      bf16x8 av = *(const bf16x8*)(base + (k_rd ^ (32 * ks)));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, q[ks], s, 0, 0, 0);
+    for (int ks = 0; ks < 8; ++ks) av[ks] = *(const bf16x8*)(base + (k_rd ^ (32 * ks)));
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks], q[ks], s, 0, 0, 0);
+    sched<0x100, 3>();
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      sched<0x008, 1>();
+      sched<0x100, 1>();
     }
+    sched<0x008, 3>();
     return s;
   }
   __device__ __forceinline__ void pv(int stage, int kb, const bf16x8 (&p)[2]) {
     const uint8_t* base = sm.v[grp][stage] + kb * 32 * 256;
+    bf16x8 av[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -285,9 +304,20 @@ struct Step {
         s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off + 4 * 256));
         // whole-vector assembly: element-wise __bf16 inserts were mis-lowered
         const s16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8 av = __builtin_bit_cast(bf16x8, w);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, p[t], o[db], 0, 0, 0);
+        av[t][db] = __builtin_bit_cast(bf16x8, w);
       }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[t][db], p[t], o[db], 0, 0, 0);
+    sched<0x100, 6>();  // two transposing reads per operand
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      sched<0x008, 1>();
+      sched<0x100, 2>();
+    }
+    sched<0x008, 3>();
   }
 
   // Masks keys of one 32-key half to -inf: those after the query (position
@@ -406,14 +436,17 @@ struct Step {
     wait_loads(has_k ? 9 : has_v ? 4 : 0);
   }
 
-  // GEMM phase after the softmax of own tile s: O += P(s) V(s) and the
-  // scores of own tile s+1 (S^T = K Q^T).  s = -1 computes only the scores
-  // of own tile 0; the last phase only PV.
   // GEMM phase after the softmax of own tile s: the scores of own tile s+1
   // (S^T = K Q^T) and O += P(s) V(s).  s = -1 computes only the scores of
   // own tile 0; the last phase only PV.
+  //
+  // The wave in its GEMM phase runs at raised issue priority: when both waves
+  // of a SIMD have an instruction ready, its MFMAs and their operand reads go
+  // first, so the matrix pipe stays fed and the softmax wave's VALU work fills
+  // the cycles in between.
   template <bool PV, bool QK>
   __device__ __forceinline__ void gemm_phase(int s) {
+    __builtin_amdgcn_s_setprio(1);
     if (PV && !QK) prefetch_next_head();
     if (QK) {
       sc[0] = qk((s + 1) & 1, 0);
@@ -428,6 +461,7 @@ struct Step {
       pv(s & 1, 1, pp[1]);
     }
     pin_gemm();
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // ---- one run: a query tile (128 rows of one head) against blocks --------
@@ -844,7 +878,6 @@ void allgather_kernel_fast(const MultiArgs ma) {
 // Every global position lies in exactly one block, so a tile's walk over all
 // blocks is about (last row's position - first row's document start) / 64
 // key tiles; a tile is split when that span exceeds kSplitSpan positions.
-constexpr int kSplitSpan = 8192;
 __device__ __forceinline__ bool split_tile(const int32_t* q_pos, const int32_t* q_lo, int n_q,
                                            int t) {
   const int last = min((t + 1) * ROWS, n_q) - 1;
@@ -938,16 +971,23 @@ hipError_t launch_allgather_fast(const MultiArgs& ma, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_step_fast(const StepArgs& a, bool read, bool final_, hipStream_t stream) {
+hipError_t launch_step_fast(const StepArgs& a, bool read, bool final_, hipStream_t stream,
+                            hipEvent_t start, hipEvent_t stop) {
   dim3 grid((unsigned)(a.n_pairs * a.h_q)), block(fast::THREADS);
+  auto go = [&](auto kernel) {
+    if (start || stop)
+      hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0, a);
+    else
+      hipLaunchKernelGGL(kernel, grid, block, 0, stream, a);
+  };
   if (read && final_)
-    hipLaunchKernelGGL((fast::step_kernel_fast<true, true>), grid, block, 0, stream, a);
+    go(fast::step_kernel_fast<true, true>);
   else if (read)
-    hipLaunchKernelGGL((fast::step_kernel_fast<true, false>), grid, block, 0, stream, a);
+    go(fast::step_kernel_fast<true, false>);
   else if (final_)
-    hipLaunchKernelGGL((fast::step_kernel_fast<false, true>), grid, block, 0, stream, a);
+    go(fast::step_kernel_fast<false, true>);
   else
-    hipLaunchKernelGGL((fast::step_kernel_fast<false, false>), grid, block, 0, stream, a);
+    go(fast::step_kernel_fast<false, false>);
   return hipGetLastError();
 }
 

@@ -150,9 +150,9 @@ ra_status fill_args(const ra_problem* p, ra::StepArgs* a) {
 }
 
 ra_status launch(const ra_problem* p, const ra::StepArgs& a, bool read, bool final_,
-                 hipStream_t s) {
+                 hipStream_t s, hipEvent_t start = nullptr, hipEvent_t stop = nullptr) {
   if (a.n_qt == 0) return RA_OK;
-  hipError_t e = ra::launch_step(a, p->dtype, p->d_k, read, final_, s);
+  hipError_t e = ra::launch_step(a, p->dtype, p->d_k, read, final_, s, start, stop);
   return e == hipSuccess ? RA_OK : RA_ERR_HIP;
 }
 
@@ -273,6 +273,13 @@ extern "C" {
 
 int32_t ra_abi_version(void) { return 1; }
 
+int32_t ra_docs_split_span(void) { return ra::kSplitSpan; }
+
+int32_t ra_docs_splits(const ra_problem* p, int32_t n_cp) {
+  if (check_problem(p) != RA_OK || n_cp < 1 || n_cp > ra::kMaxBlocks) return 0;
+  return docs_splits(p, n_cp);
+}
+
 const char* ra_status_string(ra_status s) {
   switch (s) {
     case RA_OK: return "ok";
@@ -359,6 +366,17 @@ ra_status ra_forward(const ra_problem* p, int32_t n_cp, const void* q, const int
                      const int32_t* const* k_pos_blocks, void* workspace, size_t ws_bytes,
                      float* out, float* lse, int64_t* work, int64_t* staged_bytes,
                      void* main_stream, void* side_stream) {
+  return ra_forward_timed(p, n_cp, q, q_pos, k_blocks, v_blocks, k_pos_blocks, workspace,
+                          ws_bytes, out, lse, work, staged_bytes, main_stream, side_stream,
+                          nullptr, nullptr);
+}
+
+ra_status ra_forward_timed(const ra_problem* p, int32_t n_cp, const void* q, const int32_t* q_pos,
+                           const void* const* k_blocks, const void* const* v_blocks,
+                           const int32_t* const* k_pos_blocks, void* workspace, size_t ws_bytes,
+                           float* out, float* lse, int64_t* work, int64_t* staged_bytes,
+                           void* main_stream, void* side_stream, void* const* launch_events,
+                           void* const* staged_events) {
   ra_status st = check_problem(p);
   if (st != RA_OK) return st;
   if (n_cp < 1) return RA_ERR_SHAPE;
@@ -380,6 +398,16 @@ ra_status ra_forward(const ra_problem* p, int32_t n_cp, const void* q, const int
   if (!workspace) return RA_ERR_NULL;
   if (!aligned16(workspace)) return RA_ERR_ALIGN;
   if (ws_bytes < w.total) return RA_ERR_WORKSPACE;
+  if (launch_events)
+    for (int i = 0; i < 2 * n_cp; ++i)
+      if (!launch_events[i]) return RA_ERR_NULL;
+  if (staged_events)
+    for (int i = 0; i < n_cp; ++i)
+      if (!staged_events[i]) return RA_ERR_NULL;
+  // Timing marks (caller-owned events); a failed record fails the call.
+  auto mark = [](void* const* evs, int i, hipStream_t s) {
+    return !evs || hipEventRecord((hipEvent_t)evs[i], s) == hipSuccess;
+  };
 
   hipStream_t ms = (hipStream_t)main_stream;
   hipStream_t ss = (hipStream_t)side_stream;
@@ -390,10 +418,18 @@ ra_status ra_forward(const ra_problem* p, int32_t n_cp, const void* q, const int
   float* o = (float*)(ws + w.o);
 
   if (staged_bytes) *staged_bytes = 0;
+  if (!mark(staged_events, 0, ms)) return RA_ERR_HIP;
   if (work) {
     if (ra::launch_zero_i64(work, 3, ms) != hipSuccess) return RA_ERR_HIP;
   }
-  if (p->n_q == 0) return RA_OK;
+  if (p->n_q == 0) {
+    // nothing runs: every mark still gets recorded, so the caller can read them
+    for (int b = 0; b < n_cp; ++b)
+      if (!mark(launch_events, 2 * b, ms) || !mark(launch_events, 2 * b + 1, ms) ||
+          (b > 0 && !mark(staged_events, b, ms)))
+        return RA_ERR_HIP;
+    return RA_OK;
+  }
 
   ra::StepArgs a;
   fill_args(p, &a);
@@ -462,6 +498,7 @@ ra_status ra_forward(const ra_problem* p, int32_t n_cp, const void* q, const int
         }
       }
       staged += 2 * (int64_t)w.kbytes;
+      if (!mark(staged_events, b, cs)) { result = RA_ERR_HIP; goto cleanup; }
       if (use_side) {
         if (hipEventRecord(ev_staged[s], ss) != hipSuccess ||
             hipStreamWaitEvent(ms, ev_staged[s], 0) != hipSuccess) {
@@ -473,7 +510,10 @@ ra_status ra_forward(const ra_problem* p, int32_t n_cp, const void* q, const int
       a.v = dv;
       a.k_pos = (const int32_t*)dp;
     }
-    result = launch(p, a, /*read=*/!first, /*final=*/last, ms);
+    // with timing, the kernel's own start and end times go to the events
+    result = launch(p, a, /*read=*/!first, /*final=*/last, ms,
+                    launch_events ? (hipEvent_t)launch_events[2 * b] : nullptr,
+                    launch_events ? (hipEvent_t)launch_events[2 * b + 1] : nullptr);
     if (result != RA_OK) goto cleanup;
     if (use_side && !first && b + 2 < n_cp) {
       if (hipEventRecord(ev_used[b & 1], ms) != hipSuccess) { result = RA_ERR_HIP; goto cleanup; }

@@ -13,6 +13,10 @@ constexpr int kRowsPerGroup = kWavesPerGroup * kRowsPerWave;  // 128
 constexpr int kKeysPerTile = 64;   // keys per LDS tile
 constexpr int kMaxHeads = 256;
 constexpr int kMaxBlocks = 64;     // key/value blocks of one all-gather launch
+// Document-masked all-gather: a query tile whose rows span more than this
+// many positions from its first row's document start to its last row is
+// split over several workgroups (its walk over the blocks is long).
+constexpr int kSplitSpan = 8192;
 
 // Arguments of one ring-step launch (one key/value block against all local
 // queries of all heads).  READ selects whether the state is read (else it
@@ -53,10 +57,13 @@ struct MultiArgs {
   const int32_t* k_pos[kMaxBlocks];
 };
 
+// start / stop: optional events that take the kernel's own start and end
+// times (hipExtLaunchKernel); null for a plain launch.
 hipError_t launch_step(const StepArgs& a, int dtype, int d_k, bool read, bool final_,
-                       hipStream_t stream);
+                       hipStream_t stream, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // bfloat16, d_k = 128: the 8-wave kernel with direct-to-LDS staging.
-hipError_t launch_step_fast(const StepArgs& a, bool read, bool final_, hipStream_t stream);
+hipError_t launch_step_fast(const StepArgs& a, bool read, bool final_, hipStream_t stream,
+                            hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // Backward of one key/value block (bfloat16, d_k = 128): dq, dk and dv
 // (fp32) each get this block's part added (dk, dv summed over the query heads
 // of each key/value head).

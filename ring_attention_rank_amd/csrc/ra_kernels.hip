@@ -38,6 +38,7 @@
 //  * Tiles are classified from the explicit positions: skipped (no visible
 //    pair), full, or masked (diagonal or ragged).  Only masked tiles compare
 //    positions.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -702,27 +703,34 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* p, int64_t n) {
 }
 
 template <typename Tr, int D>
-static hipError_t launch_typed(const StepArgs& a, bool read, bool final_, hipStream_t stream) {
+static hipError_t launch_typed(const StepArgs& a, bool read, bool final_, hipStream_t stream,
+                               hipEvent_t start, hipEvent_t stop) {
   dim3 grid((unsigned)(a.n_pairs * a.h_q)), block(256);
+  auto go = [&](auto kernel) {
+    if (start || stop)
+      hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0, a);
+    else
+      hipLaunchKernelGGL(kernel, grid, block, 0, stream, a);
+  };
   if (read && final_)
-    hipLaunchKernelGGL((step_kernel<Tr, D, true, true>), grid, block, 0, stream, a);
+    go(step_kernel<Tr, D, true, true>);
   else if (read)
-    hipLaunchKernelGGL((step_kernel<Tr, D, true, false>), grid, block, 0, stream, a);
+    go(step_kernel<Tr, D, true, false>);
   else if (final_)
-    hipLaunchKernelGGL((step_kernel<Tr, D, false, true>), grid, block, 0, stream, a);
+    go(step_kernel<Tr, D, false, true>);
   else
-    hipLaunchKernelGGL((step_kernel<Tr, D, false, false>), grid, block, 0, stream, a);
+    go(step_kernel<Tr, D, false, false>);
   return hipGetLastError();
 }
 
 hipError_t launch_step(const StepArgs& a, int dtype, int d_k, bool read, bool final_,
-                       hipStream_t stream) {
+                       hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (dtype == 0) {
-    if (d_k == 128) return launch_step_fast(a, read, final_, stream);
-    return launch_typed<TraitsBf16<64>, 64>(a, read, final_, stream);
+    if (d_k == 128) return launch_step_fast(a, read, final_, stream, start, stop);
+    return launch_typed<TraitsBf16<64>, 64>(a, read, final_, stream, start, stop);
   }
-  if (d_k == 128) return launch_typed<TraitsF32<128>, 128>(a, read, final_, stream);
-  return launch_typed<TraitsF32<64>, 64>(a, read, final_, stream);
+  if (d_k == 128) return launch_typed<TraitsF32<128>, 128>(a, read, final_, stream, start, stop);
+  return launch_typed<TraitsF32<64>, 64>(a, read, final_, stream, start, stop);
 }
 
 hipError_t launch_state_init(float* m, float* l, float* o, int64_t rows, int d_k,

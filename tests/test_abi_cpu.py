@@ -116,6 +116,42 @@ def test_forward_checks():
                         ctypes.byref(staged), None, None) == NULL
 
 
+def test_forward_timed_checks():
+    """ra_forward_timed checks what ra_forward checks, and every event handle
+    it is given, before enqueuing anything."""
+    p = good()
+    L = ra.lib()
+    v = ctypes.c_void_p(FAKE)
+    arr = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    staged = ctypes.c_int64(0)
+    need = ra.workspace_bytes(p)
+    launch = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, 0)
+    cps = (ctypes.c_void_p * 2)(0, FAKE)
+    args = lambda ncp, ws, wsb: (ctypes.byref(p), ncp, v, v, arr, arr, arr, ws, wsb, v, v,
+                                 None, ctypes.byref(staged), None, None)
+    assert L.ra_forward_timed(*args(0, v, need), None, None) == SHAPE
+    assert L.ra_forward_timed(*args(2, v, need - 1), None, None) == WORKSPACE
+    assert L.ra_forward_timed(*args(2, v, need), launch, None) == NULL
+    assert L.ra_forward_timed(*args(2, v, need), None, cps) == NULL
+
+
+def test_debug_position_check(monkeypatch):
+    """RA_DEBUG=1 makes the binding refuse positions that do not increase and
+    document starts that decrease; without it nothing is checked."""
+    up = torch.tensor([0, 3, 7], dtype=torch.int32)
+    flat = torch.tensor([0, 3, 3], dtype=torch.int32)
+    down = torch.tensor([5, 2, 2], dtype=torch.int32)
+    ra._check_increasing(flat, [flat], down)
+    monkeypatch.setenv("RA_DEBUG", "1")
+    ra._check_increasing(up, [up], torch.tensor([0, 0, 4], dtype=torch.int32))
+    with pytest.raises(ValueError):
+        ra._check_increasing(flat, [up])
+    with pytest.raises(ValueError):
+        ra._check_increasing(up, [up, flat])
+    with pytest.raises(ValueError):
+        ra._check_increasing(up, [up], down)
+
+
 def test_allgather_checks():
     L = ra.lib()
     v = ctypes.c_void_p(FAKE)
@@ -205,6 +241,15 @@ def test_docs_split_counts(n_q, h_q, h_kv, n_cp, splits):
     per_split = h_q * n_q * 130 * 4
     assert ws // per_split == splits
     assert ws - splits * per_split < 3 * 256
+    # the count the library reports itself (1 = no split)
+    assert ra.docs_splits(p, n_cp) == max(splits, 1)
+
+
+def test_docs_split_span_and_bad_arguments():
+    assert ra.docs_split_span() == 8192
+    assert ra.docs_splits(good(), 0) == 0 and ra.docs_splits(good(), 65) == 0
+    assert ra.docs_splits(good(d_k=96), 2) == 0
+    assert ra.docs_splits(good(dtype=ra.RA_F32, d_k=64), 4) == 1
 
 
 def test_backward_checks():

@@ -42,14 +42,13 @@ def run_docs(sh, lo, order=None):
     return out.cpu().numpy(), lse.cpu().numpy()
 
 
-SPLIT_SPAN = 8192  # positions a 128-row tile may span before it is split
 
 
 def split_tiles(sh, starts):
     """Query tiles (128 rows) of the share whose key walk is split."""
     lo = L.document_start_of(sh.q_pos, starts)
     n = sh.q_pos.size
-    return sum(int(sh.q_pos[min(t + 128, n) - 1] - lo[t] > SPLIT_SPAN) for t in range(0, n, 128))
+    return sum(int(sh.q_pos[min(t + 128, n) - 1] - lo[t] > ra.docs_split_span()) for t in range(0, n, 128))
 
 
 def check_docs(sh, starts, label):

@@ -224,6 +224,29 @@ def test_deterministic_and_staging_order_independent():
         assert np.array_equal(a[2], x[2]) and a[3] == x[3]
 
 
+def test_timed_forward_matches_and_reports_every_step():
+    """ra_forward_timed gives ra_forward's bits, one kernel time per step and
+    a staging wait that is never negative; with the side stream held back the
+    copies show up as exposed wait."""
+    case = synth.case_by_name("llama70b_stage_share")
+    sh = Share(case, 0, T=16384, n_cp=8).to_gpu()
+    f = ra.Forward(sh.gq, sh.gq_pos, sh.gk, sh.gv, sh.gk_pos)
+    o1, l1 = (t.clone() for t in f())
+    t = f.timed()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, f.out) and torch.equal(l1, f.lse)
+    n = len(sh.gk)
+    assert len(t["kernel_ms"]) == len(t["gap_ms"]) == len(t["staging_wait_ms"]) == n
+    assert all(k > 0 for k in t["kernel_ms"]) and min(t["gap_ms"]) >= 0
+    assert min(t["staging_wait_ms"]) >= 0 and t["total_ms"] >= sum(t["kernel_ms"])
+    side = ra.side_stream()
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)  # ~10 ms: the first copy lands late
+    late = f.timed()
+    assert torch.equal(o1, f.out) and torch.equal(l1, f.lse)
+    assert late["staging_wait_ms"][1] > 1.0
+
+
 def test_work_counts_give_pages_half_blocks():
     """Tile counters reproduce the pages' causal work: contiguous rank i does
     2i+1 half-blocks, zigzag ranks all do 4*n_cp."""
