@@ -161,6 +161,27 @@ ra_status ra_forward_timed(const ra_problem* p, int32_t n_cp, const void* q, con
                            void* main_stream, void* side_stream, void* const* launch_events,
                            void* const* staged_events);
 
+/*
+ * ra_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation).  Arguments and results are those of ra_forward.
+ * The running state and staging slots live in a fixed array of
+ * RA_NOALLOC_MAX_BYTES that every device the library runs on holds from the
+ * library's load until the process ends; the first call on a device takes
+ * that array's address and creates five ordering events (once), and no call
+ * allocates device memory.  A problem whose ra_forward_workspace_bytes()
+ * exceeds RA_NOALLOC_MAX_BYTES is refused with RA_ERR_WORKSPACE before any
+ * work.  Nothing in the array needs to start at zero (every step writes
+ * what it later reads), but all calls on one device share it: calls that
+ * overlap in time on one device race and give unspecified results.
+ */
+#define RA_NOALLOC_MAX_BYTES ((size_t)256 << 20)
+ra_status ra_forward_noalloc(const ra_problem* p, int32_t n_cp, const void* q,
+                             const int32_t* q_pos, const void* const* k_blocks,
+                             const void* const* v_blocks, const int32_t* const* k_pos_blocks,
+                             float* out, float* lse, int64_t* work, int64_t* staged_bytes,
+                             void* main_stream, void* side_stream);
+
 /* Bytes of device workspace ra_forward_allgather needs: 0 for bfloat16 with
  * d_k = 128 (the state stays in registers), else the running state (m, l, o). */
 size_t ra_forward_allgather_workspace_bytes(const ra_problem* p);

@@ -25,7 +25,7 @@ RA_BF16, RA_F32 = 0, 1
 
 SYMBOLS = (
     "ra_state_init", "ra_step", "ra_finalize", "ra_forward_workspace_bytes", "ra_forward",
-    "ra_forward_timed",
+    "ra_forward_timed", "ra_forward_noalloc",
     "ra_forward_allgather_workspace_bytes", "ra_forward_allgather",
     "ra_forward_allgather_docs_workspace_bytes", "ra_forward_allgather_docs",
     "ra_backward_prep", "ra_backward_workspace_bytes", "ra_backward_step",
@@ -71,6 +71,9 @@ def lib():
                              ctypes.POINTER(vp), vp, ctypes.c_size_t, vp, vp, vp,
                              ctypes.POINTER(ctypes.c_int64), vp, vp]
     L.ra_forward_timed.argtypes = L.ra_forward.argtypes + [ctypes.POINTER(vp), ctypes.POINTER(vp)]
+    L.ra_forward_noalloc.argtypes = [P, i32, vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                     ctypes.POINTER(vp), vp, vp, vp,
+                                     ctypes.POINTER(ctypes.c_int64), vp, vp]
     L.ra_forward_allgather_workspace_bytes.argtypes = [P]
     L.ra_forward_allgather_workspace_bytes.restype = ctypes.c_size_t
     L.ra_forward_allgather_docs_workspace_bytes.argtypes = [P, i32]
@@ -99,6 +102,7 @@ def lib():
     L.ra_docs_splits.argtypes = [P, i32]
     L.ra_docs_splits.restype = i32
     for name in ("ra_state_init", "ra_step", "ra_finalize", "ra_forward", "ra_forward_timed",
+                 "ra_forward_noalloc",
                  "ra_tile_shape",
                  "ra_forward_allgather", "ra_forward_allgather_docs", "ra_backward_prep",
                  "ra_backward_step",
@@ -342,6 +346,36 @@ class Forward:
         total_ms = cp[0].elapsed_time(en[n - 1])
         return {"kernel_ms": kernel_ms, "gap_ms": gap_ms, "staging_wait_ms": wait_ms,
                 "total_ms": total_ms}
+
+
+NOALLOC_MAX_BYTES = 256 << 20  # RA_NOALLOC_MAX_BYTES of include/ra.h
+
+
+def forward_noalloc(q, q_pos, k_blocks, v_blocks, k_pos_blocks, out, lse, work=None, causal=True,
+                    scale=None, side=True, stream=None):
+    """ra_forward_noalloc: the ring forward with the library's fixed per-device
+    workspace; ``out`` (fp32 like q) and ``lse`` are the caller's.  Returns
+    the staged byte count.  Calls that overlap on one device race."""
+    _need_gpu(q, q_pos, *k_blocks, *v_blocks, *k_pos_blocks, out, lse, work)
+    n_cp = len(k_blocks)
+    if not (n_cp == len(v_blocks) == len(k_pos_blocks)) or n_cp < 1:
+        raise ValueError("need n_cp >= 1 blocks of k, v and k_pos")
+    _check_rows(q, q_pos, k_blocks, v_blocks, k_pos_blocks)
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != torch.float32 \
+            or tuple(lse.shape) != tuple(q.shape[:2]) or lse.dtype != torch.float32:
+        raise ValueError("out must be float32 like q and lse float32 [h_q][n_q]")
+    p = _problem_from(q, k_blocks[0], causal, scale)
+    arr = ctypes.c_void_p * n_cp
+    main = torch.cuda.current_stream() if stream is None else stream
+    sd = side_stream(q.device) if side else None
+    staged = ctypes.c_int64(0)
+    _check(lib().ra_forward_noalloc(
+        ctypes.byref(p), n_cp, _ptr(q), _ptr(q_pos), arr(*[t.data_ptr() for t in k_blocks]),
+        arr(*[t.data_ptr() for t in v_blocks]), arr(*[t.data_ptr() for t in k_pos_blocks]),
+        _ptr(out), _ptr(lse), _ptr(work), ctypes.byref(staged), _stream(main),
+        ctypes.c_void_p(sd.cuda_stream) if sd is not None else ctypes.c_void_p(0)),
+        "ra_forward_noalloc")
+    return staged.value
 
 
 class ForwardGraph:

@@ -377,6 +377,24 @@ ra_status ra_forward_timed(const ra_problem* p, int32_t n_cp, const void* q, con
                            float* out, float* lse, int64_t* work, int64_t* staged_bytes,
                            void* main_stream, void* side_stream, void* const* launch_events,
                            void* const* staged_events) {
+  return ra::forward_ring(p, n_cp, q, q_pos, k_blocks, v_blocks, k_pos_blocks, workspace,
+                          ws_bytes, out, lse, work, staged_bytes, main_stream, side_stream,
+                          launch_events, staged_events, nullptr);
+}
+
+}  // extern "C"
+
+size_t ra::forward_workspace_bytes(const ra_problem* p) { return ws_layout(p).total; }
+
+// The ring of ra_forward.  fixed: null, or five events made by the caller
+// (no timing, no system fence) that this call uses instead of creating and
+// destroying its own.
+ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, const int32_t* q_pos,
+                           const void* const* k_blocks, const void* const* v_blocks,
+                           const int32_t* const* k_pos_blocks, void* workspace, size_t ws_bytes,
+                           float* out, float* lse, int64_t* work, int64_t* staged_bytes,
+                           void* main_stream, void* side_stream, void* const* launch_events,
+                           void* const* staged_events, const hipEvent_t* fixed) {
   ra_status st = check_problem(p);
   if (st != RA_OK) return st;
   if (n_cp < 1) return RA_ERR_SHAPE;
@@ -460,8 +478,14 @@ ra_status ra_forward_timed(const ra_problem* p, int32_t n_cp, const void* q, con
            hipSuccess;
   };
   if (use_side && n_cp > 1) {
-    if (!mk(&ev_start) || !mk(&ev_staged[0]) || !mk(&ev_staged[1]) || !mk(&ev_used[0]) ||
-        !mk(&ev_used[1])) {
+    if (fixed) {
+      ev_start = fixed[0];
+      ev_staged[0] = fixed[1];
+      ev_staged[1] = fixed[2];
+      ev_used[0] = fixed[3];
+      ev_used[1] = fixed[4];
+    } else if (!mk(&ev_start) || !mk(&ev_staged[0]) || !mk(&ev_staged[1]) || !mk(&ev_used[0]) ||
+               !mk(&ev_used[1])) {
       result = RA_ERR_HIP;
       goto cleanup;
     }
@@ -522,10 +546,13 @@ ra_status ra_forward_timed(const ra_problem* p, int32_t n_cp, const void* q, con
   if (staged_bytes) *staged_bytes = staged;
 
 cleanup:
-  for (hipEvent_t e : {ev_start, ev_staged[0], ev_staged[1], ev_used[0], ev_used[1]})
-    if (e) (void)hipEventDestroy(e);  // the call's status is already decided
+  if (!fixed)
+    for (hipEvent_t e : {ev_start, ev_staged[0], ev_staged[1], ev_used[0], ev_used[1]})
+      if (e) (void)hipEventDestroy(e);  // the call's status is already decided
   return result;
 }
+
+extern "C" {
 
 ra_status ra_backward_prep(const ra_problem* p, const float* out, const void* dout,
                            float* delta, void* stream) {

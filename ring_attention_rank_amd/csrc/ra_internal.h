@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/ra.h"
+
 namespace ra {
 
 constexpr int kWave = 64;          // CDNA wavefront width
@@ -17,6 +19,18 @@ constexpr int kMaxBlocks = 64;     // key/value blocks of one all-gather launch
 // many positions from its first row's document start to its last row is
 // split over several workgroups (its walk over the blocks is long).
 constexpr int kSplitSpan = 8192;
+
+// The ring forward behind ra_forward / ra_forward_timed (arguments as
+// there); fixed: null, or five caller-made events (no timing, no system
+// fence) used in place of per-call ones.  forward_workspace_bytes: the
+// workspace it needs (the problem already checked).
+ra_status forward_ring(const ra_problem* p, int32_t n_cp, const void* q, const int32_t* q_pos,
+                       const void* const* k_blocks, const void* const* v_blocks,
+                       const int32_t* const* k_pos_blocks, void* workspace, size_t ws_bytes,
+                       float* out, float* lse, int64_t* work, int64_t* staged_bytes,
+                       void* main_stream, void* side_stream, void* const* launch_events,
+                       void* const* staged_events, const hipEvent_t* fixed);
+size_t forward_workspace_bytes(const ra_problem* p);
 
 // Arguments of one ring-step launch (one key/value block against all local
 // queries of all heads).  READ selects whether the state is read (else it

@@ -135,6 +135,19 @@ def test_forward_timed_checks():
     assert L.ra_forward_timed(*args(2, v, need), None, cps) == NULL
 
 
+def test_forward_noalloc_refuses_oversize():
+    """A share whose workspace exceeds RA_NOALLOC_MAX_BYTES is refused before
+    any device call; a bad problem reports its own error."""
+    L = ra.lib()
+    v = ctypes.c_void_p(FAKE)
+    arr = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    big = good(n_q=8192, h_q=64, h_kv=1)
+    assert ra.workspace_bytes(big) > ra.NOALLOC_MAX_BYTES
+    args = lambda p: (ctypes.byref(p), 2, v, v, arr, arr, arr, v, v, None, None, None, None)
+    assert L.ra_forward_noalloc(*args(big)) == WORKSPACE
+    assert L.ra_forward_noalloc(*args(good(d_k=96))) == SHAPE
+
+
 def test_debug_position_check(monkeypatch):
     """RA_DEBUG=1 makes the binding refuse positions that do not increase and
     document starts that decrease; without it nothing is checked."""
