@@ -5,10 +5,16 @@
 // "distributed/context-expert", section "Splitting the sequence, and the one
 // layer that objects"), organised for CDNA4 throughput:
 //
-//  * Two waves per SIMD.  A workgroup is 8 waves: two groups of 4 waves
-//    on the same 128 query rows (32 per wave).  Group g takes the key tiles
-//    j = g, g+2, g+4, ... of the block; the two partial states are folded
-//    together through LDS at the end (the same online-softmax fold).
+//  * Two waves per SIMD, in one of two forms chosen per launch.  With fewer
+//    than two workgroup-sized work units (query tile pair x head) per
+//    compute unit, a workgroup is 8 waves: two groups of 4 waves on the same
+//    128 query rows (32 per wave).  Group g takes the key tiles j = g, g+2,
+//    g+4, ... of the block; the two partial states are folded together
+//    through LDS at the end (the same online-softmax fold).  With at least
+//    two units per compute unit, a workgroup is one group of 4 waves taking
+//    every key tile, and two such workgroups share a compute unit: their
+//    waves pair up on each SIMD without the barriers that tie the two
+//    groups of one workgroup together (4-5% faster where it applies).
 //  * No staging registers.  K and V tiles go from HBM straight into LDS with
 //    buffer_load_dwordx4 ... lds, in row-major 256-byte rows whose 16-byte chunks
 //    are XOR-swizzled by row, so both read patterns below are free of bank
@@ -22,12 +28,12 @@
 //  * The V^T operand comes from row-major V with ds_read_b64_tr_b16: within
 //    each 16-lane group, lane j receives element j of the 4 rows the group
 //    addressed, i.e. 4 consecutive keys of one d column.
-//  * Ping-pong between the two groups.  Each group alternates a softmax
-//    phase (VALU: classify, mask, row max, rescale, exponentials) and a GEMM
-//    phase (MFMA: P V of that tile, then S^T of its next tile), with a
-//    workgroup barrier after every phase.  Group 1 runs one phase behind
-//    group 0, so on each SIMD one wave keeps the matrix pipe busy while the
-//    other runs the softmax, and every barrier swaps the roles.
+//  * Each group alternates a softmax phase (VALU: classify, mask, row max,
+//    rescale, exponentials) and a GEMM phase (MFMA: P V of that tile, then
+//    S^T of its next tile), with a workgroup barrier after every phase.  In
+//    the two-group form group 1 runs one phase behind group 0 (a ping-pong),
+//    so on each SIMD one wave keeps the matrix pipe busy while the other runs
+//    the softmax, and every barrier swaps the roles.
 //  * Loads are DMA issued three phases before their use and waited for with
 //    explicit vmcnt counts; K and V tiles have two stages per group,
 //    positions three.
@@ -58,7 +64,11 @@ constexpr int D = 128;
 constexpr int BN = 64;                      // keys per tile
 constexpr int ROWS = 128;                   // query rows per workgroup tile
 constexpr int WAVE_ROWS = 32;
-constexpr int THREADS = 512;                // 8 waves: 2 groups of 4
+// G, the groups of 4 waves in a workgroup, is a template parameter: 2 runs
+// the ping-pong of the two groups on the same query rows, 1 a single group
+// per workgroup with two workgroups resident per compute unit.
+template <int G>
+constexpr int threads() { return 256 * G; }
 constexpr int TILE_BYTES = BN * D * 2;      // 16 KiB
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -72,14 +82,25 @@ constexpr int kBufferFlags = 0x00020000;
 static_assert(ROWS == 4 * WAVE_ROWS, "4 waves per group");
 static_assert(kRowsPerGroup == ROWS, "host launch geometry");
 
+template <int G>
 struct __attribute__((aligned(1024))) Smem {
-  uint8_t k[2][2][TILE_BYTES];   // [group][stage]
-  uint8_t v[2][2][TILE_BYTES];
-  int32_t pos[2][3][BN];         // [group][stage]
+  uint8_t k[G][2][TILE_BYTES];   // [group][stage]
+  uint8_t v[G][2][TILE_BYTES];
+  int32_t pos[G][3][BN];         // [group][stage]
 };
 // The merge of the two groups reuses the K/V area.
 static_assert(4 * 64 * 64 * 4 + 4 * 64 * 2 * 4 <= (int)sizeof(uint8_t[2][2][TILE_BYTES]) * 2,
               "merge buffer fits");
+// One group per workgroup: two workgroups fit the compute unit's 160 KiB.
+static_assert(2 * sizeof(Smem<1>) <= 160 * 1024, "two one-group workgroups per CU");
+
+// A value the compiler cannot see through.  With one group the group index
+// is always 0; folding that constant into the loop bodies made the compiler
+// hoist enough to spill 50-190 registers, so it is computed at run time.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 __device__ __forceinline__ int sigma(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 
@@ -143,10 +164,10 @@ __device__ __forceinline__ void dma_words_to_lds(const i32x4& rsrc, uint32_t lds
 __device__ __forceinline__ int k_chunk_off(int r, int c) { return r * 256 + 16 * (c ^ (r & 15)); }
 __device__ __forceinline__ int v_chunk_off(int r, int c) { return r * 256 + 16 * (c ^ (4 * (r & 3))); }
 
-template <bool READ, bool FINAL, bool DOCS = false>
+template <int G, bool READ, bool FINAL, bool DOCS = false>
 struct Step {
   const StepArgs& a;
-  Smem& sm;
+  Smem<G>& sm;
   const int tid, lane, gwave, grp, h, col;
   const int n_q, n_k;
   const bool causal;
@@ -186,10 +207,10 @@ struct Step {
   f32x16 sc[2];        // scores of one own tile (S^T, two 32-key halves)
   bf16x8 pp[2][2];      // its probabilities, bf16
 
-  __device__ Step(const StepArgs& a_, Smem& sm_, int tid_)
+  __device__ Step(const StepArgs& a_, Smem<G>& sm_, int tid_)
       : a(a_), sm(sm_), tid(tid_), lane(tid_ & 63),
         gwave(__builtin_amdgcn_readfirstlane((tid_ >> 6) & 3)),
-        grp(__builtin_amdgcn_readfirstlane(tid_ >> 8)), h((tid_ & 63) >> 5), col(tid_ & 31),
+        grp(__builtin_amdgcn_readfirstlane(G == 1 ? opaque(tid_ >> 8) : tid_ >> 8)), h((tid_ & 63) >> 5), col(tid_ & 31),
         n_q(a_.n_q), n_k(a_.n_k), causal(a_.causal != 0), kbase(nullptr), vbase(nullptr) {
     // Tile loads: wave w fills rows 16w .. 16w+15 of a tile, load i rows
     // 16w + 4i + L/16 for lane L, which writes physical chunk L%16 of its
@@ -203,9 +224,9 @@ struct Step {
       }
       v_ld_off = (L / 16) * 256 + 16 * ((L % 16) ^ (4 * ((L / 16) & 3)));
       const uint32_t base = (uint32_t)(uintptr_t)(lds_void*)&sm_;
-      lds_k = base + (uint32_t)offsetof(Smem, k) + grp * 2 * TILE_BYTES;
-      lds_v = base + (uint32_t)offsetof(Smem, v) + grp * 2 * TILE_BYTES;
-      lds_pos = base + (uint32_t)offsetof(Smem, pos) + grp * 3 * BN * 4;
+      lds_k = base + (uint32_t)offsetof(Smem<G>, k) + grp * 2 * TILE_BYTES;
+      lds_v = base + (uint32_t)offsetof(Smem<G>, v) + grp * 2 * TILE_BYTES;
+      lds_pos = base + (uint32_t)offsetof(Smem<G>, pos) + grp * 3 * BN * 4;
     }
     // K reads: row sigma(col) (+32 kb), logical chunk 2ks + h.
     {
@@ -259,8 +280,8 @@ struct Step {
       load_pos(j0_b + grp, 0);
     }
     if (n_own_b > 1) {
-      load_k_tile(j0_b + 2 + grp, 1);
-      load_pos(j0_b + 2 + grp, 1);
+      load_k_tile(j0_b + G + grp, 1);
+      load_pos(j0_b + G + grp, 1);
     }
   }
 
@@ -390,10 +411,10 @@ struct Step {
     // The batch's DMA instructions are spread over the phase: a wave that
     // issues them back to back stalls on the CU's load path (64 B/clk).
     const bool has_k = s + 2 < n_own, has_v = s + 1 < n_own;
-    if (has_k) load_k_tile(tile0() + 2 * (s + 2) + grp, s & 1);
+    if (has_k) load_k_tile(tile0() + G * (s + 2) + grp, s & 1);
     __builtin_amdgcn_sched_barrier(0);
 
-    const int j = tile0() + 2 * s + grp;
+    const int j = tile0() + G * s + grp;
     const int nvalid = min(BN, n_k - j * BN);
     const bool skip = j >= n_vis_w || (DOCS && j < lo_vis_w);
     const bool full = j < n_full_w && (!DOCS || j >= lo_full_w);
@@ -425,11 +446,11 @@ struct Step {
     }
     const float muse = (m2 == -INFINITY) ? 0.f : m2;
     __builtin_amdgcn_sched_barrier(0);
-    if (has_v) load_v_tile(tile0() + 2 * (s + 1) + grp, (s + 1) & 1);
+    if (has_v) load_v_tile(tile0() + G * (s + 1) + grp, (s + 1) & 1);
     __builtin_amdgcn_sched_barrier(0);
     exp_pack(sc[0], muse, pp[0]);
     __builtin_amdgcn_sched_barrier(0);
-    if (has_k) load_pos(tile0() + 2 * (s + 2) + grp, (s + 2) % 3);
+    if (has_k) load_pos(tile0() + G * (s + 2) + grp, (s + 2) % 3);
     __builtin_amdgcn_sched_barrier(0);
     exp_pack(sc[1], muse, pp[1]);
     pin_softmax();
@@ -550,7 +571,9 @@ struct Step {
     return c;
   }
   // This group's own tiles among n_iter visited key tiles.
-  __device__ __forceinline__ int own_tiles(int n_it) const { return (n_it - grp + 1) / 2; }
+  __device__ __forceinline__ int own_tiles(int n_it) const {
+    return (n_it - grp + G - 1) / G;
+  }
   __device__ __forceinline__ void use_classes(const Classes& c) {
     n_kt = (n_k + BN - 1) / BN;
     n_iter = c.n_iter;
@@ -560,7 +583,7 @@ struct Step {
     lo_full_w = c.lo_full_w;
     lo_vis_w = c.lo_vis_w;
     // tiles of this group among all key tiles, and among the visited ones
-    n_kt_g = (n_kt - grp + 1) / 2;
+    n_kt_g = (n_kt - grp + G - 1) / G;
     n_own = own_tiles(n_iter);
   }
   __device__ __forceinline__ void classify(const int32_t* k_pos) { use_classes(classes_of(k_pos)); }
@@ -648,7 +671,7 @@ struct Step {
         wait_loads(0);
       }
       phase_barrier();
-      if (grp == 1) phase_barrier();
+      if (G == 2 && grp == 1) phase_barrier();
       if (n_own > 0) gemm_phase<false, true>(-1);
       phase_barrier();
       for (int s = 0; s + 1 < n_own; ++s) {
@@ -663,9 +686,11 @@ struct Step {
         gemm_phase<true, false>(n_own - 1);
         phase_barrier();
       }
-      const int n0 = (n_iter + 1) / 2, n1 = n_iter / 2;
-      const int n_bar = max(2 * n0 + 1, 2 * n1 + 2);
-      for (int b = grp + 1 + 2 * n_own; b < n_bar; ++b) phase_barrier();
+      if (G == 2) {
+        const int n0 = (n_iter + 1) / 2, n1 = n_iter / 2;
+        const int n_bar = max(2 * n0 + 1, 2 * n1 + 2);
+        for (int b = grp + 1 + 2 * n_own; b < n_bar; ++b) phase_barrier();
+      }
     }
     if (count && lane == 0) {
       atomicAdd(a.work + 0, (unsigned long long)cnt_full);
@@ -676,7 +701,8 @@ struct Step {
 
   // Folds group 1's partial state into group 0's through LDS and writes the
   // result: normalised out/lse (FINAL) or the running state.
-  __device__ __forceinline__ void finish() {
+  // Two groups: group 1's partial state folds into group 0's through LDS.
+  __device__ __forceinline__ void merge_groups() {
     __syncthreads();  // every wave is done with the K/V stages
     float* mo = (float*)&sm.k[0][0][0];            // [wave][reg][lane] O^T values
     float* ml = mo + 4 * 64 * 64;                  // [wave][lane] m2, then lsum
@@ -689,8 +715,7 @@ struct Step {
       ml[4 * 64 + gwave * 64 + lane] = lsum;
     }
     __syncthreads();
-    if (grp == 1) return;
-    {
+    if (grp == 0) {
       const float m2b = ml[gwave * 64 + lane];
       const float lb = ml[4 * 64 + gwave * 64 + lane];
       const float mn = fmaxf(m2, m2b);
@@ -704,6 +729,11 @@ struct Step {
       lsum = lsum * fa + lb * fb;
       m2 = mn;
     }
+  }
+
+  __device__ __forceinline__ void finish() {
+    if constexpr (G == 2) merge_groups();
+    if (grp == 1) return;
 
     const float ltot = half_swap_sum(lsum);
     if (row >= n_q) return;
@@ -830,16 +860,16 @@ struct Step {
   }
 };
 
-template <bool READ, bool FINAL>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int G, bool READ, bool FINAL>
+__global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void step_kernel_fast(const StepArgs a) {
-  __shared__ Smem sm;
+  __shared__ Smem<G> sm;
   const int tid = threadIdx.x;
   const int u = blockIdx.x;
   const int head = a.head_of[u % a.h_q];
   const int p = u / a.h_q;
   const int t_hi = a.n_qt - 1 - p, t_lo = p;
-  Step<READ, FINAL> s(a, sm, tid);
+  Step<G, READ, FINAL> s(a, sm, tid);
   s.run(t_hi, head);
   if (t_lo < t_hi) {
     __syncthreads();
@@ -849,16 +879,16 @@ void step_kernel_fast(const StepArgs a) {
 
 // All-gather form: every key/value block resident, one launch.  DOCS: each
 // query's keys are also bounded below by its document start (a.q_lo).
-template <bool DOCS>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int G, bool DOCS>
+__global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void allgather_kernel_fast(const MultiArgs ma) {
-  __shared__ Smem sm;
+  __shared__ Smem<G> sm;
   const int tid = threadIdx.x;
   const int u = blockIdx.x;
   const int head = ma.s.head_of[u % ma.s.h_q];
   const int p = u / ma.s.h_q;
   const int t_hi = ma.s.n_qt - 1 - p, t_lo = p;
-  Step<false, true, DOCS> s(ma.s, sm, tid);
+  Step<G, false, true, DOCS> s(ma.s, sm, tid);
   s.run_all(ma, t_hi, head);
   if (t_lo < t_hi) {
     __syncthreads();
@@ -884,16 +914,16 @@ __device__ __forceinline__ bool split_tile(const int32_t* q_pos, const int32_t* 
   return q_pos[last] - q_lo[t * ROWS] > kSplitSpan;
 }
 
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void allgather_split_kernel_fast(const MultiArgs ma, int n_split) {
-  __shared__ Smem sm;
+  __shared__ Smem<2> sm;
   const int tid = threadIdx.x;
   const int u = blockIdx.x;
   const int sp = blockIdx.y;
   const int head = ma.s.head_of[u % ma.s.h_q];
   const int p = u / ma.s.h_q;
   const int t_hi = ma.s.n_qt - 1 - p, t_lo = p;
-  Step<false, false, true> s(ma.s, sm, tid);
+  Step<2, false, false, true> s(ma.s, sm, tid);
   for (int k = 0; k < 2; ++k) {
     const int t = k == 0 ? t_hi : t_lo;
     if (k == 1) {
@@ -949,7 +979,7 @@ void merge_splits_kernel(const float* __restrict__ m, const float* __restrict__ 
 }  // namespace fast
 
 hipError_t launch_allgather_split_fast(const MultiArgs& ma, int n_split, hipStream_t stream) {
-  dim3 grid((unsigned)(ma.s.n_pairs * ma.s.h_q), (unsigned)n_split), block(fast::THREADS);
+  dim3 grid((unsigned)(ma.s.n_pairs * ma.s.h_q), (unsigned)n_split), block(fast::threads<2>());
   hipLaunchKernelGGL(fast::allgather_split_kernel_fast, grid, block, 0, stream, ma, n_split);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -962,18 +992,39 @@ hipError_t launch_allgather_split_fast(const MultiArgs& ma, int n_split, hipStre
   return hipGetLastError();
 }
 
+// Groups per workgroup for a launch of `units` workgroup-sized work units
+// (query tile pairs x heads): one group when there are at least two units per
+// compute unit, so that two one-group workgroups share each compute unit;
+// otherwise the two-group ping-pong keeps both waves of a SIMD busy.
+static int groups_for(long long units) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return units >= 2LL * cus ? 1 : 2;
+}
+
 hipError_t launch_allgather_fast(const MultiArgs& ma, hipStream_t stream) {
-  dim3 grid((unsigned)(ma.s.n_pairs * ma.s.h_q)), block(fast::THREADS);
+  const int g = ma.s.q_lo != nullptr ? 2 : groups_for((long long)ma.s.n_pairs * ma.s.h_q);
+  dim3 grid((unsigned)(ma.s.n_pairs * ma.s.h_q)), block(256 * g);
   if (ma.s.q_lo != nullptr)
-    hipLaunchKernelGGL(fast::allgather_kernel_fast<true>, grid, block, 0, stream, ma);
+    hipLaunchKernelGGL((fast::allgather_kernel_fast<2, true>), grid, block, 0, stream, ma);
+  else if (g == 1)
+    hipLaunchKernelGGL((fast::allgather_kernel_fast<1, false>), grid, block, 0, stream, ma);
   else
-    hipLaunchKernelGGL(fast::allgather_kernel_fast<false>, grid, block, 0, stream, ma);
+    hipLaunchKernelGGL((fast::allgather_kernel_fast<2, false>), grid, block, 0, stream, ma);
   return hipGetLastError();
 }
 
-hipError_t launch_step_fast(const StepArgs& a, bool read, bool final_, hipStream_t stream,
-                            hipEvent_t start, hipEvent_t stop) {
-  dim3 grid((unsigned)(a.n_pairs * a.h_q)), block(fast::THREADS);
+template <int G>
+static void launch_step_g(const StepArgs& a, bool read, bool final_, hipStream_t stream,
+                          hipEvent_t start, hipEvent_t stop) {
+  dim3 grid((unsigned)(a.n_pairs * a.h_q)), block(256 * G);
   auto go = [&](auto kernel) {
     if (start || stop)
       hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0, a);
@@ -981,13 +1032,21 @@ hipError_t launch_step_fast(const StepArgs& a, bool read, bool final_, hipStream
       hipLaunchKernelGGL(kernel, grid, block, 0, stream, a);
   };
   if (read && final_)
-    go(fast::step_kernel_fast<true, true>);
+    go(fast::step_kernel_fast<G, true, true>);
   else if (read)
-    go(fast::step_kernel_fast<true, false>);
+    go(fast::step_kernel_fast<G, true, false>);
   else if (final_)
-    go(fast::step_kernel_fast<false, true>);
+    go(fast::step_kernel_fast<G, false, true>);
   else
-    go(fast::step_kernel_fast<false, false>);
+    go(fast::step_kernel_fast<G, false, false>);
+}
+
+hipError_t launch_step_fast(const StepArgs& a, bool read, bool final_, hipStream_t stream,
+                            hipEvent_t start, hipEvent_t stop) {
+  if (groups_for((long long)a.n_pairs * a.h_q) == 1)
+    launch_step_g<1>(a, read, final_, stream, start, stop);
+  else
+    launch_step_g<2>(a, read, final_, stream, start, stop);
   return hipGetLastError();
 }
 

@@ -101,6 +101,22 @@ def test_ragged_and_small(dtype, d_k, n_q, n_k, h_q, h_kv):
     check_share(sh, f"ragged {dtype} d{d_k} nq{n_q} nk{n_k}")
 
 
+@pytest.mark.parametrize("n_q,h_q,h_kv,causal", [(1000, 128, 8, True), (1024, 128, 1, False),
+                                                 (2048, 64, 64, True)])
+def test_one_group_workgroups(n_q, h_q, h_kv, causal):
+    """Launches of at least two tile pairs x heads per compute unit (512 on
+    MI355X) run one 4-wave group per workgroup instead of the two-group
+    ping-pong; the same parity, ragged last tile included."""
+    rng = np.random.default_rng(n_q + h_q)
+    sh = _custom_share(rng, "bf16", 128, h_q, h_kv, n_q, 160, 2, causal=causal)
+    n_pairs = ((n_q + 127) // 128 + 1) // 2
+    assert n_pairs * h_q >= 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    check_share(sh, f"one group nq{n_q} h{h_q}/{h_kv} causal={causal}")
+    ro, rl = sh.oracle()
+    out, lse, _ = ra.forward_allgather(sh.gq, sh.gq_pos, sh.gk, sh.gv, sh.gk_pos, causal=causal)
+    compare(out.cpu(), lse.cpu(), ro, rl, TOL["bf16"], "one group all-gather")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_noncausal(dtype):
     rng = np.random.default_rng(11)
