@@ -39,8 +39,15 @@ KERNEL_SOURCE = os.path.join(ROOT, "ring_attention_rank_amd", "csrc", "ra_fast.h
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_SUMMARY = os.path.join(PROFILES, "traffic_step_kernel_fast_llama405b_stage_share.md")
 # The dominant kernel of the ring forward: a middle step (reads and writes the
-# running state), n_cp - 2 of the n_cp launches.
-DOMINANT = "step_kernel_fast<true, false>"
+# running state), n_cp - 2 of the n_cp launches.  G is its groups of 4 waves
+# per workgroup: 1 when the launch has at least two query-tile pairs x heads
+# per compute unit, else 2 (the library's own rule).
+
+
+def dominant_kernel(case, n_q, cus):
+    n_pairs = ((n_q + 127) // 128 + 1) // 2
+    g = 1 if n_pairs * case.h_q >= 2 * cus else 2
+    return f"step_kernel_fast<{g}, true, false>"
 # The other workloads of the size table timed beside the headline (bf16, d_k=128).
 SIDE_WORKLOADS = ("llama8b_gqa_zigzag", "llama70b_stage_share", "million_striped_mha")
 
@@ -285,7 +292,7 @@ def time_call(f, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
-def side_workload(name, dev, steps, warmup, timing_reps):
+def side_workload(name, dev, steps, warmup, timing_reps, cus):
     """One more workload of the size table, timed like the headline: the ring
     forward (every rank share the case lists), its per-launch kernel times
     and staging waits (last rank), and the all-gather form of the last share."""
@@ -304,7 +311,8 @@ def side_workload(name, dev, steps, warmup, timing_reps):
                    "n_k_per_block": len(share["k_pos"][0])},
         "per_rank": ring["per_rank"],
         "dominant_kernel": {
-            "kernel": DOMINANT, "event_mean_ms": t["middle_mean_ms"],
+            "kernel": dominant_kernel(case, len(share["q_pos"]), cus),
+            "event_mean_ms": t["middle_mean_ms"],
             "achieved": t["middle_tflops"], "frac": t["middle_tflops"] / PEAK_BF16_TFLOPS,
             "traced_avg_us": committed_trace_us(name)},
         "staging_wait_ms_total": t["staging_wait_ms_total"], "gap_ms_total": t["gap_ms_total"],
@@ -379,7 +387,8 @@ def main():
         # kernel time, HIP events around each launch on its stream
         "bound": "mfma", "achieved": t["middle_tflops"], "peak": peak, "unit": "TFLOP/s",
         "frac": t["middle_tflops"] / peak, "traffic": committed_traffic(case.name),
-        "kernel": (DOMINANT + " (bf16 MFMA 32x32x16)") if fast else "step_kernel<true, false> (generic)",
+        "kernel": (dominant_kernel(case, len(share["q_pos"]), props.multi_processor_count) +
+                   " (bf16 MFMA 32x32x16)") if fast else "step_kernel<true, false> (generic)",
         "flops_per_launch": t["middle_flops_per_launch"], "avg_launch_ms": t["middle_mean_ms"],
         "launches_per_step": n_launch, "middle_launches_per_step": t["middle_launches"],
         # the committed kernel trace of the same command (rocprofv3 --stats)
@@ -490,7 +499,8 @@ def main():
         for name in SIDE_WORKLOADS:
             print(f"[bench] side workload {name}", file=sys.stderr, flush=True)
             result["side_workloads"][name] = side_workload(name, dev, args.steps, args.warmup,
-                                                           args.timing_reps)
+                                                           args.timing_reps,
+                                                           props.multi_processor_count)
     print(json.dumps(result), flush=True)
 
 
