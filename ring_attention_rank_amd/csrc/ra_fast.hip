@@ -363,19 +363,23 @@ struct Step {
   }
 
   __device__ __forceinline__ void exp_pack(const f32x16& s, float muse, bf16x8 (&p)[2]) {
-    float acc0 = 0.f, acc1 = 0.f;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = fast_exp2(__builtin_fmaf(s[r], c2, -muse));
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        float x0 = fast_exp2(__builtin_fmaf(s[8 * t + e], c2, -muse));
-        float x1 = fast_exp2(__builtin_fmaf(s[8 * t + e + 1], c2, -muse));
-        p[t][e] = (__bf16)x0;
-        p[t][e + 1] = (__bf16)x1;
-        acc0 += x0;
-        acc1 += x1;
-      }
-    lsum += acc0 + acc1;
+      for (int e = 0; e < 8; ++e) p[t][e] = (__bf16)x[8 * t + e];
+    // four chains started from their first term: 12 adds, 3 to combine
+    float a0 = x[0], a1 = x[1], a2 = x[2], a3 = x[3];
+#pragma unroll
+    for (int r = 4; r < 16; r += 4) {
+      a0 += x[r];
+      a1 += x[r + 1];
+      a2 += x[r + 2];
+      a3 += x[r + 3];
+    }
+    lsum += (a0 + a1) + (a2 + a3);
   }
 
   // Empty asm statements that make the phase's results exist at this point:
@@ -429,12 +433,19 @@ struct Step {
       mask(sc[0], pos, 0, qp, nvalid);
       mask(sc[1], pos, 1, qp, nvalid);
     }
+    // four chains of three-input maxima over the 32 scores (v_max3: fewer
+    // VALU instructions, which matters where the chip is power-limited)
     float mx4[4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) mx4[x] = fmaxf(sc[0][x], sc[1][x]);
-#pragma unroll
-    for (int r = 4; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], fmaxf(sc[0][r], sc[1][r]));
-    const float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+    for (int c = 0; c < 4; ++c) {
+      const f32x16& x = sc[c >> 1];
+      const int o = 8 * (c & 1);
+      float m = __builtin_fmaxf(__builtin_fmaxf(x[o], x[o + 1]), x[o + 2]);
+      m = __builtin_fmaxf(__builtin_fmaxf(m, x[o + 3]), x[o + 4]);
+      m = __builtin_fmaxf(__builtin_fmaxf(m, x[o + 5]), x[o + 6]);
+      mx4[c] = __builtin_fmaxf(m, x[o + 7]);
+    }
+    const float mx = __builtin_fmaxf(__builtin_fmaxf(mx4[0], mx4[1]), __builtin_fmaxf(mx4[2], mx4[3]));
     const float mloc = half_swap_max(mx) * c2;
     // O is rescaled in the next GEMM phase, where the VALU is otherwise idle.
     resc = __ballot(mloc > m2) != 0;
