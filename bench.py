@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import ring_attention_rank_amd as ra  # noqa: E402
+from ring_attention_rank_amd import comm  # noqa: E402
 import synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
@@ -243,6 +244,26 @@ def launch_timing(fwd, pairs_per_step, case, reps):
     }
 
 
+def comm_model(case, staged_bytes, step_ms):
+    """The pages' exchange model for this share (Zero to Frontier, "What
+    context parallelism communicates" and "When the ring hides its
+    communication"): bytes a GPU receives per layer by ring and by Ulysses,
+    the group size above which Ulysses moves less, and the link bandwidth a
+    real ring would need for one key/value block to arrive within one
+    measured step."""
+    d, d_kv = case.h_q * case.d_k, case.h_kv * case.d_k
+    eb = 2 if case.dtype == "bf16" else 4
+    block = comm.kv_block_bytes(case.T // case.n_cp, d_kv, eb)
+    ring = comm.cp_comm_bytes(case.T, d, d_kv, case.n_cp, "ring", eb)
+    return {
+        "ring_bytes_per_layer": ring, "staged_bytes_measured": staged_bytes,
+        "ulysses_bytes_per_layer": comm.cp_comm_bytes(case.T, d, d_kv, case.n_cp, "ulysses", eb),
+        "ulysses_breakeven_group": comm.ulysses_breakeven(case.h_q, case.h_kv),
+        "kv_block_bytes": block, "middle_step_ms": step_ms,
+        "link_GBps_to_hide_each_step": block / (step_ms * 1e-3) / 1e9,
+    }
+
+
 def time_ring(case, ranks, dev, steps, warmup, side=True):
     """The headline measure: ``steps`` ra_forward calls per rank share after
     ``warmup`` untimed ones, wall clock with the device synchronised on both
@@ -430,6 +451,7 @@ def main():
             "gap_ms_total": t["gap_ms_total"], "kernel_ms_total": t["kernel_ms_total"],
             "forward_ms": t["forward_ms"], "reps": t["reps"],
         },
+        "comm_model": comm_model(case, fwd.staged.value, t["middle_mean_ms"]),
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "sclk_mhz": committed_sclk_mhz(case.name) if fast else None},
     }

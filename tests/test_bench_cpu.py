@@ -12,6 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
+import synth  # noqa: E402
 
 
 def test_more_than_one_gpu_is_refused():
@@ -60,3 +61,15 @@ def test_document_mask_pair_count_matches_brute_force():
             same = oracle.doc_ids(kp, starts)[None, :] == oracle.doc_ids(qp, starts)[:, None]
             brute = int(((kp[None, :] <= qp[:, None]) & same).sum())
             assert bench.visible_pairs_docs(qp, lo, kp) == brute
+
+
+def test_comm_model_of_the_405b_share():
+    """The pages' exchange model for the headline share: 15 incoming blocks of
+    4 MiB (the 63 MB of the pages), Ulysses' break-even group 1 + 16/1, and
+    the link rate that lands one block within one step."""
+    case = synth.case_by_name("llama405b_stage_share")
+    m = bench.comm_model(case, 62914560, 0.25)
+    assert m["ring_bytes_per_layer"] == m["staged_bytes_measured"] == 15 * 4194304
+    assert m["kv_block_bytes"] == 4194304 and m["ulysses_breakeven_group"] == 17
+    assert m["ulysses_bytes_per_layer"] > m["ring_bytes_per_layer"]  # n_cp = 16 < 17
+    assert abs(m["link_GBps_to_hide_each_step"] - 4194304 / 0.25e-3 / 1e9) < 1e-9
