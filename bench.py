@@ -193,7 +193,8 @@ def cpu_baseline(case, share, out, lse, budget_rows):
 def time_backward(share, fwd, fwd_flops, steps, warmup, rank):
     """The share's backward in one call (ra_backward_share): delta =
     rowsum(dout * out), then every block's dq kernel on the launch stream and
-    its dk/dv kernels on a side stream.  Its algorithmic flops are five GEMMs
+    its dk/dv kernel on a side stream (the first dq kernel writes dq, dk and
+    dv are written: nothing is zeroed).  Its algorithmic flops are five GEMMs
     over the visible pairs (S, dP, dQ, dK, dV), 2.5 times the forward's; the
     dq kernel recomputes S and dP, which is not counted."""
     g = torch.Generator(device="cuda").manual_seed(2024)
@@ -216,7 +217,7 @@ def time_backward(share, fwd, fwd_flops, steps, warmup, rank):
             "pct_of_bf16_peak": 100.0 * flops / dt / 1e12 / PEAK_BF16_TFLOPS,
             "flops_per_step": flops, "flops_counted": "S, dP, dQ, dK, dV over visible pairs",
             "entry_point": "ra_backward_share (dk/dv on a side stream)",
-            "launches_per_step": 2 + n * (5 if split else 4), "rank": rank}
+            "launches_per_step": 1 + n * (3 if split else 2), "rank": rank}
 
 
 def launch_timing(fwd, pairs_per_step, case, reps):

@@ -240,7 +240,7 @@ void dkv_kernel(const BwdArgs a) {
       ddk = a.ws + (size_t)split * part;
       ddv = a.ws + (size_t)(n_split + split) * part;
     }
-    if (n_split > 1) {
+    if (n_split > 1 || a.overwrite) {
       store_rows<false>(ddk + skey * D, dk, L.h, a.scale);
       store_rows<false>(ddv + skey * D, dv, L.h, 1.f);
     } else {  // added to the caller's (travelling) dk, dv
@@ -252,7 +252,7 @@ void dkv_kernel(const BwdArgs a) {
 
 // dk, dv += sums of the splits' partials, split 0 first.
 __global__ __launch_bounds__(256) void reduce_kernel(const float* ws, float* dk, float* dv,
-                                                     int64_t n4, int n_split) {
+                                                     int64_t n4, int n_split, int overwrite) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n4) return;
   const f32x4* w = (const f32x4*)ws;
@@ -262,8 +262,14 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* ws, float* dk,
     sv += w[(int64_t)(n_split + s) * n4 + i];
   }
   // the block's part is summed first, then added once to the caller's value
-  ((f32x4*)dk)[i] = ((const f32x4*)dk)[i] + sk;
-  ((f32x4*)dv)[i] = ((const f32x4*)dv)[i] + sv;
+  // (or written, overwrite)
+  if (overwrite) {
+    ((f32x4*)dk)[i] = sk;
+    ((f32x4*)dv)[i] = sv;
+  } else {
+    ((f32x4*)dk)[i] = ((const f32x4*)dk)[i] + sk;
+    ((f32x4*)dv)[i] = ((const f32x4*)dv)[i] + sv;
+  }
 }
 
 }  // namespace bwd
@@ -294,7 +300,7 @@ hipError_t launch_backward_dkv(const BwdArgs& a, hipStream_t stream) {
   if (a.n_split > 1) {
     const int64_t n4 = (int64_t)a.h_kv * a.n_k * bwd::D / 4;
     hipLaunchKernelGGL(bwd::reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
-                       stream, a.ws, a.dk, a.dv, n4, a.n_split);
+                       stream, a.ws, a.dk, a.dv, n4, a.n_split, a.overwrite);
   }
   return hipGetLastError();
 }

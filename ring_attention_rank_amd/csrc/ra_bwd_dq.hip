@@ -242,7 +242,14 @@ void dq_kernel(const BwdArgs a) {
     tile(Set1{}, j);
     if (j + 1 < n_iter) tile(Set0{}, j + 1);
   }
-  if (rv) store_rows<true>(a.dq + srow * D, dq, L.h, a.scale);
+  // dq += this block's part, or dq = it (a.dq_write: the first block of a
+  // whole-share backward, which then needs no zeroed dq)
+  if (rv) {
+    if (a.dq_write)
+      store_rows<false>(a.dq + srow * D, dq, L.h, a.scale);
+    else
+      store_rows<true>(a.dq + srow * D, dq, L.h, a.scale);
+  }
 }
 
 // delta = rowsum(dout * out) per query head and row.

@@ -715,9 +715,13 @@ ra_status ra_backward_share(const ra_problem* p, int32_t n_cp, const void* q,
     return hipEventCreateWithFlags(e, hipEventDisableTiming | hipEventDisableSystemFence) ==
            hipSuccess;
   };
-  // dq and delta first (main stream); the dk/dv steps wait for delta
+  // bf16 d 128: dk and dv are written, not accumulated, and the first
+  // block's dq kernel writes dq, so nothing is zeroed first; the other
+  // shapes accumulate onto zeros.
+  a.overwrite = fast ? 1 : 0;
+  // delta first (main stream); the dk/dv steps wait for it
   if (rows > 0) {
-    if (!hip(ra::launch_zero_f32(dq, rows * p->d_k, ms))) goto cleanup;
+    if (!fast && !hip(ra::launch_zero_f32(dq, rows * p->d_k, ms))) goto cleanup;
     if (!hip(fast ? ra::launch_backward_delta(out, dout, delta, rows, ms)
                   : ra::launch_backward_delta_generic(out, dout, delta, rows, p->dtype, p->d_k,
                                                       ms)))
@@ -737,12 +741,14 @@ ra_status ra_backward_share(const ra_problem* p, int32_t n_cp, const void* q,
     a.k_pos = k_pos_blocks[b];
     a.dk = dk_blocks[b];
     a.dv = dv_blocks[b];
-    if (p->n_k > 0) {
+    if (!fast && p->n_k > 0) {
       if (!hip(ra::launch_zero_f32(a.dk, kv_elems, ks)) ||
           !hip(ra::launch_zero_f32(a.dv, kv_elems, ks)))
         goto cleanup;
     }
     if (fast) {
+      // the first block's dq kernel writes dq, the later ones add to it
+      a.dq_write = b == 0 ? 1 : 0;
       if (p->n_q > 0 && !hip(ra::launch_backward_dq(a, ms))) goto cleanup;
       if (!hip(ra::launch_backward_dkv(a, ks))) goto cleanup;
     } else if (p->n_q > 0 || p->n_k > 0) {

@@ -96,12 +96,16 @@ struct BwdArgs {
   float* ws;           // [2][n_split][h_kv][n_k][128] partial sums when n_split > 1
   int32_t n_q, n_k, h_q, h_kv, causal, n_split;
   float scale, c2;
+  int32_t overwrite;   // 1: dk, dv are written, not added to (0: accumulate)
+  int32_t dq_write;    // 1: the per-block dq kernel writes dq instead of adding to it
 };
+
 // Splits of each head group in the dk/dv kernel, and the workspace they need.
 int backward_splits(int n_k, int h_q, int h_kv);
 size_t backward_ws_bytes(int n_k, int h_q, int h_kv);
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_backward_dq(const BwdArgs& a, hipStream_t stream);
+
 hipError_t launch_backward_dkv(const BwdArgs& a, hipStream_t stream);
 // Plain per-row backward for the other supported shapes (fp32; bf16 d_k 64).
 hipError_t launch_backward_generic(const BwdArgs& a, int dtype, int d_k, hipStream_t stream);

@@ -301,7 +301,9 @@ def _share_inputs(sh):
 def test_whole_share_equals_block_steps(which, side):
     """ra_backward_share (every block in one call, dk/dv on a side stream)
     gives bit for bit what the block-by-block ra_backward_step loop gives:
-    same kernels, same order of additions into dq."""
+    same kernels, same order of additions into dq (its first block's kernel
+    writes dq where the loop adds to zeros, and dk, dv are written where the
+    loop adds them to zeros: the same values)."""
     if which == "405b":
         sh = Share(synth.case_by_name("llama405b_stage_share"), 0, T=16384, n_cp=16).to_gpu()
     elif which == "ragged":
