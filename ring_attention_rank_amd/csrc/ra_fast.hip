@@ -210,7 +210,8 @@ struct Step {
   __device__ Step(const StepArgs& a_, Smem<G>& sm_, int tid_)
       : a(a_), sm(sm_), tid(tid_), lane(tid_ & 63),
         gwave(__builtin_amdgcn_readfirstlane((tid_ >> 6) & 3)),
-        grp(__builtin_amdgcn_readfirstlane(G == 1 ? opaque(tid_ >> 8) : tid_ >> 8)), h((tid_ & 63) >> 5), col(tid_ & 31),
+        grp(__builtin_amdgcn_readfirstlane(G == 1 ? opaque(tid_ >> 8) : tid_ >> 8)),
+        h((tid_ & 63) >> 5), col(tid_ & 31),
         n_q(a_.n_q), n_k(a_.n_k), causal(a_.causal != 0), kbase(nullptr), vbase(nullptr) {
     // Tile loads: wave w fills rows 16w .. 16w+15 of a tile, load i rows
     // 16w + 4i + L/16 for lane L, which writes physical chunk L%16 of its
