@@ -376,6 +376,8 @@ def main():
                     help="skip timing the other bf16 workloads of the size table")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only run the matrix-pipe calibration (ra_mfma_ceiling) and print it")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -388,6 +390,11 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 5)
+        return
+    if args.mfma_ceiling:
+        tf, ms = ra.mfma_ceiling()
+        print(json.dumps({"mfma_ceiling_tflops": tf, "ms": ms,
+                          "pct_of_bf16_peak": 100.0 * tf / PEAK_BF16_TFLOPS}), flush=True)
         return
 
     case = synth.case_by_name(args.config)
@@ -421,6 +428,12 @@ def main():
         "event_forward_per_launch_ms": float(np.mean(ring["step_ms"])) / n_launch,
         "event_median_ms_per_step": float(np.median(ring["step_ms"])),
     }
+    # The bf16 MFMA rate the device sustains with the matrix pipe kept busy and
+    # nothing else running: the clock it holds under that load sets it.
+    ceil_tf, ceil_ms = ra.mfma_ceiling() if fast else (None, None)
+    if ceil_tf:
+        roofline["sustained_mfma_tflops"] = ceil_tf
+        roofline["frac_of_sustained"] = t["middle_tflops"] / ceil_tf
     result = {
         "metric": METRIC,
         "value": value,

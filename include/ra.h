@@ -318,6 +318,17 @@ ra_status ra_tile_shape(const ra_problem* p, int32_t* bm, int32_t* bn);
 /* Static description of a status code. */
 const char* ra_status_string(ra_status s);
 
+/* Matrix-pipe calibration (measurement support, not a step of the pages'
+ * method): n_workgroups workgroups of 8 waves (two per SIMD) each issue
+ * 4 * iters v_mfma_f32_32x32x16_bf16 on independent accumulators, with no
+ * memory traffic, and write one float per workgroup to sink (device,
+ * n_workgroups floats, 4-byte aligned).  Each workgroup performs
+ * 8 * 4 * iters * 32768 FLOPs; timing the call on its stream gives the bf16
+ * MFMA rate the device sustains under full matrix-pipe load, the ceiling
+ * against which the attention kernels' rates are also read.  RA_ERR_SHAPE
+ * for n_workgroups or iters below 1. */
+ra_status ra_mfma_ceiling(int32_t n_workgroups, int32_t iters, float* sink, void* stream);
+
 /* ABI version of this header (bumped on any incompatible change). */
 int32_t ra_abi_version(void);
 

@@ -30,7 +30,7 @@ SYMBOLS = (
     "ra_forward_allgather_docs_workspace_bytes", "ra_forward_allgather_docs",
     "ra_backward_prep", "ra_backward_workspace_bytes", "ra_backward_step",
     "ra_backward_share_workspace_bytes", "ra_backward_share", "ra_tile_shape", "ra_status_string", "ra_abi_version",
-    "ra_docs_split_span", "ra_docs_splits",
+    "ra_docs_split_span", "ra_docs_splits", "ra_mfma_ceiling",
 )
 
 
@@ -97,6 +97,8 @@ def lib():
     L.ra_status_string.argtypes = [i32]
     L.ra_status_string.restype = ctypes.c_char_p
     L.ra_abi_version.argtypes = []
+    L.ra_mfma_ceiling.argtypes = [i32, i32, vp, vp]
+    L.ra_mfma_ceiling.restype = i32
     L.ra_docs_split_span.argtypes = []
     L.ra_docs_split_span.restype = i32
     L.ra_docs_splits.argtypes = [P, i32]
@@ -403,6 +405,28 @@ class ForwardGraph:
     def __call__(self):
         self.graph.replay()  # on the current stream, in order with the caller's work
         return self.out, self.lse
+
+
+def mfma_ceiling(iters=65536, workgroups_per_cu=4, reps=3, stream=None):
+    """Sustained bf16 MFMA rate of this device (TFLOP/s, and the ms of the
+    timed call) from ra_mfma_ceiling: four 8-wave workgroups per compute
+    unit, about 50 ms a call, timed with HIP events on the launch stream.
+    The chip lowers its clock over the first milliseconds of such a load, so
+    the last of ``reps`` back-to-back calls is the steady-state figure."""
+    dev = torch.cuda.current_device()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    n = cus * workgroups_per_cu
+    sink = torch.empty(n, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream() if stream is None else stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for rep in range(reps):
+        e0.record(s)
+        _check(lib().ra_mfma_ceiling(n, int(iters), _ptr(sink), _stream(s)), "ra_mfma_ceiling")
+        e1.record(s)
+    s.synchronize()
+    ms = e0.elapsed_time(e1)
+    flops = n * 8 * 4 * iters * 32768
+    return flops / (ms * 1e-3) / 1e12, ms
 
 
 def docs_split_span():

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libra.so")
 SOURCES = [os.path.join(CSRC, n) for n in
            ("ra_kernels.hip", "ra_fast.hip", "ra_bwd_dq.hip", "ra_bwd_dkv.hip",
-            "ra_bwd_generic.hip", "ra_noalloc.hip", "ra_host.cpp")]
+            "ra_bwd_generic.hip", "ra_noalloc.hip", "ra_calib.hip", "ra_host.cpp")]
 # Per-source additions.  The backward dq kernel keeps its MFMA accumulators
 # in VGPRs, where its VALU work reads them directly; the dk/dv kernel needs
 # the AGPRs for its 256 accumulator values per lane and keeps the default.

@@ -148,6 +148,15 @@ def test_forward_noalloc_refuses_oversize():
     assert L.ra_forward_noalloc(*args(good(d_k=96))) == SHAPE
 
 
+def test_mfma_ceiling_checks():
+    L = ra.lib()
+    v = ctypes.c_void_p(FAKE)
+    assert L.ra_mfma_ceiling(0, 10, v, None) == SHAPE
+    assert L.ra_mfma_ceiling(4, 0, v, None) == SHAPE
+    assert L.ra_mfma_ceiling(4, 10, None, None) == NULL
+    assert L.ra_mfma_ceiling(4, 10, ctypes.c_void_p(FAKE + 2), None) == ALIGN
+
+
 def test_debug_position_check(monkeypatch):
     """RA_DEBUG=1 makes the binding refuse positions that do not increase and
     document starts that decrease; without it nothing is checked."""
