@@ -289,3 +289,26 @@ def test_max_heads(h_q, h_kv):
     rng = np.random.default_rng(h_kv)
     sh = _custom_share(rng, "bf16", 128, h_q, h_kv, 160, 96, 2)
     check_share(sh, f"max heads {h_q}/{h_kv}")
+
+
+def test_mfma_ceiling_runs_and_reports_a_rate():
+    """The matrix-pipe calibration runs on every compute unit and its rate is
+    a plausible fraction of the nominal peak (the clock the chip holds under
+    full matrix load is below 2.4 GHz, never above)."""
+    tf, ms = ra.mfma_ceiling(iters=2048, reps=2)
+    assert ms > 0 and 0.3 * 2516.6 < tf < 1.02 * 2516.6
+
+
+def test_debug_check_on_device_positions(monkeypatch):
+    """RA_DEBUG=1: the binding refuses positions that do not increase before
+    any launch; valid positions pass through to the same results."""
+    rng = np.random.default_rng(31)
+    sh = _custom_share(rng, "bf16", 128, 2, 1, 130, 70, 2)
+    monkeypatch.setenv("RA_DEBUG", "1")
+    out, lse, _, _ = ra.forward(sh.gq, sh.gq_pos, sh.gk, sh.gv, sh.gk_pos)
+    ro, rl = sh.oracle()
+    compare(out.cpu(), lse.cpu(), ro, rl, TOL["bf16"], "debug-checked forward")
+    bad = sh.gq_pos.clone()
+    bad[5] = bad[4]
+    with pytest.raises(ValueError):
+        ra.forward(sh.gq, bad, sh.gk, sh.gv, sh.gk_pos)
