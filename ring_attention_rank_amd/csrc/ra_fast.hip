@@ -43,6 +43,8 @@
 //    start; without it that code compiles away.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -877,7 +879,7 @@ __global__ __launch_bounds__(256 * G) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void step_kernel_fast(const StepArgs a) {
   __shared__ Smem<G> sm;
   const int tid = threadIdx.x;
-  const int u = blockIdx.x;
+  const int u = blockIdx.x + a.unit0;
   const int head = a.head_of[u % a.h_q];
   const int p = u / a.h_q;
   const int t_hi = a.n_qt - 1 - p, t_lo = p;
@@ -1009,17 +1011,23 @@ hipError_t launch_allgather_split_fast(const MultiArgs& ma, int n_split, hipStre
 // compute unit, so that two one-group workgroups share each compute unit;
 // otherwise the two-group ping-pong keeps both waves of a SIMD busy.
 static int groups_for(long long units) {
-  static int cus = 0;
+  // compute units of the current device, looked up once per device
+  static std::atomic<int> cus_of[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int cus = cus_of[dev].load(std::memory_order_relaxed);
   if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
+    int n = 0;
+    cus = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                  n > 0
+              ? n
+              : 256;
+    cus_of[dev].store(cus, std::memory_order_relaxed);
   }
   return units >= 2LL * cus ? 1 : 2;
 }
+
+int fast_groups_for(long long units) { return groups_for(units); }
 
 hipError_t launch_allgather_fast(const MultiArgs& ma, hipStream_t stream) {
   const int g = ma.s.q_lo != nullptr ? 2 : groups_for((long long)ma.s.n_pairs * ma.s.h_q);
@@ -1036,7 +1044,7 @@ hipError_t launch_allgather_fast(const MultiArgs& ma, hipStream_t stream) {
 template <int G>
 static void launch_step_g(const StepArgs& a, bool read, bool final_, hipStream_t stream,
                           hipEvent_t start, hipEvent_t stop) {
-  dim3 grid((unsigned)(a.n_pairs * a.h_q)), block(256 * G);
+  dim3 grid((unsigned)(a.n_units ? a.n_units : a.n_pairs * a.h_q)), block(256 * G);
   auto go = [&](auto kernel) {
     if (start || stop)
       hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0, a);
@@ -1055,7 +1063,7 @@ static void launch_step_g(const StepArgs& a, bool read, bool final_, hipStream_t
 
 hipError_t launch_step_fast(const StepArgs& a, bool read, bool final_, hipStream_t stream,
                             hipEvent_t start, hipEvent_t stop) {
-  if (groups_for((long long)a.n_pairs * a.h_q) == 1)
+  if ((a.groups ? a.groups : groups_for((long long)a.n_pairs * a.h_q)) == 1)
     launch_step_g<1>(a, read, final_, stream, start, stop);
   else
     launch_step_g<2>(a, read, final_, stream, start, stop);

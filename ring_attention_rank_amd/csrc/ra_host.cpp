@@ -92,6 +92,23 @@ void head_order(const ra_problem* p, uint8_t* head_of) {
 // bf16 with d_k = 128 runs the 8-wave fast kernels.
 bool fast_path(const ra_problem* p) { return p->dtype == RA_BF16 && p->d_k == 128; }
 
+// Whether ra_forward splits each ring step into two half launches, one on
+// each stream.  The two chains of half launches drift apart, so each half's
+// start-up, state traffic and launch gap overlap the other half's compute
+// (the all-gather form has none of these costs).  The side stream stages the
+// next block before its half, which then waits for that copy; so the split
+// pays only where the copy is short against a step: its estimated time (K
+// and V read and written, 8 TB/s) at most 5 % of the step's causal compute
+// (half the pairs visible, 2.5 PFLOP/s).  That holds for the GQA shares
+// (1-4 %) and not for the striped MHA share (15 %), where the split measured
+// 5 % slower; where it holds, 2-7 % faster.
+bool split_ring(const ra_problem* p, const ra::StepArgs& a) {
+  if (!fast_path(p) || (int64_t)a.n_pairs * a.h_q < 2) return false;
+  const double copy_s = 8.0 * p->h_kv * (double)p->n_k * p->d_k / 8e12;
+  const double step_s = 2.0 * p->d_k * p->h_q * (double)p->n_q * p->n_k / 2.5e15;
+  return copy_s <= 0.05 * step_s;
+}
+
 // State (m, l, o) of the per-block fallback of ra_forward_allgather.
 size_t allgather_ws_bytes(const ra_problem* p) {
   if (fast_path(p)) return 0;
@@ -463,12 +480,19 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
   a.lse = lse;
   a.work = reinterpret_cast<unsigned long long*>(work);
 
-  // Events: slot s staged (side -> main), slot s consumed (main -> side), and
-  // the caller's prior work on main (main -> side) before the first copy.
+  // Events: slot s staged (side -> main), slot s consumed (main -> side), the
+  // caller's prior work on main (main -> side) before the first copy, and
+  // the side stream's last half launch (side -> main) in the split schedule.
   hipEvent_t ev_staged[2] = {nullptr, nullptr}, ev_used[2] = {nullptr, nullptr},
-             ev_start = nullptr;
+             ev_start = nullptr, ev_join = nullptr;
   ra_status result = RA_OK;
   int64_t staged = 0;
+  // Split schedule: each step's launch is two halves of the work units, one
+  // on each stream (see split_ring); caller-made events or timing marks keep
+  // the one-launch schedule.
+  const bool split = use_side && n_cp > 1 && fixed == nullptr && launch_events == nullptr &&
+                     staged_events == nullptr && split_ring(p, a);
+  const int split_groups = split ? ra::fast_groups_for((int64_t)a.n_pairs * a.h_q) : 0;
   // The events only order work between two streams of this device; the copy
   // kernels' completion and the step kernels' launch carry their own memory
   // fences, so the events skip the system-scope fence (a cache writeback and
@@ -476,6 +500,23 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
   auto mk = [](hipEvent_t* e) {
     return hipEventCreateWithFlags(e, hipEventDisableTiming | hipEventDisableSystemFence) ==
            hipSuccess;
+  };
+  // Copies block b (b >= 1) into slot b & 1 on stream cs, after the step that
+  // last read that slot (b - 2) is done, and marks it staged.
+  auto stage = [&](int b, hipStream_t cs) {
+    const int s = b & 1;
+    char* slot = ws + w.slot[s];
+    if (use_side && b >= 3 && hipStreamWaitEvent(ss, ev_used[s], 0) != hipSuccess) return false;
+    if (w.kbytes &&
+        (hipMemcpyAsync(slot, k_blocks[b], w.kbytes, hipMemcpyDeviceToDevice, cs) != hipSuccess ||
+         hipMemcpyAsync(slot + align_up(w.kbytes), v_blocks[b], w.kbytes, hipMemcpyDeviceToDevice,
+                        cs) != hipSuccess ||
+         hipMemcpyAsync(slot + 2 * align_up(w.kbytes), k_pos_blocks[b], w.pbytes,
+                        hipMemcpyDeviceToDevice, cs) != hipSuccess))
+      return false;
+    staged += 2 * (int64_t)w.kbytes;
+    if (!mark(staged_events, b, cs)) return false;
+    return !use_side || hipEventRecord(ev_staged[s], ss) == hipSuccess;
   };
   if (use_side && n_cp > 1) {
     if (fixed) {
@@ -485,7 +526,7 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
       ev_used[0] = fixed[3];
       ev_used[1] = fixed[4];
     } else if (!mk(&ev_start) || !mk(&ev_staged[0]) || !mk(&ev_staged[1]) || !mk(&ev_used[0]) ||
-               !mk(&ev_used[1])) {
+               !mk(&ev_used[1]) || (split && !mk(&ev_join))) {
       result = RA_ERR_HIP;
       goto cleanup;
     }
@@ -503,51 +544,55 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
       a.v = v_blocks[0];
       a.k_pos = k_pos_blocks[0];
     } else {
-      const int s = b & 1;
-      char* slot = ws + w.slot[s];
-      void* dk = slot;
-      void* dv = slot + align_up(w.kbytes);
-      void* dp = slot + 2 * align_up(w.kbytes);
-      hipStream_t cs = use_side ? ss : ms;
-      if (use_side && b >= 3) {
-        // slot s was last read by step b-2
-        if (hipStreamWaitEvent(ss, ev_used[s], 0) != hipSuccess) { result = RA_ERR_HIP; goto cleanup; }
+      // the split schedule staged block b during step b - 1
+      if (!split && !stage(b, use_side ? ss : ms)) { result = RA_ERR_HIP; goto cleanup; }
+      if (use_side && hipStreamWaitEvent(ms, ev_staged[b & 1], 0) != hipSuccess) {
+        result = RA_ERR_HIP;
+        goto cleanup;
       }
-      if (w.kbytes) {
-        if (hipMemcpyAsync(dk, k_blocks[b], w.kbytes, hipMemcpyDeviceToDevice, cs) != hipSuccess ||
-            hipMemcpyAsync(dv, v_blocks[b], w.kbytes, hipMemcpyDeviceToDevice, cs) != hipSuccess ||
-            hipMemcpyAsync(dp, k_pos_blocks[b], w.pbytes, hipMemcpyDeviceToDevice, cs) != hipSuccess) {
-          result = RA_ERR_HIP;
-          goto cleanup;
-        }
-      }
-      staged += 2 * (int64_t)w.kbytes;
-      if (!mark(staged_events, b, cs)) { result = RA_ERR_HIP; goto cleanup; }
-      if (use_side) {
-        if (hipEventRecord(ev_staged[s], ss) != hipSuccess ||
-            hipStreamWaitEvent(ms, ev_staged[s], 0) != hipSuccess) {
-          result = RA_ERR_HIP;
-          goto cleanup;
-        }
-      }
-      a.k = dk;
-      a.v = dv;
-      a.k_pos = (const int32_t*)dp;
+      char* slot = ws + w.slot[b & 1];
+      a.k = slot;
+      a.v = slot + align_up(w.kbytes);
+      a.k_pos = (const int32_t*)(slot + 2 * align_up(w.kbytes));
     }
-    // with timing, the kernel's own start and end times go to the events
-    result = launch(p, a, /*read=*/!first, /*final=*/last, ms,
-                    launch_events ? (hipEvent_t)launch_events[2 * b] : nullptr,
-                    launch_events ? (hipEvent_t)launch_events[2 * b + 1] : nullptr);
-    if (result != RA_OK) goto cleanup;
+    if (split) {
+      // first half on the main stream; the side stream stages block b + 1
+      // and then runs the second half
+      const int total = a.n_pairs * a.h_q, half = total / 2;
+      ra::StepArgs ha = a, hb = a;
+      ha.unit0 = 0;
+      ha.n_units = half;
+      hb.unit0 = half;
+      hb.n_units = total - half;
+      ha.groups = hb.groups = split_groups;
+      result = launch(p, ha, /*read=*/!first, /*final=*/last, ms);
+      if (result != RA_OK) goto cleanup;
+      if (b + 1 < n_cp && !stage(b + 1, ss)) { result = RA_ERR_HIP; goto cleanup; }
+      result = launch(p, hb, /*read=*/!first, /*final=*/last, ss);
+      if (result != RA_OK) goto cleanup;
+    } else {
+      // with timing, the kernel's own start and end times go to the events
+      result = launch(p, a, /*read=*/!first, /*final=*/last, ms,
+                      launch_events ? (hipEvent_t)launch_events[2 * b] : nullptr,
+                      launch_events ? (hipEvent_t)launch_events[2 * b + 1] : nullptr);
+      if (result != RA_OK) goto cleanup;
+    }
     if (use_side && !first && b + 2 < n_cp) {
+      // slot b & 1 is free for block b + 2 once this step's main-stream part
+      // is done (its side-stream part precedes that copy on the side stream)
       if (hipEventRecord(ev_used[b & 1], ms) != hipSuccess) { result = RA_ERR_HIP; goto cleanup; }
     }
+  }
+  if (split && (hipEventRecord(ev_join, ss) != hipSuccess ||
+                hipStreamWaitEvent(ms, ev_join, 0) != hipSuccess)) {
+    result = RA_ERR_HIP;
+    goto cleanup;
   }
   if (staged_bytes) *staged_bytes = staged;
 
 cleanup:
   if (!fixed)
-    for (hipEvent_t e : {ev_start, ev_staged[0], ev_staged[1], ev_used[0], ev_used[1]})
+    for (hipEvent_t e : {ev_start, ev_staged[0], ev_staged[1], ev_used[0], ev_used[1], ev_join})
       if (e) (void)hipEventDestroy(e);  // the call's status is already decided
   return result;
 }

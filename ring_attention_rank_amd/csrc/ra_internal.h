@@ -59,6 +59,10 @@ struct StepArgs {
   int32_t n_pairs;           // workgroups per head: tile t is paired with tile n_qt-1-t
   float c2;                  // scale * log2(e): scores go to base-2 units
   uint8_t head_of[kMaxHeads];  // launch-order slot -> query head (L2 locality)
+  // bf16 d_k 128 step kernels: this launch covers work units (query tile
+  // pair x head) [unit0, unit0 + n_units), n_units 0 meaning all of them,
+  // with `groups` groups of 4 waves per workgroup (0: chosen for the launch).
+  int32_t unit0, n_units, groups;
 };
 
 // All key/value blocks resident (the all-gather form): one launch folds them
@@ -78,6 +82,9 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d_k, bool read, bool fi
 // bfloat16, d_k = 128: the 8-wave kernel with direct-to-LDS staging.
 hipError_t launch_step_fast(const StepArgs& a, bool read, bool final_, hipStream_t stream,
                             hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+// Groups of 4 waves per workgroup the bf16 d_k 128 kernels use for a launch
+// of `units` work units on the current device (1 or 2).
+int fast_groups_for(long long units);
 // Backward of one key/value block (bfloat16, d_k = 128): dq, dk and dv
 // (fp32) each get this block's part added (dk, dv summed over the query heads
 // of each key/value head).

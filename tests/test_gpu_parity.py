@@ -312,3 +312,27 @@ def test_debug_check_on_device_positions(monkeypatch):
     bad[5] = bad[4]
     with pytest.raises(ValueError):
         ra.forward(sh.gq, bad, sh.gk, sh.gv, sh.gk_pos)
+
+
+@pytest.mark.parametrize("name", ["llama405b_stage_share", "llama70b_stage_share"])
+def test_split_schedule_matches_one_launch(name):
+    """At full size these shares run each ring step as two half launches, one
+    on each stream.  Every work unit computes exactly what it computes in the
+    one-launch schedule (one stream; the timed call, which never splits), so
+    the results and tile counts are the same bit for bit, and so is a
+    HIP-graph replay of the split schedule."""
+    sh = Share(synth.case_by_name(name), 0).to_gpu()
+    print(f"[parity] split schedule {name}", flush=True)
+    a = run_forward(sh)              # side stream: split halves
+    b = run_forward(sh, side=False)  # one stream: one launch per step
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert np.array_equal(a[2], b[2]) and a[3] == b[3]
+    f = ra.Forward(sh.gq, sh.gq_pos, sh.gk, sh.gv, sh.gk_pos)
+    f.timed()
+    torch.cuda.synchronize()
+    assert np.array_equal(f.out.cpu().numpy(), a[0]) and np.array_equal(f.lse.cpu().numpy(), a[1])
+    g = ra.ForwardGraph(sh.gq, sh.gq_pos, sh.gk, sh.gv, sh.gk_pos)
+    for _ in range(2):
+        out, lse = g()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), a[0]) and np.array_equal(lse.cpu().numpy(), a[1])
