@@ -179,6 +179,73 @@ __device__ __forceinline__ void read_half(const E* arr, int kb, int h, T4 (&x)[4
   x[3] = *(const T4*)(b + 20);
 }
 
+// ---- one-copy tiles (LDS DMA) ------------------------------------------
+// A tile staged once and read both ways: 16-byte chunk c of row r sits at
+// physical chunk c ^ uswz(r).  uswz is a bijection on r & 15 (row reads of 16
+// rows with the same chunk hit 16 distinct chunks) whose bits 2-3 take all
+// four values over any four rows 4k .. 4k + 3 (the 4 rows x 4 chunks a
+// half-wave of transposing reads touches hit 16 distinct chunks): both read
+// patterns are free of bank conflicts.
+__device__ __forceinline__ int uswz(int r) { return 4 * (r & 3) | ((r >> 2) & 3); }
+
+// Per-lane read bases into a one-copy tile: the same logical bytes as
+// Lanes::rd_row and Lanes::rd_tr (and rd_tr + 4 rows) on the two-copy
+// layouts, so the operands are identical.
+struct Lanes1 {
+  int rd_row, rd_lo, rd_hi, h, col;
+  __device__ Lanes1(int lane) {
+    h = lane >> 5;
+    col = lane & 31;
+    const int r = sigma(col), g = uswz(r);
+    rd_row = r * 256 + 16 * (h ^ (g & 1)) + 32 * (g >> 1);  // ^ (32 ks)
+    const int g4 = lane >> 4, i = lane & 15;
+    const int hh = g4 >> 1, dgrp = g4 & 1, rho = i >> 2, b = (i & 3) >> 1, half = i & 1;
+    const int c = 2 * dgrp + b;
+    rd_lo = (8 * hh + rho) * 256 + 64 * rho + 16 * (c ^ (2 * hh)) + 8 * half;          // ^ (64 db)
+    rd_hi = (8 * hh + rho + 4) * 256 + 64 * rho + 16 * (c ^ (2 * hh + 1)) + 8 * half;  // ^ (64 db)
+  }
+};
+
+__device__ __forceinline__ bf16x8 row_operand1(const uint8_t* tile, const Lanes1& L, int kb,
+                                               int ks) {
+  return *(const bf16x8*)(tile + kb * 32 * 256 + (L.rd_row ^ (32 * ks)));
+}
+__device__ __forceinline__ bf16x8 tr_operand1(const uint8_t* tile, const Lanes1& L, int kb, int t,
+                                              int db) {
+  const uint8_t* base = tile + kb * 32 * 256 + t * 16 * 256;
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + (L.rd_lo ^ (64 * db))));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + (L.rd_hi ^ (64 * db))));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Buffer resource as four wave-uniform words, for the inline LDS DMA below
+// (reads at or past `bytes` return zeros).
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
+               __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32) & 0xffff),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
+// Eight rows (2 KiB) from HBM straight into LDS: load i of lane L reads
+// global byte soff + 1024 i + v_i and lands at LDS byte lds + 1024 i + 16 L.
+// Inline asm, so the compiler does not track these loads (it would wait for
+// them before the next LDS read of the other stage); the caller waits with
+// vmcnt before the barrier that publishes the stage.  M0 carries the LDS
+// address, and the nop is the wait state between writing M0 and its use.
+__device__ __forceinline__ void dma_rows8(const i32x4& rs, uint32_t lds, int v0, int v1,
+                                          int soff) {
+  const int m0v = __builtin_amdgcn_readfirstlane((int)lds);
+  const int so = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile(
+      "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %3, %4 offen lds\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen offset:1024 lds"
+      :
+      : "s"(m0v), "v"(v0), "v"(v1), "s"(rs), "s"(so)
+      : "m0");
+}
+
 // Scheduling fence: the tile loops below are written in the order they
 // should issue (each MFMA with the LDS reads four MFMAs ahead and a slice of
 // the other half's VALU work) and the compiler keeps that order.
