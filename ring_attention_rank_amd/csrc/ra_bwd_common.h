@@ -246,6 +246,17 @@ __device__ __forceinline__ void dma_rows8(const i32x4& rs, uint32_t lds, int v0,
       : "m0");
 }
 
+// One 4-byte word per lane (256 bytes) from HBM straight into LDS: lane L's
+// word lands at lds + 4 L (same conventions as dma_rows8).
+__device__ __forceinline__ void dma_words64(const i32x4& rs, uint32_t lds, int voff, int soff) {
+  const int m0v = __builtin_amdgcn_readfirstlane((int)lds);
+  const int so = __builtin_amdgcn_readfirstlane(soff);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(rs), "s"(so)
+               : "m0");
+}
+
 // Scheduling fence: the tile loops below are written in the order they
 // should issue (each MFMA with the LDS reads four MFMAs ahead and a slice of
 // the other half's VALU work) and the compiler keeps that order.

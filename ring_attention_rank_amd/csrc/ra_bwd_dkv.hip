@@ -361,11 +361,13 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* ws, float* dk,
 }  // namespace bwd
 
 int backward_splits(int n_k, int h_q, int h_kv) {
-  // Split the head group until the dk/dv grid has about 1024 workgroups (4
-  // per compute unit), over divisors of the group size.
+  // Split the head group until the dk/dv grid has about 512 workgroups (two
+  // rounds of one workgroup per compute unit), over divisors of the group
+  // size.  More splits fill the rounds no better and add partial sums for
+  // the reduction to read.
   const int grp = h_q / h_kv, tiles = (n_k + bwd::ROWS - 1) / bwd::ROWS * h_kv;
   int g = 1;
-  while (g < grp && (int64_t)tiles * g < 1024) {
+  while (g < grp && (int64_t)tiles * g < 512) {
     int nx = g + 1;
     while (grp % nx) ++nx;
     g = nx;

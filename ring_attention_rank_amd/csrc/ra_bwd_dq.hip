@@ -25,230 +25,251 @@
 //    dS = P (dP - delta), dV^T += dout^T P and dK^T += Q^T dS (dout and Q
 //    read transposed).
 //
-// One wave per SIMD (up to 512 registers).  Each 64-row tile is loaded into
-// registers one tile ahead, then written to LDS in two XOR swizzles per
-// tensor (one for row reads, one for the transposing ds_read_b64_tr_b16
-// reads), both free of bank conflicts.  Inside a tile the instructions are
-// fenced in issue order: every MFMA goes out with the LDS operand reads four
-// MFMAs ahead and a slice of the other half-tile's VALU work.
+// Both kernels run two waves per SIMD, each under 256 registers, as pairs
+// of waves that own the same rows (here 32 queries, in ra_bwd_dkv.hip 32
+// keys) and split the work between them.  Tiles go from HBM straight into
+// LDS by buffer-load DMA, one copy each, in a swizzle that serves both the
+// row reads and the transposing ds_read_b64_tr_b16 reads without bank
+// conflicts.  Inside a phase the instructions are fenced in issue order,
+// with the LDS operand reads a few MFMAs ahead of their use.
 //
-// This unit: the dq kernel and delta = rowsum(dout * out).  Its MFMA
-// accumulators live in ordinary VGPRs (built with the VGPR form), so the
-// softmax-gradient VALU work reads them without moves.
+// This unit: the dq kernel and delta = rowsum(dout * out).  A workgroup of
+// 8 waves owns 128 query rows; on each SIMD
+//  * the P wave (q in registers): S^T_j = K_j q^T, p = exp(scale s - lse)
+//    under the mask, written to LDS in fp32;
+//  * the dS wave (dout and the dQ accumulator in registers): with the p of
+//    tile j - 1 from LDS, dS^T = p (dP^T - delta) and dQ^T += K_{j-1}^T dS^T,
+//    then dP^T_j = V_j dout^T for the next step.
+// One barrier per step; K has three stages (j - 1, j, and j + 1 landing),
+// V two, p two.  The MFMA accumulators live in ordinary VGPRs (built with
+// the VGPR form), so the VALU work reads them without moves.
 #include "ra_bwd_common.h"
 
 namespace ra {
 namespace bwd {
 
-// 1024-byte aligned: the second buffer keeps the 16-byte chunk alignment and
-// the bank mapping of the swizzles.
-struct __attribute__((aligned(1024))) TileQ {
-  uint8_t k_row[TILE_BYTES];
-  uint8_t k_tr[TILE_BYTES];
-  uint8_t v_row[TILE_BYTES];
-  int32_t pos[TILE];
-};
-// Two tile buffers: tile j is read from t[j & 1] while tile j + 1 is written
-// into the other one, slice by slice between the MFMAs.
-struct SmemQ {
-  TileQ t[2];
+constexpr int Q_THREADS = 512;
+
+struct __attribute__((aligned(1024))) SmemQ {
+  uint8_t k[3][TILE_BYTES];  // K tiles, one copy each (uswz layout): rows for S^T, transposed for dQ^T
+  uint8_t v[2][TILE_BYTES];  // V tiles: rows for dP^T
+  // p of a tile, per wave pair, half, register group and lane: the P wave's
+  // S^T accumulator layout, which is the dS wave's dP^T layout too
+  f32x4 p[2][4][2][4][64];
+  int32_t pos[3][TILE];  // key positions as stored (keys past the block read as 0)
 };
 
 // LDS operand reads run this many MFMAs ahead of their use.
-constexpr int AHEAD = 4;
+constexpr int Q_AHEAD = 3;
 
 // dq kernel: one workgroup = 128 query rows of one head; a one-dimensional
 // grid of n_qt128 * h_q workgroups.
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(Q_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dq_kernel(const BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) SmemQ sm;
+  __shared__ SmemQ sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const Lanes L(lane);
+  const bool pw = wave < 4;  // P wave (else dS wave)
+  const int pair = wave & 3;
+  const Lanes1 L(lane);
   int bx, head;  // heads that share a key/value head on one XCD
   xcd_split(blockIdx.x, a.h_q, bx, head);
   const int kvh = head / (a.h_q / a.h_kv);
   const int n_q = a.n_q, n_k = a.n_k;
-  const int row0_wg = bx * ROWS, row0 = row0_wg + wave * 32;
+  const bool causal = a.causal != 0;
+  const int row0_wg = bx * ROWS, row0 = row0_wg + pair * 32;
   const int row = row0 + L.col;
   const bool rv = row < n_q;
   const size_t srow = (size_t)head * n_q + row;
 
-  // queries and their output gradients in registers (B operands)
-  const uint16_t* qb = (const uint16_t*)a.q + ((size_t)head * n_q) * D;
-  const uint16_t* gb = (const uint16_t*)a.dout + ((size_t)head * n_q) * D;
-  bf16x8 q[8], dout[8];
+  // q (P wave) or dout (dS wave) in registers: the B operand of S^T or dP^T
+  const uint16_t* src = (const uint16_t*)(pw ? a.q : a.dout) + ((size_t)head * n_q) * D;
+  bf16x8 qg[8];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    q[ks] = rv ? *(const bf16x8*)(qb + (size_t)row * D + ks * 16 + L.h * 8) : bf16x8{};
-    dout[ks] = rv ? *(const bf16x8*)(gb + (size_t)row * D + ks * 16 + L.h * 8) : bf16x8{};
-  }
-  // q and dout land before any tile load is issued, so the waits inside the
-  // tile loop only ever concern the prefetch of the next tile
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  for (int ks = 0; ks < 8; ++ks)
+    qg[ks] = rv ? *(const bf16x8*)(src + (size_t)row * D + ks * 16 + L.h * 8) : bf16x8{};
   // rows past n_q and rows that saw no key at all have lse = -inf: p = 0
   const float lse2 = rv ? a.lse[srow] * kLog2e : -INFINITY;
   const bool seen = lse2 != -INFINITY;
   const float delta = rv ? a.delta[srow] : 0.f;
-  const int qp = rv ? (a.causal ? a.q_pos[row] : 0x7ffffffe) : (int)0x80000000;
+  const int qp = rv ? (causal ? a.q_pos[row] : 0x7ffffffe) : (int)0x80000000;
   const int n_kt = (n_k + TILE - 1) / TILE;
   // key tiles whose first key is visible to the workgroup's last query (a
   // prefix: positions increase)
   int n_iter = n_kt;
-  if (a.causal) {
+  if (causal) {
     const int qmax = a.q_pos[min(row0_wg + ROWS, n_q) - 1];
     int cnt = 0;
     for (int j = lane; j < n_kt; j += 64) cnt += a.k_pos[j * TILE] <= qmax ? 1 : 0;
     for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
     n_iter = __builtin_amdgcn_readfirstlane(cnt);
   }
-  const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)kvh * n_k) * D;
-  const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)kvh * n_k) * D;
-
-  // Two register sets: the set that holds tile j + 1 is written to LDS
-  // during tile j and then receives tile j + 3, so every tile's loads have
-  // about two tiles of compute to land.  Set indices are compile-time
-  // (std::integral_constant), the loop steps two tiles at a time.
-  u32x4 pk[2][4], pv[2][4];
-  int ppos[2] = {0, 0};
-  using Set0 = std::integral_constant<int, 0>;
-  using Set1 = std::integral_constant<int, 1>;
-  const auto rk = rsrc(kbase, (uint32_t)n_k * 256u), rv_ = rsrc(vbase, (uint32_t)n_k * 256u);
-  const auto rp = rsrc(a.k_pos, (uint32_t)n_k * 4u);
-  auto fetch_tile = [&](auto set, int j) {
-    constexpr int s = decltype(set)::value;
-    fetch_rows(rk, j * TILE, pk[s], tid);  // keys past the block read as zeros
-    fetch_rows(rv_, j * TILE, pv[s], tid);
-    // raw position; the range and causal selects wait until it is written
-    ppos[s] = __builtin_amdgcn_raw_buffer_load_b32(
-        rp, (uint32_t)(j * TILE + (tid & (TILE - 1))) * 4u, 0, 0);
-  };
-  // slice w (0..12) of register set s into buffer b: K chunks (row and
-  // transposing copies), then V chunks, then the key positions of tile j
-  auto put_slice = [&](auto set, TileQ& b, int w, int j) {
-    constexpr int s = decltype(set)::value;
-    if (w < 8) {
-      put_one(pk[s][w >> 1], (w & 1) ? nullptr : b.k_row, (w & 1) ? b.k_tr : nullptr, tid,
-              w >> 1);
-    } else if (w < 12) {
-      put_one(pv[s][w - 8], b.v_row, nullptr, tid, w - 8);
-    } else if (tid < TILE) {
-      const int gk = j * TILE + tid;
-      b.pos[tid] = gk < n_k ? (a.causal ? ppos[s] : (int)0x80000000) : 0x7fffffff;
-    }
-  };
-  f32x16 dq[4] = {};
+  // registers and row values land before any tile load is issued, so the
+  // waits inside the loop only ever concern the next tile's DMA
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   const bool wave_ok = __builtin_amdgcn_ballot_w64(!(rv && seen)) == 0;
   const int qmin = __builtin_amdgcn_readfirstlane(qp);  // lane 0 holds the wave's first row
-  if (n_iter > 0) {
-    fetch_tile(Set0{}, 0);
+
+  // DMA of a tile: wave w moves rows 8 w .. 8 w + 7 of K and of V, load i
+  // rows 8 w + 4 i + L / 16; lane L fills physical chunk L % 16 of its row
+  // with logical chunk (L % 16) ^ uswz(row).  Wave 0 also moves the 64 key
+  // positions.
+  int dma_v[2];
 #pragma unroll
-    for (int w = 0; w < 13; ++w) put_slice(Set0{}, sm.t[0], w, 0);
-    fetch_tile(Set1{}, 1);
-    fetch_tile(Set0{}, 2);
+  for (int i = 0; i < 2; ++i)
+    dma_v[i] = (lane >> 4) * 256 + 16 * ((lane & 15) ^ (4 * (lane >> 4) | ((2 * wave + i) & 3)));
+  const i32x4 rk = rsrc_words((const uint16_t*)a.k + ((size_t)kvh * n_k) * D, (uint32_t)n_k * 256u);
+  const i32x4 rvv = rsrc_words((const uint16_t*)a.v + ((size_t)kvh * n_k) * D, (uint32_t)n_k * 256u);
+  const i32x4 rp = rsrc_words(a.k_pos, (uint32_t)n_k * 4u);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)&sm;
+  auto dma_tile = [&](int j) {
+    const uint32_t w = 8 * wave * 256;
+    const int soff = (j * TILE + 8 * wave) * 256;
+    dma_rows8(rk, lds0 + (uint32_t)offsetof(SmemQ, k) + (j % 3) * TILE_BYTES + w, dma_v[0],
+              dma_v[1], soff);
+    dma_rows8(rvv, lds0 + (uint32_t)offsetof(SmemQ, v) + (j & 1) * TILE_BYTES + w, dma_v[0],
+              dma_v[1], soff);
+    if (wave == 0)
+      dma_words64(rp, lds0 + (uint32_t)offsetof(SmemQ, pos) + (j % 3) * TILE * 4, lane * 4,
+                  j * TILE * 4);
+  };
+  // The P wave's mask decision for a tile: whole tile inside the block and
+  // its last key visible to the wave's first row (positions increase), from
+  // a scalar load one step ahead.
+  auto tile_full = [&](int j) {
+    const int last = j * TILE + TILE - 1;
+    if (!wave_ok || last >= n_k) return false;
+    return !causal || a.k_pos[last] <= qmin;
+  };
+
+  f32x16 acc[4] = {};  // dQ^T (dS wave)
+  f32x16 sp[2];        // S^T (P wave) or dP^T (dS wave) of a tile's two 32-key halves
+  bf16x8 op[16], tr[16];
+  if (n_iter > 0) {
+    dma_tile(0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   }
   __syncthreads();
 
-  // tile j; `set` holds tile j + 1
-  auto tile = [&](auto set, int j) {
-    TileQ& cur = sm.t[j & 1];
-    TileQ& nxt = sm.t[(j + 1) & 1];  // last read by tile j - 1, before the barrier
-    // no mask when every row of the wave is valid, saw some key, and sees the
-    // whole tile (positions increase, so the tile's last key decides)
-    const bool full = wave_ok && __builtin_amdgcn_readfirstlane(cur.pos[TILE - 1]) <= qmin;
-    auto body = [&](auto masked) {
-      // A[kb][2 ks] = K rows, A[kb][2 ks + 1] = V rows of half kb; T[kb][4 t + db]
-      // = transposed K for dQ^T += K^T dS^T.
-      bf16x8 A[2][16], T[2][8];
-      i32x4 pz[2][4];
-      f32x16 S[2] = {}, P[2] = {};
-      float X[2][16];
-      bf16x8 ds[2][2];
-      auto rdA = [&](int kb, int i) {
-        A[kb][i] = row_operand((i & 1) ? cur.v_row : cur.k_row, L, kb, i >> 1);
-      };
-      auto rdT = [&](int kb, int i) { T[kb][i] = tr_operand(cur.k_tr, L, kb, i >> 2, i & 3); };
-      auto mA = [&](int kb, int i) {
-        if (i & 1)
-          P[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[kb][i], dout[i >> 1], P[kb], 0, 0, 0);
-        else
-          S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[kb][i], q[i >> 1], S[kb], 0, 0, 0);
-      };
-      auto mT = [&](int kb, int i) {
-        dq[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(T[kb][i], ds[kb][i >> 2], dq[i & 3], 0,
-                                                            0, 0);
-      };
-      auto valu = [&](int kb, int r) {
-        float p;
-        if constexpr (decltype(masked)::value) {
-          const bool vis = pz[kb][r >> 2][r & 3] <= qp && seen;
-          p = vis ? exp2f_(__builtin_fmaf(S[kb][r], a.c2, -lse2)) : 0.f;
-        } else {
-          p = exp2f_(__builtin_fmaf(S[kb][r], a.c2, -lse2));
-        }
-        X[kb][r] = p * (P[kb][r] - delta);
-      };
-      auto pack_ds = [&](int kb) {
-  #pragma unroll
-        for (int t = 0; t < 2; ++t)
-  #pragma unroll
-          for (int e = 0; e < 8; ++e) ds[kb][t][e] = (__bf16)X[kb][8 * t + e];
-      };
-  #pragma unroll
-      for (int i = 0; i < AHEAD; ++i) rdA(0, i);
-      read_half(cur.pos, 0, L.h, pz[0]);
-      read_half(cur.pos, 1, L.h, pz[1]);
+  // 16 MFMAs sp[kb] += (rows of X, half kb) x qg; hook(n) after MFMA n
+  auto rows_mfma = [&](const uint8_t* X, auto hook) {
+    sp[0] = f32x16{};
+    sp[1] = f32x16{};
+#pragma unroll
+    for (int n = 0; n < Q_AHEAD; ++n) op[n] = row_operand1(X, L, n >> 3, n & 7);
+    RA_FENCE();
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      sp[n >> 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[n], qg[n & 7], sp[n >> 3], 0, 0, 0);
+      if (n + Q_AHEAD < 16) op[n + Q_AHEAD] = row_operand1(X, L, (n + Q_AHEAD) >> 3, (n + Q_AHEAD) & 7);
+      hook(n);
       RA_FENCE();
-  #pragma unroll
-      for (int i = 0; i < 16; ++i) {  // S, dP of half 0
-        mA(0, i);
-        if (i + AHEAD < 16) rdA(0, i + AHEAD); else rdA(1, i + AHEAD - 16);
-        RA_FENCE();
-      }
-  #pragma unroll
-      for (int i = 0; i < 16; ++i) {  // S, dP of half 1; dS of half 0
-        mA(1, i);
-        if (i + AHEAD < 16) rdA(1, i + AHEAD); else rdT(0, i + AHEAD - 16);
-        valu(0, i);
-        RA_FENCE();
-      }
-      pack_ds(0);
-  #pragma unroll
-      for (int i = 0; i < 8; ++i) {  // dQ from half 0; dS of half 1; tile j + 1 to LDS
-        mT(0, i);
-        if (i + AHEAD < 8) rdT(0, i + AHEAD); else rdT(1, i + AHEAD - 8);
-        valu(1, 2 * i);
-        valu(1, 2 * i + 1);
-        put_slice(set, nxt, i, j + 1);
-        RA_FENCE();
-      }
-      pack_ds(1);
-  #pragma unroll
-      for (int i = 0; i < 8; ++i) {  // dQ from half 1
-        mT(1, i);
-        if (i + AHEAD < 8) rdT(1, i + AHEAD);
-        if (i < 5) put_slice(set, nxt, 8 + i, j + 1);
-        if (i == 5) fetch_tile(set, j + 3);  // loads land two tiles later
-        RA_FENCE();
-      }
-    };
-    if (full)
-      body(std::false_type{});
-    else
-      body(std::true_type{});
-    __syncthreads();  // tile j + 1 is in place; tile j's buffer is free
+    }
   };
-  for (int j = 0; j < n_iter; j += 2) {
-    tile(Set1{}, j);
-    if (j + 1 < n_iter) tile(Set0{}, j + 1);
-  }
+
+  // ---- the P wave: p of tile j into p slot j & 1
+  auto p_step = [&](int j, auto masked) {
+    constexpr bool M = decltype(masked)::value;
+    const int32_t* pos = sm.pos[j % 3];
+    f32x4* pb = &sm.p[j & 1][pair][0][0][lane];  // [half][group] stride 64
+    auto pgroup = [&](int kb, int g) {
+      f32x4 pv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        float p;
+        if constexpr (M) {
+          const int kr = acc_row(kb, L.h, r);
+          const bool vis = (!causal || pos[kr] <= qp) && seen && j * TILE + kr < n_k;
+          p = vis ? exp2f_(__builtin_fmaf(sp[kb][r], a.c2, -lse2)) : 0.f;
+        } else {
+          p = exp2f_(__builtin_fmaf(sp[kb][r], a.c2, -lse2));
+        }
+        pv[e] = p;
+      }
+      pb[64 * (4 * kb + g)] = pv;
+    };
+    __builtin_amdgcn_s_setprio(1);  // its MFMAs first: the dS wave's fill its exponential tail
+    rows_mfma(sm.k[j % 3], [&](int n) {
+      if (n >= 8 && (n & 1)) pgroup(0, (n - 8) >> 1);
+    });
+    __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) pgroup(1, g);
+  };
+
+  // ---- the dS wave: dS and dQ of tile j - 1 (its dP^T in sp), then dP^T of
+  // tile j
+  auto ds_step = [&](int j) {
+    if (j > 0) {
+      const int jp = j - 1;
+      const f32x4* pb = &sm.p[jp & 1][pair][0][0][lane];
+      const uint8_t* K = sm.k[jp % 3];
+      bf16x8 ds[2][2];
+      f32x4 pv[4];
+      // dQ^T MFMA n: half n / 8, i = n % 8: d block i % 4, key group i / 4
+      auto rd_t = [&](int n) { tr[n] = tr_operand1(K, L, n >> 3, (n & 7) >> 2, n & 3); };
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) pv[g] = pb[64 * (4 * kb + g)];
+        if (kb == 0) {
+#pragma unroll
+          for (int n = 0; n < Q_AHEAD; ++n) rd_t(n);
+        }
+        RA_FENCE();
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          ds[kb][r >> 3][r & 7] = (__bf16)(pv[r >> 2][r & 3] * (sp[kb][r] - delta));
+        RA_FENCE();
+      }
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        const int i = n & 7;
+        acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr[n], ds[n >> 3][i >> 2], acc[i & 3],
+                                                             0, 0, 0);
+        if (n + Q_AHEAD < 16) rd_t(n + Q_AHEAD);
+        RA_FENCE();
+      }
+    }
+    if (j < n_iter) rows_mfma(sm.v[j & 1], [](int) {});
+  };
+
+  // Each role runs its own copy of the loop (the same barriers in the same
+  // order): steps j = 0 .. n_iter, the last one only the dS wave's tail.
+  auto run = [&](auto is_p) {
+    constexpr bool PW = decltype(is_p)::value;
+    bool full_next = PW && n_iter > 0 && tile_full(0);
+    for (int j = 0; j <= n_iter; ++j) {
+      const bool more = j + 1 < n_iter;
+      if (more) dma_tile(j + 1);
+      if constexpr (PW) {
+        if (j < n_iter) {
+          const bool full = full_next;
+          if (more) full_next = tile_full(j + 1);
+          if (full)
+            p_step(j, std::false_type{});
+          else
+            p_step(j, std::true_type{});
+        }
+      } else {
+        ds_step(j);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's part of tile j + 1 landed
+      __syncthreads();  // tile j + 1 and p_j are in place; stages of j - 2 are free
+    }
+  };
+  if (pw)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
   // dq += this block's part, or dq = it (a.dq_write: the first block of a
   // whole-share backward, which then needs no zeroed dq)
-  if (rv) {
+  if (!pw && rv) {
     if (a.dq_write)
-      store_rows<false>(a.dq + srow * D, dq, L.h, a.scale);
+      store_rows<false>(a.dq + srow * D, acc, L.h, a.scale);
     else
-      store_rows<true>(a.dq + srow * D, dq, L.h, a.scale);
+      store_rows<true>(a.dq + srow * D, acc, L.h, a.scale);
   }
 }
 
@@ -285,7 +306,7 @@ hipError_t launch_backward_delta(const float* out, const void* dout, float* delt
 // queries it writes zeros).
 hipError_t launch_backward_dq(const BwdArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)((a.n_q + bwd::ROWS - 1) / bwd::ROWS * a.h_q));
-  hipLaunchKernelGGL(bwd::dq_kernel, grid, dim3(bwd::THREADS), 0, stream, a);
+  hipLaunchKernelGGL(bwd::dq_kernel, grid, dim3(bwd::Q_THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
