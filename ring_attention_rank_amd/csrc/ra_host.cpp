@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/ra.h"
 #include "ra_internal.h"
@@ -95,18 +96,41 @@ bool fast_path(const ra_problem* p) { return p->dtype == RA_BF16 && p->d_k == 12
 // Whether ra_forward splits each ring step into two half launches, one on
 // each stream.  The two chains of half launches drift apart, so each half's
 // start-up, state traffic and launch gap overlap the other half's compute
-// (the all-gather form has none of these costs).  The side stream stages the
-// next block before its half, which then waits for that copy; so the split
-// pays only where the copy is short against a step: its estimated time (K
-// and V read and written, 8 TB/s) at most 5 % of the step's causal compute
-// (half the pairs visible, 2.5 PFLOP/s).  That holds for the GQA shares
-// (1-4 %) and not for the striped MHA share (15 %), where the split measured
-// 5 % slower; where it holds, 2-7 % faster.
+// (the all-gather form has none of these costs).  The next block is staged
+// on a third stream (copy_stream) meanwhile, so no half waits behind a copy.
 bool split_ring(const ra_problem* p, const ra::StepArgs& a) {
-  if (!fast_path(p) || (int64_t)a.n_pairs * a.h_q < 2) return false;
+  return fast_path(p) && (int64_t)a.n_pairs * a.h_q >= 2;
+}
+
+// The same split while the caller's stream is being captured into a graph:
+// capturing the schedule with the third stream ended in a crash of the
+// runtime's capture, so then the side stream stages the next block before
+// its half, which waits for that copy.  That pays only where the copy is
+// short against a step: its estimated time (K and V read and written, 8 TB/s)
+// at most 5 % of the step's causal compute (half the pairs visible, 2.5
+// PFLOP/s): the GQA shares (1-4 %), not the striped MHA share (15 %, 5 %
+// slower split that way).
+bool split_ring_two_streams(const ra_problem* p, const ra::StepArgs& a) {
+  if (!split_ring(p, a)) return false;
   const double copy_s = 8.0 * p->h_kv * (double)p->n_k * p->d_k / 8e12;
   const double step_s = 2.0 * p->d_k * p->h_q * (double)p->n_q * p->n_k / 2.5e15;
   return copy_s <= 0.05 * step_s;
+}
+
+// The stream the split schedule copies blocks on: one per device, made on
+// first use (default priority, not synchronising with the null stream) and
+// kept until the process ends.
+hipStream_t copy_stream() {
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static hipStream_t streams[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(once[dev], [dev] {
+    hipStream_t s = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) == hipSuccess) streams[dev] = s;
+  });
+  return streams[dev];
 }
 
 // State (m, l, o) of the per-block fallback of ra_forward_allgather.
@@ -484,14 +508,23 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
   // caller's prior work on main (main -> side) before the first copy, and
   // the side stream's last half launch (side -> main) in the split schedule.
   hipEvent_t ev_staged[2] = {nullptr, nullptr}, ev_used[2] = {nullptr, nullptr},
-             ev_start = nullptr, ev_join = nullptr;
+             ev_used2[2] = {nullptr, nullptr}, ev_start = nullptr, ev_join = nullptr;
   ra_status result = RA_OK;
   int64_t staged = 0;
   // Split schedule: each step's launch is two halves of the work units, one
   // on each stream (see split_ring); caller-made events or timing marks keep
   // the one-launch schedule.
-  const bool split = use_side && n_cp > 1 && fixed == nullptr && launch_events == nullptr &&
-                     staged_events == nullptr && split_ring(p, a);
+  // Under graph capture (or if the capture state cannot be read) the split
+  // stages on the side stream (split_ring_two_streams); otherwise on the
+  // copy stream cs.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  const bool capturing = hipStreamIsCapturing(ms, &cap) != hipSuccess ||
+                         cap != hipStreamCaptureStatusNone;
+  hipStream_t cs = nullptr;
+  const bool split_ok = use_side && n_cp > 1 && fixed == nullptr && launch_events == nullptr &&
+                        staged_events == nullptr;
+  const bool three = split_ok && !capturing && split_ring(p, a) && (cs = copy_stream()) != nullptr;
+  const bool split = three || (split_ok && split_ring_two_streams(p, a));
   const int split_groups = split ? ra::fast_groups_for((int64_t)a.n_pairs * a.h_q) : 0;
   // The events only order work between two streams of this device; the copy
   // kernels' completion and the step kernels' launch carry their own memory
@@ -501,22 +534,25 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
     return hipEventCreateWithFlags(e, hipEventDisableTiming | hipEventDisableSystemFence) ==
            hipSuccess;
   };
-  // Copies block b (b >= 1) into slot b & 1 on stream cs, after the step that
-  // last read that slot (b - 2) is done, and marks it staged.
-  auto stage = [&](int b, hipStream_t cs) {
+  // Copies block b (b >= 1) into slot b & 1 on stream dst, after the step
+  // that last read that slot (b - 2) is done, and marks it staged.
+  auto stage = [&](int b, hipStream_t dst) {
     const int s = b & 1;
     char* slot = ws + w.slot[s];
-    if (use_side && b >= 3 && hipStreamWaitEvent(ss, ev_used[s], 0) != hipSuccess) return false;
+    if (use_side && b >= 3 &&
+        (hipStreamWaitEvent(dst, ev_used[s], 0) != hipSuccess ||
+         (three && hipStreamWaitEvent(dst, ev_used2[s], 0) != hipSuccess)))
+      return false;
     if (w.kbytes &&
-        (hipMemcpyAsync(slot, k_blocks[b], w.kbytes, hipMemcpyDeviceToDevice, cs) != hipSuccess ||
+        (hipMemcpyAsync(slot, k_blocks[b], w.kbytes, hipMemcpyDeviceToDevice, dst) != hipSuccess ||
          hipMemcpyAsync(slot + align_up(w.kbytes), v_blocks[b], w.kbytes, hipMemcpyDeviceToDevice,
-                        cs) != hipSuccess ||
+                        dst) != hipSuccess ||
          hipMemcpyAsync(slot + 2 * align_up(w.kbytes), k_pos_blocks[b], w.pbytes,
-                        hipMemcpyDeviceToDevice, cs) != hipSuccess))
+                        hipMemcpyDeviceToDevice, dst) != hipSuccess))
       return false;
     staged += 2 * (int64_t)w.kbytes;
-    if (!mark(staged_events, b, cs)) return false;
-    return !use_side || hipEventRecord(ev_staged[s], ss) == hipSuccess;
+    if (!mark(staged_events, b, dst)) return false;
+    return !use_side || hipEventRecord(ev_staged[s], dst) == hipSuccess;
   };
   if (use_side && n_cp > 1) {
     if (fixed) {
@@ -526,12 +562,14 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
       ev_used[0] = fixed[3];
       ev_used[1] = fixed[4];
     } else if (!mk(&ev_start) || !mk(&ev_staged[0]) || !mk(&ev_staged[1]) || !mk(&ev_used[0]) ||
-               !mk(&ev_used[1]) || (split && !mk(&ev_join))) {
+               !mk(&ev_used[1]) ||
+               (split && !mk(&ev_join)) || (three && (!mk(&ev_used2[0]) || !mk(&ev_used2[1])))) {
       result = RA_ERR_HIP;
       goto cleanup;
     }
     if (hipEventRecord(ev_start, ms) != hipSuccess ||
-        hipStreamWaitEvent(ss, ev_start, 0) != hipSuccess) {
+        hipStreamWaitEvent(ss, ev_start, 0) != hipSuccess ||
+        (three && hipStreamWaitEvent(cs, ev_start, 0) != hipSuccess)) {
       result = RA_ERR_HIP;
       goto cleanup;
     }
@@ -556,8 +594,13 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
       a.k_pos = (const int32_t*)(slot + 2 * align_up(w.kbytes));
     }
     if (split) {
-      // first half on the main stream; the side stream stages block b + 1
-      // and then runs the second half
+      // first half on the main stream, second half on the side stream (which
+      // also waits for this block's copy), block b + 1 staged on the copy
+      // stream meanwhile (or on the side stream before its half)
+      if (three && !first && hipStreamWaitEvent(ss, ev_staged[b & 1], 0) != hipSuccess) {
+        result = RA_ERR_HIP;
+        goto cleanup;
+      }
       const int total = a.n_pairs * a.h_q, half = total / 2;
       ra::StepArgs ha = a, hb = a;
       ha.unit0 = 0;
@@ -567,7 +610,7 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
       ha.groups = hb.groups = split_groups;
       result = launch(p, ha, /*read=*/!first, /*final=*/last, ms);
       if (result != RA_OK) goto cleanup;
-      if (b + 1 < n_cp && !stage(b + 1, ss)) { result = RA_ERR_HIP; goto cleanup; }
+      if (b + 1 < n_cp && !stage(b + 1, three ? cs : ss)) { result = RA_ERR_HIP; goto cleanup; }
       result = launch(p, hb, /*read=*/!first, /*final=*/last, ss);
       if (result != RA_OK) goto cleanup;
     } else {
@@ -578,9 +621,14 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
       if (result != RA_OK) goto cleanup;
     }
     if (use_side && !first && b + 2 < n_cp) {
-      // slot b & 1 is free for block b + 2 once this step's main-stream part
-      // is done (its side-stream part precedes that copy on the side stream)
-      if (hipEventRecord(ev_used[b & 1], ms) != hipSuccess) { result = RA_ERR_HIP; goto cleanup; }
+      // slot b & 1 is free for block b + 2 once this step is done: its
+      // main-stream part, and with the copy stream its side-stream part
+      // (otherwise that precedes the copy on the side stream)
+      if (hipEventRecord(ev_used[b & 1], ms) != hipSuccess ||
+          (three && hipEventRecord(ev_used2[b & 1], ss) != hipSuccess)) {
+        result = RA_ERR_HIP;
+        goto cleanup;
+      }
     }
   }
   if (split && (hipEventRecord(ev_join, ss) != hipSuccess ||
@@ -592,7 +640,8 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
 
 cleanup:
   if (!fixed)
-    for (hipEvent_t e : {ev_start, ev_staged[0], ev_staged[1], ev_used[0], ev_used[1], ev_join})
+    for (hipEvent_t e : {ev_start, ev_staged[0], ev_staged[1], ev_used[0], ev_used[1], ev_used2[0],
+                         ev_used2[1], ev_join})
       if (e) (void)hipEventDestroy(e);  // the call's status is already decided
   return result;
 }
