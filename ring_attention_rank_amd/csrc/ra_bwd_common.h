@@ -24,61 +24,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int D = 128;
-constexpr int ROWS = 128;      // rows a workgroup owns (4 waves x 32)
+constexpr int ROWS = 128;      // rows a workgroup owns (4 wave pairs x 32)
 constexpr int TILE = 64;       // rows of a staged tile
-constexpr int THREADS = 256;
 constexpr int TILE_BYTES = TILE * D * 2;  // 16 KiB
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ int sigma(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 __device__ __forceinline__ float exp2f_(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Physical byte offset of 16-byte chunk c of row r: "row" swizzle for
-// ds_read_b128 row reads, "tr" swizzle for the transposing reads.
-__device__ __forceinline__ int off_row(int r, int c) { return r * 256 + 16 * (c ^ (r & 15)); }
-__device__ __forceinline__ int off_tr(int r, int c) { return r * 256 + 16 * (c ^ (4 * (r & 3))); }
-
-// Per-lane read bases (see the forward kernel): row reads of half kb take row
-// sigma(col) + 32 kb, logical chunk 2 ks + h; transposing reads give the
-// 32 x 16 operand of d block db and row group t of half kb.
-struct Lanes {
-  int rd_row, rd_tr, h, col;
-  __device__ Lanes(int lane) {
-    h = lane >> 5;
-    col = lane & 31;
-    const int r = sigma(col), x = r & 15;
-    rd_row = r * 256 + 16 * (h ^ (x & 1)) + 32 * (x >> 1);  // ^ (32 ks)
-    const int g4 = lane >> 4, i = lane & 15;
-    const int hh = g4 >> 1, dgrp = g4 & 1, rho = i >> 2, b = (i & 3) >> 1, half = i & 1;
-    rd_tr = (8 * hh + rho) * 256 + 64 * rho + 32 * dgrp + 16 * b + 8 * half;  // ^ (64 db)
-  }
-};
-
-__device__ __forceinline__ bf16x8 row_operand(const uint8_t* tile, const Lanes& L, int kb, int ks) {
-  return *(const bf16x8*)(tile + kb * 32 * 256 + (L.rd_row ^ (32 * ks)));
-}
-__device__ __forceinline__ bf16x8 tr_operand(const uint8_t* tile, const Lanes& L, int kb, int t,
-                                             int db) {
-  const uint8_t* base = tile + kb * 32 * 256 + (L.rd_tr ^ (64 * db)) + t * 16 * 256;
-  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)base);
-  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 4 * 256));
-  // whole-vector assembly: element-wise __bf16 inserts were mis-lowered
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// Global -> register half of the tile staging: rows [r0, r0 + 64) of a
-// [n][128] bf16 matrix, 4 chunks of 16 bytes per thread, zeros past n.  The
-// loads are issued one tile ahead and their latency hides behind the current
-// tile's MFMAs.
-__device__ __forceinline__ void fetch(const uint16_t* src, int r0, int n, u32x4 (&x)[4], int tid) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = tid + THREADS * i;
-    const int r = id >> 4, c = id & 15;
-    x[i] = u32x4{0u, 0u, 0u, 0u};
-    if (r0 + r < n) x[i] = *(const u32x4*)(src + (size_t)(r0 + r) * D + c * 8);
-  }
-}
 
 // XCD-aware split of a one-dimensional grid of n_x * n_y workgroups into
 // (x, y).  Workgroup L runs on XCD L % 8 (8 XCDs, each with its own L2); when
@@ -104,50 +56,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
                                            0x00020000);
 }
 
-// Rows [r0, r0 + 64) of a [n][128] bf16 matrix behind resource r, 4 chunks of
-// 16 bytes per thread (zeros past the resource's end).
-__device__ __forceinline__ void fetch_rows(__amdgpu_buffer_rsrc_t r, int r0, u32x4 (&x)[4],
-                                           int tid) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = tid + THREADS * i;
-    const uint32_t off = (uint32_t)(r0 + (id >> 4)) * 256u + (uint32_t)(id & 15) * 16u;
-    x[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-  }
-}
-
-// Register -> LDS, one chunk: the i-th 16-byte chunk a thread holds, into
-// one or two swizzled copies of the tile.
-__device__ __forceinline__ void put_one(const u32x4& x, uint8_t* t_row, uint8_t* t_tr, int tid,
-                                        int i) {
-  const int id = tid + THREADS * i;
-  const int r = id >> 4, c = id & 15;
-  if (t_row) *(u32x4*)(t_row + off_row(r, c)) = x;
-  if (t_tr) *(u32x4*)(t_tr + off_tr(r, c)) = x;
-}
-
-// Register -> LDS half: one or two swizzled copies of the tile.
-__device__ __forceinline__ void put(const u32x4 (&x)[4], uint8_t* t_row, uint8_t* t_tr, int tid) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int id = tid + THREADS * i;
-    const int r = id >> 4, c = id & 15;
-    if (t_row) *(u32x4*)(t_row + off_row(r, c)) = x[i];
-    if (t_tr) *(u32x4*)(t_tr + off_tr(r, c)) = x[i];
-  }
-}
-
 // Register value r of half kb of an S^T or S accumulator belongs to tile row
 // 32 kb + 8 h + 16 (r / 8) + r % 8.
 __device__ __forceinline__ int acc_row(int kb, int h, int r) {
   return 32 * kb + 8 * h + 16 * (r >> 3) + (r & 7);
-}
-
-__device__ __forceinline__ void pack(const f32x16& x, bf16x8 (&p)[2]) {
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) p[t][e] = (__bf16)x[8 * t + e];
 }
 
 // Stores a 128-wide accumulator (O^T layout: 4 d blocks, lane column = row)
@@ -168,17 +80,6 @@ __device__ __forceinline__ void store_rows(float* dst, const f32x16 (&acc)[4], i
     }
 }
 
-// The 16 values of a per-row (or per-key) LDS array that belong to the
-// accumulator registers of half kb: rows 32 kb + 8 h + {0..7, 16..23}.
-template <typename T4, typename E>
-__device__ __forceinline__ void read_half(const E* arr, int kb, int h, T4 (&x)[4]) {
-  const E* b = arr + 32 * kb + 8 * h;
-  x[0] = *(const T4*)(b);
-  x[1] = *(const T4*)(b + 4);
-  x[2] = *(const T4*)(b + 16);
-  x[3] = *(const T4*)(b + 20);
-}
-
 // ---- one-copy tiles (LDS DMA) ------------------------------------------
 // A tile staged once and read both ways: 16-byte chunk c of row r sits at
 // physical chunk c ^ uswz(r).  uswz is a bijection on r & 15 (row reads of 16
@@ -188,9 +89,11 @@ __device__ __forceinline__ void read_half(const E* arr, int kb, int h, T4 (&x)[4
 // patterns are free of bank conflicts.
 __device__ __forceinline__ int uswz(int r) { return 4 * (r & 3) | ((r >> 2) & 3); }
 
-// Per-lane read bases into a one-copy tile: the same logical bytes as
-// Lanes::rd_row and Lanes::rd_tr (and rd_tr + 4 rows) on the two-copy
-// layouts, so the operands are identical.
+// Per-lane read bases into a one-copy tile.  Row reads of half kb take row
+// sigma(col) + 32 kb, logical chunk 2 ks + h (the MFMA A operand of 32 rows
+// x 16 columns, rows permuted by sigma as in the forward kernel); the
+// transposing reads give the 32 x 16 operand of d block db and row group t
+// of half kb in two ds_read_b64_tr_b16 (rows 8 hh + rho and 4 rows on).
 struct Lanes1 {
   int rd_row, rd_lo, rd_hi, h, col;
   __device__ Lanes1(int lane) {
