@@ -314,13 +314,16 @@ def test_debug_check_on_device_positions(monkeypatch):
         ra.forward(sh.gq, bad, sh.gk, sh.gv, sh.gk_pos)
 
 
-@pytest.mark.parametrize("name", ["llama405b_stage_share", "llama70b_stage_share"])
+@pytest.mark.parametrize("name", ["llama405b_stage_share", "llama70b_stage_share",
+                                  "million_striped_mha"])
 def test_split_schedule_matches_one_launch(name):
     """At full size these shares run each ring step as two half launches, one
-    on each stream.  Every work unit computes exactly what it computes in the
-    one-launch schedule (one stream; the timed call, which never splits), so
-    the results and tile counts are the same bit for bit, and so is a
-    HIP-graph replay of the split schedule."""
+    on each stream, while the library's copy stream stages the next block.
+    Every work unit computes exactly what it computes in the one-launch
+    schedule (one stream; the timed call, which never splits), so the results
+    and tile counts are the same bit for bit, and so is a HIP-graph replay
+    (captured, the schedule stages on the side stream: split for the GQA
+    shares, one launch per step for the striped one)."""
     sh = Share(synth.case_by_name(name), 0).to_gpu()
     print(f"[parity] split schedule {name}", flush=True)
     a = run_forward(sh)              # side stream: split halves
