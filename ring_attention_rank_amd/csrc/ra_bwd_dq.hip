@@ -13,17 +13,16 @@
 // Two kernels, each shaped like the forward step kernel so that every
 // accumulator stays in registers and nothing is reduced through atomics:
 //
-//  * dq kernel: a wave owns 32 query rows (Q and dout in registers) and walks
-//    the visible 64-key tiles: S^T = K Q^T and dP^T = V dout^T (K and V rows
-//    the A operands), dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T (K read
+//  * dq kernel: 32 query rows (Q and dout in registers) walk the visible
+//    64-key tiles: S^T = K Q^T and dP^T = V dout^T (K and V rows the A
+//    operands), dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T (K read
 //    transposed, dS^T packed to bf16 as the B operand straight from the
 //    accumulators, as P^T feeds V^T P^T in the forward).
-//  * dk/dv kernel (ra_bwd_dkv.hip): the mirror image.  A wave owns 32 keys
-//    (K and V rows in registers) and walks the query heads of its split of
-//    the key/value head's group and the 64-query tiles that see those keys:
-//    S = Q K^T and dP = dout V^T (Q and dout rows the A operands),
-//    dS = P (dP - delta), dV^T += dout^T P and dK^T += Q^T dS (dout and Q
-//    read transposed).
+//  * dk/dv kernel (ra_bwd_dkv.hip): the mirror image.  32 keys (K and V rows
+//    in registers) walk the query heads of their split of the key/value
+//    head's group and the 64-query tiles that see those keys: S = Q K^T and
+//    dP = dout V^T (Q and dout rows the A operands), dS = P (dP - delta),
+//    dV^T += dout^T P and dK^T += Q^T dS (dout and Q read transposed).
 //
 // Both kernels run two waves per SIMD, each under 256 registers, as pairs
 // of waves that own the same rows (here 32 queries, in ra_bwd_dkv.hip 32
