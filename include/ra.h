@@ -108,9 +108,11 @@ ra_status ra_step(const ra_problem* p, const void* q, const int32_t* q_pos,
 ra_status ra_finalize(const ra_problem* p, const float* m, const float* l, const float* o,
                       float* out, float* lse, void* stream);
 
-/* Bytes of device workspace ra_forward needs: the running state and two
- * staging slots for incoming key/value blocks (the ring's "one block being
- * computed plus the one arriving"). */
+/* Bytes of device workspace ra_forward needs: the running state and the
+ * staging slots for incoming key/value blocks.  Two slots in general (the
+ * ring's block being computed and the one arriving); four for bf16 with
+ * d_k = 128, where with a side stream each launch after the first takes two
+ * blocks and the next launch's two arrive meanwhile. */
 size_t ra_forward_workspace_bytes(const ra_problem* p);
 
 /*
@@ -118,10 +120,19 @@ size_t ra_forward_workspace_bytes(const ra_problem* p);
  * k_blocks, v_blocks, k_pos_blocks: HOST arrays of n_cp device pointers, in
  * ring order; entry 0 is the rank's own block (used in place), and block b
  * is the one received at step b.  Each block b >= 1 is copied into a staging
- * slot of the workspace on side_stream while step b-1 computes on
- * main_stream -- a one-GPU stand-in for the ring receive -- with events so a
- * slot is never overwritten before its step has read it.  If side_stream is
- * NULL or equal to main_stream the copies run on main_stream.
+ * slot of the workspace while earlier blocks compute -- a one-GPU stand-in
+ * for the ring receive -- with events so a slot is never overwritten before
+ * the launch that reads it is done.  Schedules:
+ *  - side_stream NULL or equal to main_stream: everything on main_stream;
+ *  - otherwise, shapes other than bf16 with d_k = 128: one launch per step
+ *    on main_stream, copies on side_stream;
+ *  - bf16, d_k = 128: each launch's work split in two halves, one on
+ *    main_stream and one on side_stream, the copies on a stream the library
+ *    creates once per device; launches after the first take two blocks each
+ *    (n_cp >= 3, the state kept in registers between them, same bits as one
+ *    launch per block).  While main_stream is being captured into a graph,
+ *    one block per launch and the copies on side_stream (split only where
+ *    the copy is short against a step).
  * out, lse: results.  work: optional device int64[3], zeroed and then filled
  * with the tile counts summed over all steps.  staged_bytes: optional host
  * pointer, receives the key/value bytes copied into staging slots

@@ -798,6 +798,65 @@ struct Step {
     finish();
   }
 
+  // Consecutive ring blocks in one launch (up to kChunkBlocks, one group per
+  // workgroup), the running state in registers between them.  Between two
+  // blocks it goes through the same rounding as a store and reload between
+  // two step launches (the max in natural log, the row sum gathered in one
+  // half-wave), so the result is bit for bit that of one launch per block;
+  // a tile that sees none of the blocks leaves the state untouched.
+  __device__ void run_chunk(const MultiArgs& ma, int qt, int head) {
+    static_assert(G == 1, "one group per workgroup");
+    positions(qt, head);
+    Classes cls[kChunkBlocks];
+    bool any = false;
+#pragma unroll
+    for (int b = 0; b < kChunkBlocks; ++b) {
+      if (b < ma.n_blocks) {
+        cls[b] = classes_of(ma.k_pos[b]);
+        any = any || cls[b].n_iter > 0;
+      }
+    }
+    if (READ && !FINAL && !any) {
+      if (count && lane == 0) {
+        const int n_kt_all = (n_k + BN - 1) / BN;
+        atomicAdd(a.work + 2, (unsigned long long)(ma.n_blocks * n_kt_all));
+      }
+      return;
+    }
+    load_state(head);
+    const int kvh = head / (a.h_q / a.h_kv);
+    head_issued = false;
+    nxt_kvh = kvh;  // the prefetch of the next block's first tiles reads this head
+#pragma unroll
+    for (int b = 0; b < kChunkBlocks; ++b) {
+      if (b < ma.n_blocks) {
+        use_classes(cls[b]);
+        if (b + 1 < ma.n_blocks) {
+          nxt_k = ma.k[b + 1];
+          nxt_pos = ma.k_pos[b + 1];
+          nxt_own = own_tiles(cls[b + 1].n_iter);
+        } else {
+          nxt_k = nullptr;
+          nxt_pos = nullptr;
+          nxt_own = 0;
+        }
+        fold_block(ma.k[b], ma.v[b], ma.k_pos[b], kvh);
+        if (b + 1 < ma.n_blocks) {
+          // the store and reload between two step launches, in registers
+          const float ltot = half_swap_sum(lsum);
+          const float m_nat = (m2 == m2_0) ? m_nat0 : m2 * kLn2;
+          m_nat0 = m_nat;
+          m2 = m_nat * kLog2e;
+          m2_0 = m2;
+          lsum = h == 0 ? ltot : 0.f;
+          resc = false;
+        }
+      }
+    }
+    nxt_k = nullptr;
+    finish();
+  }
+
   // All blocks resident: the query tile against every block in turn, the
   // running state staying in registers between them.  Under a document mask
   // only the blocks b with b mod n_split = split are folded.
@@ -888,6 +947,25 @@ void step_kernel_fast(const StepArgs a) {
   if (t_lo < t_hi) {
     __syncthreads();
     s.run(t_lo, head);
+  }
+}
+
+// Up to kChunkBlocks consecutive ring blocks per launch (one group per
+// workgroup): the units as in step_kernel_fast.
+template <bool READ, bool FINAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void chunk_kernel_fast(const MultiArgs ma) {
+  __shared__ Smem<1> sm;
+  const int tid = threadIdx.x;
+  const int u = blockIdx.x + ma.s.unit0;
+  const int head = ma.s.head_of[u % ma.s.h_q];
+  const int p = u / ma.s.h_q;
+  const int t_hi = ma.s.n_qt - 1 - p, t_lo = p;
+  Step<1, READ, FINAL> s(ma.s, sm, tid);
+  s.run_chunk(ma, t_hi, head);
+  if (t_lo < t_hi) {
+    __syncthreads();
+    s.run_chunk(ma, t_lo, head);
   }
 }
 
@@ -1038,6 +1116,20 @@ hipError_t launch_allgather_fast(const MultiArgs& ma, hipStream_t stream) {
     hipLaunchKernelGGL((fast::allgather_kernel_fast<1, false>), grid, block, 0, stream, ma);
   else
     hipLaunchKernelGGL((fast::allgather_kernel_fast<2, false>), grid, block, 0, stream, ma);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_fast(const MultiArgs& ma, bool read, bool final_, hipStream_t stream) {
+  const StepArgs& a = ma.s;
+  dim3 grid((unsigned)(a.n_units ? a.n_units : a.n_pairs * a.h_q)), block(256);
+  if (read && final_)
+    hipLaunchKernelGGL((fast::chunk_kernel_fast<true, true>), grid, block, 0, stream, ma);
+  else if (read)
+    hipLaunchKernelGGL((fast::chunk_kernel_fast<true, false>), grid, block, 0, stream, ma);
+  else if (final_)
+    hipLaunchKernelGGL((fast::chunk_kernel_fast<false, true>), grid, block, 0, stream, ma);
+  else
+    hipLaunchKernelGGL((fast::chunk_kernel_fast<false, false>), grid, block, 0, stream, ma);
   return hipGetLastError();
 }
 

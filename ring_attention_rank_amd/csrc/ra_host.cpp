@@ -197,11 +197,17 @@ ra_status launch(const ra_problem* p, const ra::StepArgs& a, bool read, bool fin
   return e == hipSuccess ? RA_OK : RA_ERR_HIP;
 }
 
+// Staging slots of ra_forward's workspace: four on the bf16 d_k = 128 path,
+// where the chunked schedule (two blocks per launch) stages the next
+// launch's two blocks while the current launch reads its own two; two
+// elsewhere and in the no-alloc form.
+constexpr int kChunkSlots = 4;
+
 struct WsLayout {
-  size_t m, l, o, slot[2], kbytes, pbytes, total;
+  size_t m, l, o, slot[kChunkSlots], kbytes, pbytes, total;
 };
 
-WsLayout ws_layout(const ra_problem* p) {
+WsLayout ws_layout(const ra_problem* p, int n_slots = 2) {
   WsLayout w;
   const size_t rows = (size_t)p->h_q * p->n_q;
   w.kbytes = (size_t)p->h_kv * p->n_k * p->d_k * elem_bytes(p->dtype);
@@ -213,7 +219,8 @@ WsLayout ws_layout(const ra_problem* p) {
   off = align_up(off + rows * 4);
   w.o = off;
   off = align_up(off + rows * p->d_k * 4);
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < kChunkSlots; ++s) w.slot[s] = 0;
+  for (int s = 0; s < n_slots; ++s) {
     w.slot[s] = off;  // K, then V, then positions
     off = align_up(off + w.kbytes);
     off = align_up(off + w.kbytes);
@@ -399,7 +406,7 @@ ra_status ra_finalize(const ra_problem* p, const float* m, const float* l, const
 
 size_t ra_forward_workspace_bytes(const ra_problem* p) {
   if (check_problem(p) != RA_OK) return 0;
-  return ws_layout(p).total;
+  return ws_layout(p, fast_path(p) ? kChunkSlots : 2).total;
 }
 
 ra_status ra_forward(const ra_problem* p, int32_t n_cp, const void* q, const int32_t* q_pos,
@@ -425,7 +432,6 @@ ra_status ra_forward_timed(const ra_problem* p, int32_t n_cp, const void* q, con
 
 }  // extern "C"
 
-size_t ra::forward_workspace_bytes(const ra_problem* p) { return ws_layout(p).total; }
 
 // The ring of ra_forward.  fixed: null, or five events made by the caller
 // (no timing, no system fence) that this call uses instead of creating and
@@ -440,7 +446,7 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
   if (st != RA_OK) return st;
   if (n_cp < 1) return RA_ERR_SHAPE;
   if (!k_blocks || !v_blocks || !k_pos_blocks) return RA_ERR_NULL;
-  const WsLayout w = ws_layout(p);
+  const WsLayout w2 = ws_layout(p, 2);
   if (p->n_q > 0) {
     if (!q || !q_pos || !out || !lse) return RA_ERR_NULL;
     if (!aligned16(q) || !aligned4(q_pos) || !aligned16(out) || !aligned4(lse))
@@ -456,7 +462,10 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
   }
   if (!workspace) return RA_ERR_NULL;
   if (!aligned16(workspace)) return RA_ERR_ALIGN;
-  if (ws_bytes < w.total) return RA_ERR_WORKSPACE;
+  // ra_forward asks for what ra_forward_workspace_bytes reports; the no-alloc
+  // form (fixed events, never chunked) for the two-slot layout only.
+  if (ws_bytes < (fixed ? w2.total : ws_layout(p, fast_path(p) ? kChunkSlots : 2).total))
+    return RA_ERR_WORKSPACE;
   if (launch_events)
     for (int i = 0; i < 2 * n_cp; ++i)
       if (!launch_events[i]) return RA_ERR_NULL;
@@ -472,9 +481,9 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
   hipStream_t ss = (hipStream_t)side_stream;
   const bool use_side = ss != nullptr && ss != ms;
   char* ws = (char*)workspace;
-  float* m = (float*)(ws + w.m);
-  float* l = (float*)(ws + w.l);
-  float* o = (float*)(ws + w.o);
+  float* m = (float*)(ws + w2.m);
+  float* l = (float*)(ws + w2.l);
+  float* o = (float*)(ws + w2.o);
 
   if (staged_bytes) *staged_bytes = 0;
   if (!mark(staged_events, 0, ms)) return RA_ERR_HIP;
@@ -507,8 +516,8 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
   // Events: slot s staged (side -> main), slot s consumed (main -> side), the
   // caller's prior work on main (main -> side) before the first copy, and
   // the side stream's last half launch (side -> main) in the split schedule.
-  hipEvent_t ev_staged[2] = {nullptr, nullptr}, ev_used[2] = {nullptr, nullptr},
-             ev_used2[2] = {nullptr, nullptr}, ev_start = nullptr, ev_join = nullptr;
+  hipEvent_t ev_staged[kChunkSlots] = {}, ev_used[kChunkSlots] = {}, ev_used2[kChunkSlots] = {},
+            ev_start = nullptr, ev_join = nullptr;
   ra_status result = RA_OK;
   int64_t staged = 0;
   // Split schedule: each step's launch is two halves of the work units, one
@@ -526,6 +535,14 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
   const bool three = split_ok && !capturing && split_ring(p, a) && (cs = copy_stream()) != nullptr;
   const bool split = three || (split_ok && split_ring_two_streams(p, a));
   const int split_groups = split ? ra::fast_groups_for((int64_t)a.n_pairs * a.h_q) : 0;
+  // Chunked schedule: with the copy stream, one-group workgroups and a
+  // four-slot workspace, launches fold two blocks each ([0], [1, 2], [3, 4],
+  // ...) with the state in registers between them; block b >= 1 is staged
+  // into slot (b - 1) % 4.
+  const bool chunked = three && split_groups == 1 && n_cp >= 3;
+  const WsLayout w = ws_layout(p, chunked ? kChunkSlots : 2);
+  const int n_slots = chunked ? kChunkSlots : 2;
+  auto slot_of = [&](int b) { return chunked ? (b - 1) % kChunkSlots : b & 1; };
   // The events only order work between two streams of this device; the copy
   // kernels' completion and the step kernels' launch carry their own memory
   // fences, so the events skip the system-scope fence (a cache writeback and
@@ -534,12 +551,12 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
     return hipEventCreateWithFlags(e, hipEventDisableTiming | hipEventDisableSystemFence) ==
            hipSuccess;
   };
-  // Copies block b (b >= 1) into slot b & 1 on stream dst, after the step
-  // that last read that slot (b - 2) is done, and marks it staged.
+  // Copies block b (b >= 1) into its slot on stream dst, after the launch
+  // that last read that slot (block b - n_slots) is done, and marks it staged.
   auto stage = [&](int b, hipStream_t dst) {
-    const int s = b & 1;
+    const int s = slot_of(b);
     char* slot = ws + w.slot[s];
-    if (use_side && b >= 3 &&
+    if (use_side && b - n_slots >= 1 &&
         (hipStreamWaitEvent(dst, ev_used[s], 0) != hipSuccess ||
          (three && hipStreamWaitEvent(dst, ev_used2[s], 0) != hipSuccess)))
       return false;
@@ -561,11 +578,14 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
       ev_staged[1] = fixed[2];
       ev_used[0] = fixed[3];
       ev_used[1] = fixed[4];
-    } else if (!mk(&ev_start) || !mk(&ev_staged[0]) || !mk(&ev_staged[1]) || !mk(&ev_used[0]) ||
-               !mk(&ev_used[1]) ||
-               (split && !mk(&ev_join)) || (three && (!mk(&ev_used2[0]) || !mk(&ev_used2[1])))) {
-      result = RA_ERR_HIP;
-      goto cleanup;
+    } else {
+      bool ok = mk(&ev_start) && (!split || mk(&ev_join));
+      for (int i = 0; ok && i < n_slots; ++i)
+        ok = mk(&ev_staged[i]) && mk(&ev_used[i]) && (!three || mk(&ev_used2[i]));
+      if (!ok) {
+        result = RA_ERR_HIP;
+        goto cleanup;
+      }
     }
     if (hipEventRecord(ev_start, ms) != hipSuccess ||
         hipStreamWaitEvent(ss, ev_start, 0) != hipSuccess ||
@@ -575,6 +595,76 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
     }
   }
 
+  if (chunked) {
+    // launch c folds blocks c0 .. c0 + nb - 1: [0], [1, 2], [3, 4], ...
+    const int n_launch = 1 + n_cp / 2;
+    const int total = a.n_pairs * a.h_q, half = total / 2;
+    auto blocks_of = [&](int c, int& c0, int& nb) {
+      c0 = c == 0 ? 0 : 2 * c - 1;
+      nb = c == 0 ? 1 : std::min(2, n_cp - c0);
+    };
+    for (int c = 0; c < n_launch; ++c) {
+      int c0, nb;
+      blocks_of(c, c0, nb);
+      const bool first = c == 0, last = c == n_launch - 1;
+      ra::MultiArgs ma;
+      ma.s = a;
+      ma.n_blocks = nb;
+      for (int i = 0; i < nb; ++i) {
+        const int b = c0 + i;
+        if (b == 0) {
+          ma.k[i] = k_blocks[0];
+          ma.v[i] = v_blocks[0];
+          ma.k_pos[i] = k_pos_blocks[0];
+          continue;
+        }
+        // both halves wait for the block's copy
+        const int sl = slot_of(b);
+        if (hipStreamWaitEvent(ms, ev_staged[sl], 0) != hipSuccess ||
+            hipStreamWaitEvent(ss, ev_staged[sl], 0) != hipSuccess) {
+          result = RA_ERR_HIP;
+          goto cleanup;
+        }
+        char* slot = ws + w.slot[sl];
+        ma.k[i] = slot;
+        ma.v[i] = slot + align_up(w.kbytes);
+        ma.k_pos[i] = (const int32_t*)(slot + 2 * align_up(w.kbytes));
+      }
+      ra::MultiArgs ha = ma, hb = ma;
+      ha.s.unit0 = 0;
+      ha.s.n_units = half;
+      hb.s.unit0 = half;
+      hb.s.n_units = total - half;
+      if (ra::launch_chunk_fast(ha, !first, last, ms) != hipSuccess) {
+        result = RA_ERR_HIP;
+        goto cleanup;
+      }
+      // the next launch's blocks go to their slots on the copy stream
+      if (c + 1 < n_launch) {
+        int n0, nn;
+        blocks_of(c + 1, n0, nn);
+        for (int i = 0; i < nn; ++i)
+          if (!stage(n0 + i, cs)) {
+            result = RA_ERR_HIP;
+            goto cleanup;
+          }
+      }
+      if (ra::launch_chunk_fast(hb, !first, last, ss) != hipSuccess) {
+        result = RA_ERR_HIP;
+        goto cleanup;
+      }
+      // the slots of this launch's blocks are free once both halves are done
+      for (int i = 0; i < nb; ++i) {
+        const int b = c0 + i;
+        if (b >= 1 && b + n_slots < n_cp &&
+            (hipEventRecord(ev_used[slot_of(b)], ms) != hipSuccess ||
+             hipEventRecord(ev_used2[slot_of(b)], ss) != hipSuccess)) {
+          result = RA_ERR_HIP;
+          goto cleanup;
+        }
+      }
+    }
+  } else
   for (int b = 0; b < n_cp; ++b) {
     const bool first = b == 0, last = b == n_cp - 1;
     if (first) {
@@ -640,8 +730,9 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
 
 cleanup:
   if (!fixed)
-    for (hipEvent_t e : {ev_start, ev_staged[0], ev_staged[1], ev_used[0], ev_used[1], ev_used2[0],
-                         ev_used2[1], ev_join})
+    for (hipEvent_t e : {ev_start, ev_join, ev_staged[0], ev_staged[1], ev_staged[2], ev_staged[3],
+                         ev_used[0], ev_used[1], ev_used[2], ev_used[3], ev_used2[0], ev_used2[1],
+                         ev_used2[2], ev_used2[3]})
       if (e) (void)hipEventDestroy(e);  // the call's status is already decided
   return result;
 }

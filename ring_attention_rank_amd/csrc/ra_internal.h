@@ -22,15 +22,14 @@ constexpr int kSplitSpan = 8192;
 
 // The ring forward behind ra_forward / ra_forward_timed (arguments as
 // there); fixed: null, or five caller-made events (no timing, no system
-// fence) used in place of per-call ones.  forward_workspace_bytes: the
-// workspace it needs (the problem already checked).
+// fence) used in place of per-call ones; with them the workspace needs only
+// the two-slot layout (the schedule then never chunks).
 ra_status forward_ring(const ra_problem* p, int32_t n_cp, const void* q, const int32_t* q_pos,
                        const void* const* k_blocks, const void* const* v_blocks,
                        const int32_t* const* k_pos_blocks, void* workspace, size_t ws_bytes,
                        float* out, float* lse, int64_t* work, int64_t* staged_bytes,
                        void* main_stream, void* side_stream, void* const* launch_events,
                        void* const* staged_events, const hipEvent_t* fixed);
-size_t forward_workspace_bytes(const ra_problem* p);
 
 // Arguments of one ring-step launch (one key/value block against all local
 // queries of all heads).  READ selects whether the state is read (else it
@@ -67,6 +66,9 @@ struct StepArgs {
 
 // All key/value blocks resident (the all-gather form): one launch folds them
 // all, in order, into a register-resident state and writes out/lse.
+// Ring blocks one chunk launch folds (ra_forward's chunked schedule).
+constexpr int kChunkBlocks = 2;
+
 struct MultiArgs {
   StepArgs s;  // q, q_pos, out, lse, work, sizes; s.k, s.v, s.k_pos unused
   int32_t n_blocks;
@@ -79,6 +81,9 @@ struct MultiArgs {
 // times (hipExtLaunchKernel); null for a plain launch.
 hipError_t launch_step(const StepArgs& a, int dtype, int d_k, bool read, bool final_,
                        hipStream_t stream, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+// bfloat16, d_k = 128, one group per workgroup: ma.n_blocks (1 or 2)
+// consecutive ring blocks in one launch, the units of ma.s (unit0, n_units).
+hipError_t launch_chunk_fast(const MultiArgs& ma, bool read, bool final_, hipStream_t stream);
 // bfloat16, d_k = 128: the 8-wave kernel with direct-to-LDS staging.
 hipError_t launch_step_fast(const StepArgs& a, bool read, bool final_, hipStream_t stream,
                             hipEvent_t start = nullptr, hipEvent_t stop = nullptr);

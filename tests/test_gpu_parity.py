@@ -315,11 +315,13 @@ def test_debug_check_on_device_positions(monkeypatch):
 
 
 @pytest.mark.parametrize("name", ["llama405b_stage_share", "llama70b_stage_share",
-                                  "million_striped_mha"])
+                                  "llama8b_gqa_zigzag", "million_striped_mha"])
 def test_split_schedule_matches_one_launch(name):
-    """At full size these shares run each ring step as two half launches, one
-    on each stream, while the library's copy stream stages the next block.
-    Every work unit computes exactly what it computes in the one-launch
+    """At full size these shares run the ring as launches of two half grids,
+    one on each stream, while the library's copy stream stages the next
+    blocks; launches after the first take two blocks each where one group
+    per workgroup runs (the state kept in registers between them).  Every
+    work unit computes exactly what it computes in the one-launch-per-block
     schedule (one stream; the timed call, which never splits), so the results
     and tile counts are the same bit for bit, and so is a HIP-graph replay
     (captured, the schedule stages on the side stream: split for the GQA
