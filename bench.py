@@ -424,10 +424,19 @@ def main():
         "traced_avg_us": traced_us,
         "traced_frac": (t["middle_flops_per_launch"] / (traced_us * 1e-6) / 1e12 / peak
                         if traced_us else None),
-        # the whole forward per launch, gaps between launches included
-        "event_forward_per_launch_ms": float(np.mean(ring["step_ms"])) / n_launch,
+        # the whole forward per block, gaps between launches included
+        "event_forward_per_block_ms": float(np.mean(ring["step_ms"])) / n_launch,
         "event_median_ms_per_step": float(np.median(ring["step_ms"])),
     }
+    if fast and not args.no_side_stream:
+        one_group = "<1," in roofline["kernel"]
+        chunked = one_group and case.n_cp >= 3
+        roofline["headline_schedule"] = (
+            ("chunk_kernel_fast: launches of two blocks after the first, " if chunked else
+             "step_kernel_fast: one launch per block, ") +
+            "each as two concurrent half grids (main and side stream), the next block(s) "
+            "staged on the copy stream; the kernel above runs the same per-tile code, timed "
+            "alone one launch per block by ra_forward_timed")
     # The bf16 MFMA rate the device sustains with the matrix pipe kept busy and
     # nothing else running: the clock it holds under that load sets it.
     ceil_tf, ceil_ms = ra.mfma_ceiling() if fast else (None, None)
