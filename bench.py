@@ -429,14 +429,23 @@ def main():
         "event_median_ms_per_step": float(np.median(ring["step_ms"])),
     }
     if fast and not args.no_side_stream:
-        one_group = "<1," in roofline["kernel"]
-        chunked = one_group and case.n_cp >= 3
+        n_q = len(share["q_pos"])
+        units = ((n_q + 127) // 128 + 1) // 2 * case.h_q
+        cus = props.multi_processor_count
+        if units >= 2 * cus:
+            sched = ("chunk_kernel_fast: launches of two blocks after the first, " if case.n_cp >= 3
+                     else "step_kernel_fast: one launch per block, ") + \
+                "each as two concurrent half grids (main and side stream)"
+        elif units >= cus:
+            sched = ("step_kernel_fast<1, ...>: two chains of full-grid launches, even blocks into "
+                     "one state on the main stream and odd blocks into another on the side stream, "
+                     "merged at the end")
+        else:
+            sched = ("step_kernel_fast: one launch per block, each as two concurrent half grids "
+                     "(main and side stream)")
         roofline["headline_schedule"] = (
-            ("chunk_kernel_fast: launches of two blocks after the first, " if chunked else
-             "step_kernel_fast: one launch per block, ") +
-            "each as two concurrent half grids (main and side stream), the next block(s) "
-            "staged on the copy stream; the kernel above runs the same per-tile code, timed "
-            "alone one launch per block by ra_forward_timed")
+            sched + "; the next block(s) staged on the copy stream; the kernel above runs the "
+            "same per-tile code, timed alone one launch per block by ra_forward_timed")
     # The bf16 MFMA rate the device sustains with the matrix pipe kept busy and
     # nothing else running: the clock it holds under that load sets it.
     ceil_tf, ceil_ms = ra.mfma_ceiling() if fast else (None, None)

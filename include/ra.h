@@ -109,10 +109,10 @@ ra_status ra_finalize(const ra_problem* p, const float* m, const float* l, const
                       float* out, float* lse, void* stream);
 
 /* Bytes of device workspace ra_forward needs: the running state and the
- * staging slots for incoming key/value blocks.  Two slots in general (the
- * ring's block being computed and the one arriving); four for bf16 with
- * d_k = 128, where with a side stream each launch after the first takes two
- * blocks and the next launch's two arrive meanwhile. */
+ * staging slots for incoming key/value blocks.  In general one state and two
+ * slots (the ring's block being computed and the one arriving); for bf16
+ * with d_k = 128 two states and four slots, for the schedules that read two
+ * blocks at a time while the next two arrive (see ra_forward). */
 size_t ra_forward_workspace_bytes(const ra_problem* p);
 
 /*
@@ -126,13 +126,22 @@ size_t ra_forward_workspace_bytes(const ra_problem* p);
  *  - side_stream NULL or equal to main_stream: everything on main_stream;
  *  - otherwise, shapes other than bf16 with d_k = 128: one launch per step
  *    on main_stream, copies on side_stream;
- *  - bf16, d_k = 128: each launch's work split in two halves, one on
- *    main_stream and one on side_stream, the copies on a stream the library
- *    creates once per device; launches after the first take two blocks each
- *    (n_cp >= 3, the state kept in registers between them, same bits as one
- *    launch per block).  While main_stream is being captured into a graph,
- *    one block per launch and the copies on side_stream (split only where
- *    the copy is short against a step).
+ *  - bf16, d_k = 128, copies on a stream the library creates once per
+ *    device, and by the number of work units (query-tile pairs x query
+ *    heads) against the device's compute units:
+ *    - at least two per compute unit: each launch's work split in two
+ *      halves, one on main_stream and one on side_stream; launches after the
+ *      first take two blocks each (n_cp >= 3, the state kept in registers
+ *      between them: the same bits as one launch per block);
+ *    - one to two: two chains, the even blocks folded into one running state
+ *      on main_stream and the odd blocks into a second one on side_stream,
+ *      merged into out and lse at the end (the online-softmax combination of
+ *      two partial states; rounding differs from one chain, tile counts do
+ *      not);
+ *    - fewer: each launch split in two halves as above, one block each.
+ *    While main_stream is being captured into a graph: one block per launch
+ *    and the copies on side_stream (split only where the copy is short
+ *    against a step).
  * out, lse: results.  work: optional device int64[3], zeroed and then filled
  * with the tile counts summed over all steps.  staged_bytes: optional host
  * pointer, receives the key/value bytes copied into staging slots

@@ -1035,8 +1035,10 @@ void allgather_split_kernel_fast(const MultiArgs ma, int n_split) {
 // writes the normalised out and lse: M = max_s m_s, L = sum_s l_s e^(m_s - M),
 // out = sum_s O_s e^(m_s - M) / L, lse = M + ln L.  A slot whose max is -inf
 // saw no key and is not read further.  Rows of tiles that were not split
-// already hold their result.  One wave per row, two columns a lane.
+// already hold their result (ALL: every row is merged, q_pos and q_lo unused).
+// One wave per row, two columns a lane.
 constexpr int MERGE_ROWS = 4;
+template <bool ALL>
 __global__ __launch_bounds__(64 * MERGE_ROWS)
 void merge_splits_kernel(const float* __restrict__ m, const float* __restrict__ l,
                          const float* __restrict__ o, const int32_t* __restrict__ q_pos,
@@ -1045,7 +1047,7 @@ void merge_splits_kernel(const float* __restrict__ m, const float* __restrict__ 
   const long long r = (long long)blockIdx.x * MERGE_ROWS + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= rows) return;
-  if (!split_tile(q_pos, q_lo, n_q, (int)(r % n_q) / ROWS)) return;
+  if (!ALL && !split_tile(q_pos, q_lo, n_q, (int)(r % n_q) / ROWS)) return;
   const float ms = lane < n_split ? m[lane * rows + r] : -INFINITY;
   float mx = ms;
 #pragma unroll
@@ -1078,9 +1080,19 @@ hipError_t launch_allgather_split_fast(const MultiArgs& ma, int n_split, hipStre
   const long long rows = (long long)ma.s.h_q * ma.s.n_q;
   dim3 mgrid((unsigned)((rows + fast::MERGE_ROWS - 1) / fast::MERGE_ROWS)),
       mblock(64 * fast::MERGE_ROWS);
-  hipLaunchKernelGGL(fast::merge_splits_kernel, mgrid, mblock, 0, stream, ma.s.m_out, ma.s.l_out,
-                     ma.s.o_out, ma.s.q_pos, ma.s.q_lo, ma.s.n_q, n_split, rows, ma.s.out,
-                     ma.s.lse);
+  hipLaunchKernelGGL(fast::merge_splits_kernel<false>, mgrid, mblock, 0, stream, ma.s.m_out,
+                     ma.s.l_out, ma.s.o_out, ma.s.q_pos, ma.s.q_lo, ma.s.n_q, n_split, rows,
+                     ma.s.out, ma.s.lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_states(const float* m, const float* l, const float* o, long long rows,
+                               int n_states, float* out, float* lse, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  dim3 mgrid((unsigned)((rows + fast::MERGE_ROWS - 1) / fast::MERGE_ROWS)),
+      mblock(64 * fast::MERGE_ROWS);
+  hipLaunchKernelGGL(fast::merge_splits_kernel<true>, mgrid, mblock, 0, stream, m, l, o, nullptr,
+                     nullptr, 0, n_states, rows, out, lse);
   return hipGetLastError();
 }
 
@@ -1106,6 +1118,14 @@ static int groups_for(long long units) {
 }
 
 int fast_groups_for(long long units) { return groups_for(units); }
+
+// Two chains of one-group launches (even blocks into one state, odd blocks
+// into another, on two streams) fill the chip where one chain of one-group
+// workgroups would leave a compute unit with a single one: at least one
+// work unit per compute unit, fewer than two.
+bool fast_two_chains(long long units) {
+  return groups_for(units) == 2 && groups_for(2 * units) == 1;
+}
 
 hipError_t launch_allgather_fast(const MultiArgs& ma, hipStream_t stream) {
   const int g = ma.s.q_lo != nullptr ? 2 : groups_for((long long)ma.s.n_pairs * ma.s.h_q);

@@ -197,19 +197,20 @@ ra_status launch(const ra_problem* p, const ra::StepArgs& a, bool read, bool fin
   return e == hipSuccess ? RA_OK : RA_ERR_HIP;
 }
 
-// Staging slots of ra_forward's workspace: four on the bf16 d_k = 128 path,
-// where the chunked schedule (two blocks per launch) stages the next
-// launch's two blocks while the current launch reads its own two; two
-// elsewhere and in the no-alloc form.
+// ra_forward's workspace on the bf16 d_k = 128 path: four staging slots
+// (the chunked schedule and the two-chain schedule read two blocks while the
+// next two arrive) and two running states (the two chains'); elsewhere, and
+// in the no-alloc form, two slots and one state.
 constexpr int kChunkSlots = 4;
 
 struct WsLayout {
   size_t m, l, o, slot[kChunkSlots], kbytes, pbytes, total;
 };
 
-WsLayout ws_layout(const ra_problem* p, int n_slots = 2) {
+// State s lives at m + s rows, l + s rows, o + s rows * d_k (floats).
+WsLayout ws_layout(const ra_problem* p, int n_slots, int n_states) {
   WsLayout w;
-  const size_t rows = (size_t)p->h_q * p->n_q;
+  const size_t rows = (size_t)p->h_q * p->n_q * n_states;
   w.kbytes = (size_t)p->h_kv * p->n_k * p->d_k * elem_bytes(p->dtype);
   w.pbytes = (size_t)p->n_k * sizeof(int32_t);
   size_t off = 0;
@@ -406,7 +407,7 @@ ra_status ra_finalize(const ra_problem* p, const float* m, const float* l, const
 
 size_t ra_forward_workspace_bytes(const ra_problem* p) {
   if (check_problem(p) != RA_OK) return 0;
-  return ws_layout(p, fast_path(p) ? kChunkSlots : 2).total;
+  return fast_path(p) ? ws_layout(p, kChunkSlots, 2).total : ws_layout(p, 2, 1).total;
 }
 
 ra_status ra_forward(const ra_problem* p, int32_t n_cp, const void* q, const int32_t* q_pos,
@@ -446,7 +447,10 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
   if (st != RA_OK) return st;
   if (n_cp < 1) return RA_ERR_SHAPE;
   if (!k_blocks || !v_blocks || !k_pos_blocks) return RA_ERR_NULL;
-  const WsLayout w2 = ws_layout(p, 2);
+  // ra_forward's layout is what ra_forward_workspace_bytes reports; the
+  // no-alloc form (fixed events: one launch per block) has two slots and one
+  // state.
+  const WsLayout w = fixed || !fast_path(p) ? ws_layout(p, 2, 1) : ws_layout(p, kChunkSlots, 2);
   if (p->n_q > 0) {
     if (!q || !q_pos || !out || !lse) return RA_ERR_NULL;
     if (!aligned16(q) || !aligned4(q_pos) || !aligned16(out) || !aligned4(lse))
@@ -462,10 +466,7 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
   }
   if (!workspace) return RA_ERR_NULL;
   if (!aligned16(workspace)) return RA_ERR_ALIGN;
-  // ra_forward asks for what ra_forward_workspace_bytes reports; the no-alloc
-  // form (fixed events, never chunked) for the two-slot layout only.
-  if (ws_bytes < (fixed ? w2.total : ws_layout(p, fast_path(p) ? kChunkSlots : 2).total))
-    return RA_ERR_WORKSPACE;
+  if (ws_bytes < w.total) return RA_ERR_WORKSPACE;
   if (launch_events)
     for (int i = 0; i < 2 * n_cp; ++i)
       if (!launch_events[i]) return RA_ERR_NULL;
@@ -481,9 +482,9 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
   hipStream_t ss = (hipStream_t)side_stream;
   const bool use_side = ss != nullptr && ss != ms;
   char* ws = (char*)workspace;
-  float* m = (float*)(ws + w2.m);
-  float* l = (float*)(ws + w2.l);
-  float* o = (float*)(ws + w2.o);
+  float* m = (float*)(ws + w.m);
+  float* l = (float*)(ws + w.l);
+  float* o = (float*)(ws + w.o);
 
   if (staged_bytes) *staged_bytes = 0;
   if (!mark(staged_events, 0, ms)) return RA_ERR_HIP;
@@ -540,9 +541,15 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
   // ...) with the state in registers between them; block b >= 1 is staged
   // into slot (b - 1) % 4.
   const bool chunked = three && split_groups == 1 && n_cp >= 3;
-  const WsLayout w = ws_layout(p, chunked ? kChunkSlots : 2);
-  const int n_slots = chunked ? kChunkSlots : 2;
-  auto slot_of = [&](int b) { return chunked ? (b - 1) % kChunkSlots : b & 1; };
+  // Two chains: with the copy stream, where one chain of one-group launches
+  // would leave compute units with a single workgroup (one to two work units
+  // per compute unit), even blocks fold into state 0 on the main stream and
+  // odd blocks into state 1 on the side stream, one full-grid one-group
+  // launch per block, and a merge of the two states writes out and lse.
+  // Rounding differs from one chain; tile counts do not.
+  const bool chains = three && ra::fast_two_chains((int64_t)a.n_pairs * a.h_q);
+  const int n_slots = chunked || chains ? kChunkSlots : 2;
+  auto slot_of = [&](int b) { return n_slots == kChunkSlots ? (b - 1) % kChunkSlots : b & 1; };
   // The events only order work between two streams of this device; the copy
   // kernels' completion and the step kernels' launch carry their own memory
   // fences, so the events skip the system-scope fence (a cache writeback and
@@ -558,7 +565,7 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
     char* slot = ws + w.slot[s];
     if (use_side && b - n_slots >= 1 &&
         (hipStreamWaitEvent(dst, ev_used[s], 0) != hipSuccess ||
-         (three && hipStreamWaitEvent(dst, ev_used2[s], 0) != hipSuccess)))
+         (three && !chains && hipStreamWaitEvent(dst, ev_used2[s], 0) != hipSuccess)))
       return false;
     if (w.kbytes &&
         (hipMemcpyAsync(slot, k_blocks[b], w.kbytes, hipMemcpyDeviceToDevice, dst) != hipSuccess ||
@@ -664,6 +671,49 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
         }
       }
     }
+  } else if (chains) {
+    // block b on the main stream into state 0 (b even) or on the side stream
+    // into state 1 (b odd); block b + 2 staged on the copy stream meanwhile
+    const size_t rows = (size_t)p->h_q * p->n_q;
+    ra::StepArgs c = a;
+    c.groups = 1;
+    if (!stage(1, cs)) {
+      result = RA_ERR_HIP;
+      goto cleanup;
+    }
+    for (int b = 0; b < n_cp; ++b) {
+      hipStream_t st = (b & 1) ? ss : ms;
+      const size_t sidx = b & 1;
+      c.m_in = c.m_out = m + sidx * rows;
+      c.l_in = c.l_out = l + sidx * rows;
+      c.o_in = c.o_out = o + sidx * rows * p->d_k;
+      if (b == 0) {
+        c.k = k_blocks[0];
+        c.v = v_blocks[0];
+        c.k_pos = k_pos_blocks[0];
+      } else {
+        const int sl = slot_of(b);
+        if (hipStreamWaitEvent(st, ev_staged[sl], 0) != hipSuccess) {
+          result = RA_ERR_HIP;
+          goto cleanup;
+        }
+        char* slot = ws + w.slot[sl];
+        c.k = slot;
+        c.v = slot + align_up(w.kbytes);
+        c.k_pos = (const int32_t*)(slot + 2 * align_up(w.kbytes));
+      }
+      result = launch(p, c, /*read=*/b >= 2, /*final=*/false, st);
+      if (result != RA_OK) goto cleanup;
+      // the slot is free for block b + 4 once this launch is done
+      if (b >= 1 && b + n_slots < n_cp && hipEventRecord(ev_used[slot_of(b)], st) != hipSuccess) {
+        result = RA_ERR_HIP;
+        goto cleanup;
+      }
+      if (b + 2 < n_cp && !stage(b + 2, cs)) {
+        result = RA_ERR_HIP;
+        goto cleanup;
+      }
+    }
   } else
   for (int b = 0; b < n_cp; ++b) {
     const bool first = b == 0, last = b == n_cp - 1;
@@ -723,6 +773,13 @@ ra_status ra::forward_ring(const ra_problem* p, int32_t n_cp, const void* q, con
   }
   if (split && (hipEventRecord(ev_join, ss) != hipSuccess ||
                 hipStreamWaitEvent(ms, ev_join, 0) != hipSuccess)) {
+    result = RA_ERR_HIP;
+    goto cleanup;
+  }
+  // the two chains' states merged into out and lse (the online-softmax
+  // combination of two partial states)
+  if (chains && ra::launch_merge_states(m, l, o, (long long)p->h_q * p->n_q, 2, out, lse, ms) !=
+                    hipSuccess) {
     result = RA_ERR_HIP;
     goto cleanup;
   }

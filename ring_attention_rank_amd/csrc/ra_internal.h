@@ -84,12 +84,20 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d_k, bool read, bool fi
 // bfloat16, d_k = 128, one group per workgroup: ma.n_blocks (1 or 2)
 // consecutive ring blocks in one launch, the units of ma.s (unit0, n_units).
 hipError_t launch_chunk_fast(const MultiArgs& ma, bool read, bool final_, hipStream_t stream);
+// Merges n_states partial states (state s at m + s rows, l + s rows,
+// o + s rows * d_k; bf16 d_k = 128 layout) into out and lse.
+hipError_t launch_merge_states(const float* m, const float* l, const float* o, long long rows,
+                               int n_states, float* out, float* lse, hipStream_t stream);
 // bfloat16, d_k = 128: the 8-wave kernel with direct-to-LDS staging.
 hipError_t launch_step_fast(const StepArgs& a, bool read, bool final_, hipStream_t stream,
                             hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // Groups of 4 waves per workgroup the bf16 d_k 128 kernels use for a launch
 // of `units` work units on the current device (1 or 2).
 int fast_groups_for(long long units);
+// Whether the ring runs as two chains of one-group launches (even and odd
+// blocks into two states, merged at the end): one to two work units per
+// compute unit.
+bool fast_two_chains(long long units);
 // Backward of one key/value block (bfloat16, d_k = 128): dq, dk and dv
 // (fp32) each get this block's part added (dk, dv summed over the query heads
 // of each key/value head).

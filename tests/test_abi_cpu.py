@@ -78,11 +78,11 @@ def test_tile_shape_and_workspace():
     p = good()
     assert ra.tile_shape(p) == (32, 64)
     n = ra.workspace_bytes(p)
-    # state (m, l, o in fp32) + 4 slots of K, V (bf16) and positions (two
-    # blocks per launch, the next two arriving)
+    # 2 states (m, l, o in fp32: the two chains') + 4 slots of K, V (bf16)
+    # and positions (two blocks read, the next two arriving)
     state = 4 * 256 * 4 * 2 + 4 * 256 * 128 * 4
     slots = 4 * (2 * 2 * 256 * 128 * 2 + 256 * 4)
-    assert state + slots <= n <= state + slots + 16 * 256
+    assert 2 * state + slots <= n <= 2 * state + slots + 16 * 256
     # other shapes: 2 slots (fp32 K, V)
     nf = ra.workspace_bytes(good(dtype=ra.RA_F32))
     fslots = 2 * (2 * 2 * 256 * 128 * 4 + 256 * 4)
