@@ -33,15 +33,19 @@
 // with the LDS operand reads a few MFMAs ahead of their use.
 //
 // This unit: the dq kernel and delta = rowsum(dout * out).  A workgroup of
-// 8 waves owns 128 query rows; on each SIMD
-//  * the P wave (q in registers): S^T_j = K_j q^T, p = exp(scale s - lse)
-//    under the mask, written to LDS in fp32;
+// 8 waves owns 128 query rows; on each SIMD, with the tile's 64 keys in two
+// halves of 32,
+//  * the P wave (q and dout in registers): S^T_j = K_j q^T, p = exp(scale s
+//    - lse) under the mask; p of key half 0 to LDS in fp32; for key half 1
+//    also dP^T = V_j dout^T and dS^T = p (dP^T - delta), to LDS in bf16;
 //  * the dS wave (dout and the dQ accumulator in registers): with the p of
-//    tile j - 1 from LDS, dS^T = p (dP^T - delta) and dQ^T += K_{j-1}^T dS^T,
-//    then dP^T_j = V_j dout^T for the next step.
-// One barrier per step; K has three stages (j - 1, j, and j + 1 landing),
-// V two, p two.  The MFMA accumulators live in ordinary VGPRs (built with
-// the VGPR form), so the VALU work reads them without moves.
+//    tile j - 1's key half 0 from LDS, its dS^T from the dP^T it computed the
+//    step before, and key half 1's dS^T from LDS, dQ^T += K_{j-1}^T dS^T;
+//    then dP^T_j of key half 0 for the next step.
+// Each wave issues 24 of the 48 MFMAs of a tile.  One barrier per step; K
+// has three stages (j - 1, j, and j + 1 landing), V two, p and dS two.  The
+// MFMA accumulators live in ordinary VGPRs (built with the VGPR form), so the
+// VALU work reads them without moves.
 #include "ra_bwd_common.h"
 
 namespace ra {
@@ -52,9 +56,12 @@ constexpr int Q_THREADS = 512;
 struct __attribute__((aligned(1024))) SmemQ {
   uint8_t k[3][TILE_BYTES];  // K tiles, one copy each (uswz layout): rows for S^T, transposed for dQ^T
   uint8_t v[2][TILE_BYTES];  // V tiles: rows for dP^T
-  // p of a tile, per wave pair, half, register group and lane: the P wave's
-  // S^T accumulator layout, which is the dS wave's dP^T layout too
-  f32x4 p[2][4][2][4][64];
+  // p of a tile's key half 0, per wave pair, register group and lane: the P
+  // wave's S^T accumulator layout, which is the dS wave's dP^T layout too
+  f32x4 p[2][4][4][64];
+  // dS^T of a tile's key half 1 in bf16, per wave pair, as the two B
+  // operands of the dQ^T product (registers 0-7 and 8-15 of the layout)
+  bf16x8 ds[2][4][2][64];
   int32_t pos[3][TILE];  // key positions as stored (keys past the block read as 0)
 };
 
@@ -81,12 +88,19 @@ void dq_kernel(const BwdArgs a) {
   const bool rv = row < n_q;
   const size_t srow = (size_t)head * n_q + row;
 
-  // q (P wave) or dout (dS wave) in registers: the B operand of S^T or dP^T
+  // q (P wave) or dout (dS wave) in registers: the B operand of S^T or dP^T;
+  // the P wave also holds dout for its half of dP^T
   const uint16_t* src = (const uint16_t*)(pw ? a.q : a.dout) + ((size_t)head * n_q) * D;
-  bf16x8 qg[8];
+  const uint16_t* gsrc = (const uint16_t*)a.dout + ((size_t)head * n_q) * D;
+  bf16x8 qg[8], dg[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks)
     qg[ks] = rv ? *(const bf16x8*)(src + (size_t)row * D + ks * 16 + L.h * 8) : bf16x8{};
+  if (pw) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      dg[ks] = rv ? *(const bf16x8*)(gsrc + (size_t)row * D + ks * 16 + L.h * 8) : bf16x8{};
+  }
   // rows past n_q and rows that saw no key at all have lse = -inf: p = 0
   const float lse2 = rv ? a.lse[srow] * kLog2e : -INFINITY;
   const bool seen = lse2 != -INFINITY;
@@ -142,7 +156,8 @@ void dq_kernel(const BwdArgs a) {
   };
 
   f32x16 acc[4] = {};  // dQ^T (dS wave)
-  f32x16 sp[2];        // S^T (P wave) or dP^T (dS wave) of a tile's two 32-key halves
+  f32x16 sp[2];        // S^T of a tile's two 32-key halves (P wave); dP^T of half 0 (dS wave)
+  f32x16 dp1;          // dP^T of key half 1 (P wave)
   bf16x8 op[16], tr[16];
   if (n_iter > 0) {
     dma_tile(0);
@@ -166,11 +181,27 @@ void dq_kernel(const BwdArgs a) {
     }
   };
 
-  // ---- the P wave: p of tile j into p slot j & 1
+  // 8 MFMAs out += (rows of X, key half kb) x B; hook(n) after MFMA n
+  auto half_mfma = [&](const uint8_t* X, int kb, const bf16x8(&B)[8], f32x16& out, auto hook) {
+    out = f32x16{};
+#pragma unroll
+    for (int n = 0; n < Q_AHEAD; ++n) op[n] = row_operand1(X, L, kb, n);
+    RA_FENCE();
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      out = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[n], B[n], out, 0, 0, 0);
+      if (n + Q_AHEAD < 8) op[n + Q_AHEAD] = row_operand1(X, L, kb, n + Q_AHEAD);
+      hook(n);
+      RA_FENCE();
+    }
+  };
+
+  // ---- the P wave: p of tile j's key half 0 into p slot j & 1, dS^T of
+  // its key half 1 into dS slot j & 1
   auto p_step = [&](int j, auto masked) {
     constexpr bool M = decltype(masked)::value;
     const int32_t* pos = sm.pos[j % 3];
-    f32x4* pb = &sm.p[j & 1][pair][0][0][lane];  // [half][group] stride 64
+    f32x4* pb = &sm.p[j & 1][pair][0][lane];  // [group] stride 64
     auto pgroup = [&](int kb, int g) {
       f32x4 pv;
 #pragma unroll
@@ -186,42 +217,48 @@ void dq_kernel(const BwdArgs a) {
         }
         pv[e] = p;
       }
-      pb[64 * (4 * kb + g)] = pv;
+      return pv;
     };
     __builtin_amdgcn_s_setprio(1);  // its MFMAs first: the dS wave's fill its exponential tail
     rows_mfma(sm.k[j % 3], [&](int n) {
-      if (n >= 8 && (n & 1)) pgroup(0, (n - 8) >> 1);
+      if (n >= 8 && (n & 1)) pb[64 * ((n - 8) >> 1)] = pgroup(0, (n - 8) >> 1);
     });
     __builtin_amdgcn_s_setprio(0);
+    // key half 1: dP^T beside its exponentials, then dS^T
+    f32x4 p1[4];
+    half_mfma(sm.v[j & 1], 1, dg, dp1, [&](int n) {
+      if (n & 1) p1[n >> 1] = pgroup(1, n >> 1);
+    });
+    bf16x8 d1[2];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) pgroup(1, g);
+    for (int r = 0; r < 16; ++r) d1[r >> 3][r & 7] = (__bf16)(p1[r >> 2][r & 3] * (dp1[r] - delta));
+    sm.ds[j & 1][pair][0][lane] = d1[0];
+    sm.ds[j & 1][pair][1][lane] = d1[1];
   };
 
-  // ---- the dS wave: dS and dQ of tile j - 1 (its dP^T in sp), then dP^T of
-  // tile j
+  // ---- the dS wave: dS and dQ of tile j - 1 (its key half 0's dP^T in
+  // sp[0], key half 1's dS^T from the P wave), then dP^T of tile j's key
+  // half 0
   auto ds_step = [&](int j) {
     if (j > 0) {
       const int jp = j - 1;
-      const f32x4* pb = &sm.p[jp & 1][pair][0][0][lane];
+      const f32x4* pb = &sm.p[jp & 1][pair][0][lane];
       const uint8_t* K = sm.k[jp % 3];
       bf16x8 ds[2][2];
       f32x4 pv[4];
       // dQ^T MFMA n: half n / 8, i = n % 8: d block i % 4, key group i / 4
       auto rd_t = [&](int n) { tr[n] = tr_operand1(K, L, n >> 3, (n & 7) >> 2, n & 3); };
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int g = 0; g < 4; ++g) pv[g] = pb[64 * g];
+      ds[1][0] = sm.ds[jp & 1][pair][0][lane];
+      ds[1][1] = sm.ds[jp & 1][pair][1][lane];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) pv[g] = pb[64 * (4 * kb + g)];
-        if (kb == 0) {
+      for (int n = 0; n < Q_AHEAD; ++n) rd_t(n);
+      RA_FENCE();
 #pragma unroll
-          for (int n = 0; n < Q_AHEAD; ++n) rd_t(n);
-        }
-        RA_FENCE();
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          ds[kb][r >> 3][r & 7] = (__bf16)(pv[r >> 2][r & 3] * (sp[kb][r] - delta));
-        RA_FENCE();
-      }
+      for (int r = 0; r < 16; ++r)
+        ds[0][r >> 3][r & 7] = (__bf16)(pv[r >> 2][r & 3] * (sp[0][r] - delta));
+      RA_FENCE();
 #pragma unroll
       for (int n = 0; n < 16; ++n) {
         const int i = n & 7;
@@ -231,7 +268,7 @@ void dq_kernel(const BwdArgs a) {
         RA_FENCE();
       }
     }
-    if (j < n_iter) rows_mfma(sm.v[j & 1], [](int) {});
+    if (j < n_iter) half_mfma(sm.v[j & 1], 0, qg, sp[0], [](int) {});
   };
 
   // Each role runs its own copy of the loop (the same barriers in the same
@@ -255,7 +292,7 @@ void dq_kernel(const BwdArgs a) {
         ds_step(j);
       }
       __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's part of tile j + 1 landed
-      __syncthreads();  // tile j + 1 and p_j are in place; stages of j - 2 are free
+      __syncthreads();  // tile j + 1, p_j and dS_j are in place; stages of j - 2 are free
     }
   };
   if (pw)
