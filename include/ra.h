@@ -202,8 +202,11 @@ ra_status ra_forward_noalloc(const ra_problem* p, int32_t n_cp, const void* q,
                              float* out, float* lse, int64_t* work, int64_t* staged_bytes,
                              void* main_stream, void* side_stream);
 
-/* Bytes of device workspace ra_forward_allgather needs: 0 for bfloat16 with
- * d_k = 128 (the state stays in registers), else the running state (m, l, o). */
+/* Bytes of device workspace ra_forward_allgather needs.  bfloat16 with
+ * d_k = 128: 0 (the state stays in registers), except where the launch has
+ * one to two work units (query-tile pairs x query heads) per compute unit of
+ * the current device: two partial states (m, l, o) for the two chains (see
+ * ra_forward_allgather).  Other shapes: the running state (m, l, o). */
 size_t ra_forward_allgather_workspace_bytes(const ra_problem* p);
 
 /*
@@ -214,11 +217,17 @@ size_t ra_forward_allgather_workspace_bytes(const ra_problem* p);
  * contrasts it with the ring: same bytes, all moved first, full K and V
  * held).  All n_cp blocks are resident: k_blocks, v_blocks, k_pos_blocks are
  * HOST arrays of n_cp device pointers, 1 <= n_cp <= 64; the result does not
- * depend on their order.  bfloat16 with d_k = 128 runs one launch that folds
- * every block into a register-resident state and writes out/lse; other shapes
- * run one step launch per block against the state kept in the workspace
- * (ra_forward_allgather_workspace_bytes; workspace may be NULL when that is 0).
- * out, lse and work as in ra_forward.  Asynchronous on stream.
+ * depend on their order beyond rounding.  bfloat16 with d_k = 128 runs one
+ * launch that folds every block into a register-resident state and writes
+ * out/lse; with one to two work units per compute unit and n_cp >= 2 it runs
+ * two such launches side by side instead, the even blocks on stream and the
+ * odd blocks on a stream the library creates once per device, each into a
+ * partial state in the workspace, merged into out/lse on stream (one launch
+ * while stream is being captured into a graph).  Other shapes run one step
+ * launch per block against the state kept in the workspace.  The workspace
+ * holds ra_forward_allgather_workspace_bytes(p) bytes (it may be NULL when
+ * that is 0).  out, lse and work as in ra_forward.  Asynchronous on stream:
+ * work after the call on stream sees the results.
  */
 ra_status ra_forward_allgather(const ra_problem* p, int32_t n_cp, const void* q,
                                const int32_t* q_pos, const void* const* k_blocks,

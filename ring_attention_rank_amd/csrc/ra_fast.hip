@@ -988,6 +988,28 @@ void allgather_kernel_fast(const MultiArgs ma) {
   }
 }
 
+// Two chains of the all-gather form: one-group workgroups fold the blocks
+// in `ma` (one parity of the block list) into partial state `chain` of the
+// state arrays (chain x h_q x n_q rows in), which merge_splits_kernel<true>
+// combines after both chains; the two launches run side by side, two
+// workgroups to a compute unit.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void allgather_chain_kernel_fast(const MultiArgs ma, int chain) {
+  __shared__ Smem<1> sm;
+  const int tid = threadIdx.x;
+  const int u = blockIdx.x;
+  const int head = ma.s.head_of[u % ma.s.h_q];
+  const int p = u / ma.s.h_q;
+  const int t_hi = ma.s.n_qt - 1 - p, t_lo = p;
+  Step<1, false, false> s(ma.s, sm, tid);
+  s.slot_rows = (size_t)chain * ma.s.h_q * ma.s.n_q;
+  s.run_all(ma, t_hi, head);
+  if (t_lo < t_hi) {
+    __syncthreads();
+    s.run_all(ma, t_lo, head);
+  }
+}
+
 // The same under a document mask with the key blocks split over n_split
 // workgroups per query tile pair.  A tile whose rows see a long span of
 // positions (late rows of a long document) is split: split s folds the blocks
@@ -1136,6 +1158,12 @@ hipError_t launch_allgather_fast(const MultiArgs& ma, hipStream_t stream) {
     hipLaunchKernelGGL((fast::allgather_kernel_fast<1, false>), grid, block, 0, stream, ma);
   else
     hipLaunchKernelGGL((fast::allgather_kernel_fast<2, false>), grid, block, 0, stream, ma);
+  return hipGetLastError();
+}
+
+hipError_t launch_allgather_chain_fast(const MultiArgs& ma, int chain, hipStream_t stream) {
+  dim3 grid((unsigned)(ma.s.n_pairs * ma.s.h_q)), block(256);
+  hipLaunchKernelGGL(fast::allgather_chain_kernel_fast, grid, block, 0, stream, ma, chain);
   return hipGetLastError();
 }
 

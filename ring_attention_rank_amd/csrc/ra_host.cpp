@@ -134,11 +134,6 @@ hipStream_t copy_stream() {
 }
 
 // State (m, l, o) of the per-block fallback of ra_forward_allgather.
-size_t allgather_ws_bytes(const ra_problem* p) {
-  if (fast_path(p)) return 0;
-  const size_t rows = (size_t)p->h_q * p->n_q;
-  return 2 * align_up(rows * 4) + align_up(rows * p->d_k * 4);
-}
 
 // Key-block splits of the document-masked all-gather.  A launch of fewer than
 // kSplitBelow workgroups (4 per compute unit) is split into enough of them to
@@ -171,9 +166,26 @@ SplitLayout split_layout(const ra_problem* p, int n_split) {
   return w;
 }
 
+// Whether the bf16 d_k = 128 all-gather form of this problem runs as two
+// chains (one to two work units per compute unit of the current device; the
+// ring's rule): the even blocks and the odd blocks folded by two one-group
+// launches side by side into two partial states, then merged.
+bool allgather_chains(const ra_problem* p) {
+  if (!fast_path(p) || p->n_q == 0 || p->n_k == 0) return false;
+  const int64_t n_qt = (p->n_q + ra::kRowsPerGroup - 1) / ra::kRowsPerGroup;
+  return ra::fast_two_chains((n_qt + 1) / 2 * p->h_q);
+}
+
+size_t allgather_ws_bytes(const ra_problem* p) {
+  if (fast_path(p)) return allgather_chains(p) ? split_layout(p, 2).total : 0;
+  const size_t rows = (size_t)p->h_q * p->n_q;
+  return 2 * align_up(rows * 4) + align_up(rows * p->d_k * 4);
+}
+
 size_t docs_ws_bytes(const ra_problem* p, int32_t n_cp) {
   const int n_split = docs_splits(p, n_cp);
-  return n_split > 1 ? split_layout(p, n_split).total : allgather_ws_bytes(p);
+  if (n_split > 1) return split_layout(p, n_split).total;
+  return fast_path(p) ? 0 : allgather_ws_bytes(p);  // one launch: no chains under the mask
 }
 
 ra_status fill_args(const ra_problem* p, ra::StepArgs* a) {
@@ -294,6 +306,49 @@ ra_status allgather_impl(const ra_problem* p, int32_t n_cp, const void* q, const
       ma.s.l_out = (float*)(ws + w.l);
       ma.s.o_out = (float*)(ws + w.o);
       return ra::launch_allgather_split_fast(ma, n_split, s) == hipSuccess ? RA_OK : RA_ERR_HIP;
+    }
+    // Two chains (see allgather_chains): the even blocks on the caller's
+    // stream, the odd blocks on the library's copy stream, into the two
+    // states of the workspace; then the merge on the caller's stream.  Under
+    // graph capture (or if the capture state or that stream is not
+    // available) one launch instead.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipStream_t cs = nullptr;
+    if (!q_lo && n_cp >= 2 && allgather_chains(p) &&
+        hipStreamIsCapturing(s, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone &&
+        (cs = copy_stream()) != nullptr) {
+      const SplitLayout w = split_layout(p, 2);
+      char* ws = (char*)workspace;
+      ma.s.m_out = (float*)ws;
+      ma.s.l_out = (float*)(ws + w.l);
+      ma.s.o_out = (float*)(ws + w.o);
+      ra::MultiArgs half[2] = {ma, ma};
+      for (int c = 0; c < 2; ++c) {
+        half[c].n_blocks = 0;
+        for (int b = c; b < n_cp; b += 2) {
+          const int i = half[c].n_blocks++;
+          half[c].k[i] = k_blocks[b];
+          half[c].v[i] = v_blocks[b];
+          half[c].k_pos[i] = k_pos_blocks[b];
+        }
+      }
+      hipEvent_t fork = nullptr, join = nullptr;
+      auto mk = [](hipEvent_t* e) {
+        return hipEventCreateWithFlags(e, hipEventDisableTiming | hipEventDisableSystemFence) ==
+               hipSuccess;
+      };
+      ra_status r = RA_ERR_HIP;
+      if (mk(&fork) && mk(&join) && hipEventRecord(fork, s) == hipSuccess &&
+          hipStreamWaitEvent(cs, fork, 0) == hipSuccess &&
+          ra::launch_allgather_chain_fast(half[0], 0, s) == hipSuccess &&
+          ra::launch_allgather_chain_fast(half[1], 1, cs) == hipSuccess &&
+          hipEventRecord(join, cs) == hipSuccess && hipStreamWaitEvent(s, join, 0) == hipSuccess &&
+          ra::launch_merge_states(ma.s.m_out, ma.s.l_out, ma.s.o_out,
+                                  (long long)p->h_q * p->n_q, 2, out, lse, s) == hipSuccess)
+        r = RA_OK;
+      if (fork) (void)hipEventDestroy(fork);  // the call's status is already decided
+      if (join) (void)hipEventDestroy(join);
+      return r;
     }
     return ra::launch_allgather_fast(ma, s) == hipSuccess ? RA_OK : RA_ERR_HIP;
   }

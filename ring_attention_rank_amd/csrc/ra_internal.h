@@ -84,6 +84,10 @@ hipError_t launch_step(const StepArgs& a, int dtype, int d_k, bool read, bool fi
 // bfloat16, d_k = 128, one group per workgroup: ma.n_blocks (1 or 2)
 // consecutive ring blocks in one launch, the units of ma.s (unit0, n_units).
 hipError_t launch_chunk_fast(const MultiArgs& ma, bool read, bool final_, hipStream_t stream);
+// One chain of the two-chain all-gather: the blocks in ma folded by one-group
+// workgroups into partial state `chain` (ma.s.m_out / l_out / o_out hold two
+// states, state s at s x h_q x n_q rows in).
+hipError_t launch_allgather_chain_fast(const MultiArgs& ma, int chain, hipStream_t stream);
 // Merges n_states partial states (state s at m + s rows, l + s rows,
 // o + s rows * d_k; bf16 d_k = 128 layout) into out and lse.
 hipError_t launch_merge_states(const float* m, const float* l, const float* o, long long rows,

@@ -195,6 +195,11 @@ def test_allgather_checks():
     odd = (ctypes.c_void_p * 2)(FAKE, FAKE + 8)
     assert L.ra_forward_allgather(ctypes.byref(p), 2, v, v, odd, arr, arr, None, 0, v, v,
                                   None, None) == ALIGN
+    # one to two work units per compute unit (256 on a device with 256
+    # compute units, the count assumed without a device): two partial states
+    # for the two chains
+    pc = good(n_q=2048, h_q=32, h_kv=8)
+    assert ra.allgather_workspace_bytes(pc) >= 2 * (32 * 2048 * 4 * 2 + 32 * 2048 * 128 * 4)
     # other shapes keep the running state in the workspace
     pf = ra.problem(256, 256, 4, 2, 64, torch.float32)
     need = ra.allgather_workspace_bytes(pf)

@@ -1,7 +1,8 @@
 """Parity of the all-gather form (ra_forward_allgather: every key/value block
-resident, one launch for bf16 d_k = 128) with the float64 oracle: element by
-element at reduced sizes, sampled rows at full size, tile counters bit exact,
-the result independent of the block order."""
+resident, one launch for bf16 d_k = 128, or two side by side where a launch
+has one to two work units per compute unit) with the float64 oracle: element
+by element at reduced sizes, sampled rows at full size, tile counters bit
+exact, the result independent of the block order."""
 
 import numpy as np
 import pytest
@@ -71,7 +72,26 @@ def test_matches_ring_and_is_order_independent():
     assert list(a_work) == list(b_work) == list(r_work.cpu().numpy())
 
 
-@pytest.mark.parametrize("name", ["llama405b_stage_share", "million_striped_mha"])
+@pytest.mark.parametrize("n_q,n_k,n_cp", [(2000, 300, 7), (2048, 256, 2)])
+def test_two_chains(n_q, n_k, n_cp):
+    """One to two work units per compute unit: two one-group launches side by
+    side (even and odd blocks, two partial states in the workspace, merged at
+    the end), against the oracle, tile counts exact, and within the bound of
+    the same blocks in another order."""
+    rng = np.random.default_rng(3 * n_q + n_cp)
+    sh = _custom_share(rng, "bf16", 128, 32, 8, n_q, n_k, n_cp)
+    p = ra.problem(n_q, n_k, 32, 8, 128, torch.bfloat16)
+    assert ra.allgather_workspace_bytes(p) > 0  # the two partial states
+    check(sh, f"two chains nq{n_q} nk{n_k} ncp{n_cp}")
+    a = run_allgather(sh)
+    b = run_allgather(sh, order=list(reversed(range(n_cp))))
+    compare(a[0], a[1], b[0].astype(np.float64), b[1].astype(np.float64), TOL["bf16"],
+            "two chains, blocks reversed")
+    assert list(a[2]) == list(b[2])
+
+
+@pytest.mark.parametrize("name", ["llama405b_stage_share", "llama70b_stage_share",
+                                  "million_striped_mha"])
 def test_full_size_sampled(name):
     case = synth.case_by_name(name)
     sh = Share(case, 0).to_gpu()

@@ -31,8 +31,9 @@ pytestmark = [pytest.mark.gpu,
 def digests(full=False):
     """Hashes of the forward's out and lse and of the backward's dq, dk, dv
     for a reduced 70B stage share (16 blocks of 1024 keys, 8 q / 1 kv heads),
-    or for the full one (16 blocks of 8192 keys: the forward as two chains of
-    launches on two streams, merged at the end)."""
+    or for the full one (16 blocks of 8192 keys: the ring forward and the
+    all-gather form as two chains of launches on two streams, merged at the
+    end)."""
     sh = (Share(synth.case_by_name("llama70b_stage_share"), 0).to_gpu() if full else
           Share(synth.case_by_name("llama70b_stage_share"), 0, T=16384, n_cp=16).to_gpu())
     fwd = ra.Forward(sh.gq, sh.gq_pos, sh.gk, sh.gv, sh.gk_pos)
@@ -43,7 +44,12 @@ def digests(full=False):
     dq, dks, dvs = bwd(out, lse, dout)
     torch.cuda.synchronize()
     h = lambda ts: hashlib.sha256(b"".join(t.cpu().numpy().tobytes() for t in ts)).hexdigest()
-    return {"out": h([out]), "lse": h([lse]), "dq": h([dq]), "dk": h(dks), "dv": h(dvs)}
+    res = {"out": h([out]), "lse": h([lse]), "dq": h([dq]), "dk": h(dks), "dv": h(dvs)}
+    if full:  # the all-gather form as two chains on two streams
+        ao, al, _ = ra.forward_allgather(sh.gq, sh.gq_pos, sh.gk, sh.gv, sh.gk_pos)
+        torch.cuda.synchronize()
+        res["allgather"] = h([ao, al])
+    return res
 
 
 @pytest.mark.parametrize("full", [False, True])
