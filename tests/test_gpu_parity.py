@@ -158,6 +158,29 @@ def test_two_chain_schedule(n_q, n_k, n_cp):
             "two chains against one stream")
 
 
+def test_two_chain_edge_cases():
+    """Two-chain shapes where a chain sees nothing: the odd blocks wholly
+    after every query (state 1 stays empty, m = -inf, and the merge returns
+    state 0's result), and blocks with no keys at all (both states empty:
+    out = 0, lse = -inf)."""
+    rng = np.random.default_rng(404)
+    sh = _custom_share(rng, "bf16", 128, 32, 8, 2048, 256, 4)
+    assert _chains(32, 2048)
+    future = int(sh.q_pos.max()) + 1
+    for b in (1, 3):
+        sh.k_pos[b] = np.arange(future, future + 256, dtype=np.int64) + 1000 * b
+    sh = sh.to_gpu()
+    check_share(sh, "two chains, odd blocks in the future")
+    d = 128
+    q = sh.gq
+    ek = torch.empty((8, 0, d), dtype=torch.bfloat16, device="cuda")
+    ep = torch.empty((0,), dtype=torch.int32, device="cuda")
+    out, lse, work, staged = ra.forward(q, sh.gq_pos, [ek] * 3, [ek] * 3, [ep] * 3)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    assert work.tolist() == [0, 0, 0] and staged == 0
+
+
 def test_step_by_step_matches_oracle_and_forward():
     """state_init + ra_step per block + ra_finalize: after every step the
     state finalises to the oracle's, and the end result equals ra_forward
