@@ -185,13 +185,15 @@ ra_status ra_forward_timed(const ra_problem* p, int32_t n_cp, const void* q, con
  * ra_forward without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, hosts
  * that forbid allocation).  Arguments and results are those of ra_forward.
- * The running state and staging slots live in a fixed array of
- * RA_NOALLOC_MAX_BYTES that every device the library runs on holds from the
- * library's load until the process ends; the first call on a device takes
- * that array's address and creates five ordering events (once), and no call
- * allocates device memory.  A problem whose ra_forward_workspace_bytes()
- * exceeds RA_NOALLOC_MAX_BYTES is refused with RA_ERR_WORKSPACE before any
- * work.  Nothing in the array needs to start at zero (every step writes
+ * It runs one launch per block (the one-block schedules of ra_forward), so
+ * it needs one running state (fp32 m and l of h_q x n_q rows, o of
+ * h_q x n_q x d_k) and two staging slots (a block's K, V and positions),
+ * which live in a fixed array of RA_NOALLOC_MAX_BYTES that every device the
+ * library runs on holds from the library's load until the process ends; the
+ * first call on a device takes that array's address and creates five
+ * ordering events (once), and no call allocates device memory.  A problem
+ * whose state and two slots (16-byte aligned each) exceed
+ * RA_NOALLOC_MAX_BYTES is refused with RA_ERR_WORKSPACE before any work.  Nothing in the array needs to start at zero (every step writes
  * what it later reads), but all calls on one device share it: calls that
  * overlap in time on one device race and give unspecified results.
  */

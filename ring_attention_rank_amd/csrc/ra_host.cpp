@@ -465,6 +465,16 @@ size_t ra_forward_workspace_bytes(const ra_problem* p) {
   return fast_path(p) ? ws_layout(p, kChunkSlots, 2).total : ws_layout(p, 2, 1).total;
 }
 
+}  // extern "C"
+
+// The no-alloc form's workspace: one running state and two staging slots (it
+// runs one launch per block with its fixed events).
+size_t ra::forward_noalloc_bytes(const ra_problem* p) {
+  return check_problem(p) == RA_OK ? ws_layout(p, 2, 1).total : 0;
+}
+
+extern "C" {
+
 ra_status ra_forward(const ra_problem* p, int32_t n_cp, const void* q, const int32_t* q_pos,
                      const void* const* k_blocks, const void* const* v_blocks,
                      const int32_t* const* k_pos_blocks, void* workspace, size_t ws_bytes,

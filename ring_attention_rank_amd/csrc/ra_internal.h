@@ -30,6 +30,9 @@ ra_status forward_ring(const ra_problem* p, int32_t n_cp, const void* q, const i
                        float* out, float* lse, int64_t* work, int64_t* staged_bytes,
                        void* main_stream, void* side_stream, void* const* launch_events,
                        void* const* staged_events, const hipEvent_t* fixed);
+// Bytes of the no-alloc form's workspace (one state, two staging slots); 0
+// for an invalid problem.
+size_t forward_noalloc_bytes(const ra_problem* p);
 
 // Arguments of one ring-step launch (one key/value block against all local
 // queries of all heads).  READ selects whether the state is read (else it

@@ -59,7 +59,7 @@ extern "C" ra_status ra_forward_noalloc(const ra_problem* p, int32_t n_cp, const
   int32_t bm = 0, bn = 0;
   const ra_status st = ra_tile_shape(p, &bm, &bn);
   if (st != RA_OK) return st;
-  if (ra_forward_workspace_bytes(p) > kScratchBytes) return RA_ERR_WORKSPACE;
+  if (ra::forward_noalloc_bytes(p) > kScratchBytes) return RA_ERR_WORKSPACE;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RA_ERR_HIP;
   DeviceScratch& d = g_dev[dev];

@@ -151,6 +151,14 @@ def test_forward_noalloc_refuses_oversize():
     args = lambda p: (ctypes.byref(p), 2, v, v, arr, arr, arr, v, v, None, None, None, None)
     assert L.ra_forward_noalloc(*args(big)) == WORKSPACE
     assert L.ra_forward_noalloc(*args(good(d_k=96))) == SHAPE
+    # the full 8B share: ra_forward's workspace (two states, four slots)
+    # exceeds the array, but the no-alloc form's own (one state, two slots:
+    # about 200 MB) fits, so the size check passes (without a device the
+    # call then fails on the device query, never on the size)
+    p8 = good(n_q=8192, n_k=8192, h_q=32, h_kv=8)
+    assert ra.workspace_bytes(p8) > ra.NOALLOC_MAX_BYTES
+    if not torch.cuda.is_available():
+        assert L.ra_forward_noalloc(*args(p8)) not in (WORKSPACE, SHAPE, NULL, ALIGN)
 
 
 def test_mfma_ceiling_checks():
