@@ -43,6 +43,20 @@ def test_noalloc_matches_forward_twice(first, second):
     assert sizes[1] < sizes[0]  # the second call runs on a smaller input
 
 
+def test_noalloc_full_8b_share():
+    """The largest share of the size table, the full 8B one: ra_forward's own
+    workspace would not fit the array, the no-alloc form's (one state, two
+    slots) does, and it gives ra_forward's bits (ra_forward's two blocks per
+    launch are bit for bit one launch per block)."""
+    print("[noalloc] llama8b_gqa_zigzag full share rank 0", flush=True)
+    sh = Share(synth.case_by_name("llama8b_gqa_zigzag"), 0).to_gpu()
+    need = ra.workspace_bytes(ra._problem_from(sh.gq, sh.gk[0], True, None))
+    assert need > ra.NOALLOC_MAX_BYTES
+    (o1, l1, w1, s1), (o2, l2, w2, s2) = _both(sh)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(w1, w2) and s1 == s2
+
+
 def test_noalloc_refuses_what_does_not_fit():
     """A share whose workspace exceeds the fixed array is refused before any
     work: out and lse keep their contents."""
