@@ -381,8 +381,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's rank share only; multi-GPU runs are not part of "
-              "this build (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU's rank share only: the library runs the ring on one "
+              "GPU (the exchange between ranks is a copy on that GPU); use --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

@@ -8,7 +8,7 @@ kernels, helpers, tables or pre/post-processing.  The only thing both sides use
 is the seeded input generator in ``synth/``, which holds none of the method's
 arithmetic.
 
-Sources (the three web pages this build follows):
+Sources (the three web pages it follows):
 
 * "Context Parallelism (CP)" concept page (research-hub), section
   "Key math / How it works": ring of GPUs, blockwise attention with the online
