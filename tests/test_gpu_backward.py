@@ -239,10 +239,12 @@ def test_unsupported_shapes_refused():
         ra.backward_step(q96, sh.gq_pos, k96, k96, sh.gk_pos[0], q96, z, z, dq)
 
 
-@pytest.mark.parametrize("name", ["llama405b_stage_share", "million_striped_mha"])
+@pytest.mark.parametrize("name", ["llama405b_stage_share", "llama70b_stage_share",
+                                  "llama8b_gqa_zigzag", "million_striped_mha"])
 def test_full_size_sampled(name):
     """A share at full size (405B stage: 8192 queries, 16 heads, 16 blocks of
-    8192 keys; striped MHA: 8 heads, 64 blocks), in the launch configuration
+    8192 keys; 70B stage: 8 heads; 8B: 32 query heads on 8 key/value heads,
+    4 blocks; striped MHA: 8 heads, 64 blocks), in the launch configuration
     the benchmark times.  Sampled rows' dq against the oracle (those rows get
     the oracle's out and lse; the other rows take the library's forward, which
     only the sum rules below use).  Sum rules over all blocks: per key/value
